@@ -1,0 +1,228 @@
+/*
+ * pkv.h - paged KV cache for MI355X (gfx950): page write, in-place paged
+ * decode attention, gather, and the host page pool / block-table plumbing.
+ *
+ * The method.  A sequence's K/V rows live in fixed-size pages of a shared
+ * pool; a per-sequence block table maps logical block j to a physical page,
+ * so token t of the sequence lives at (table[t / page_size], t % page_size)
+ * (tiny-llm paged_kv.py, module docstring).  Pages may sit anywhere in the
+ * pool, several tables may name the same page (libmir-metal
+ * src/engine/kv/paged/mod.rs, PagedStore::snapshot), and only real tokens are
+ * stored.  Decode attention reads the pages in place through the table
+ * instead of gathering them into a contiguous copy first (tiny-llm
+ * paged_kv.py docstring: the gather is the toy's extra copy).
+ *
+ * Conventions for every call:
+ *   - "device" pointers are device addresses (hipMalloc memory or the data
+ *     pointer of a torch GPU tensor); "host" pointers are ordinary memory.
+ *   - The caller owns every buffer.  The library never allocates or frees
+ *     device memory and never synchronises a stream.  Kernels are enqueued
+ *     on `stream` (a hipStream_t; NULL = the default stream) and read their
+ *     inputs when they run, so buffers must stay alive until the stream has
+ *     passed them.
+ *   - Calls return PKV_OK or a negative PKV_E* status; pkv_last_error()
+ *     returns a message for the calling thread's last failure.  Arguments
+ *     are validated on the host before anything is enqueued: a failing call
+ *     enqueues nothing.
+ *   - Device-side checks never fault: a table entry outside [0, n_pages), a
+ *     write position past the table row or a length past the bound makes the
+ *     kernel skip that row/page (or clamp the length) and OR a PKV_DEV_* bit
+ *     into the cache's device status word.
+ *
+ * Page layout in HBM (chosen for gfx950, see the pool layout note below):
+ *   K pages  [n_layers][n_pages][n_kv_heads][page_size][head_dim]
+ *            (per page and KV head one token-major slab: slot rows of head_dim)
+ *   V pages  [n_layers][n_pages][n_kv_heads][head_dim][page_size]
+ *            (per page and KV head one dim-major slab: for each dim, the
+ *             page_size slots are contiguous)
+ *   element  float32 (PKV_FMT_F32), bfloat16 (PKV_FMT_BF16) or an int8 code
+ *            (PKV_FMT_INT8)
+ *   int8 scales, K and V each: float32 [n_layers][n_pages][n_kv_heads][page_size]
+ *            (a separate array per K and V as in libmir-metal's Arena
+ *             key_scales / value_scales, indexed by the same physical page)
+ * Row buffers crossing the ABI (write input, gather output) are token-major
+ * [n_rows][n_kv_heads][head_dim], like AstrAI inference/cache.py's
+ * PagedCache.write input.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define PKV_OK 0
+#define PKV_EINVAL (-1)      /* null pointer, bad shape, bad enum, G does not divide */
+#define PKV_ERANGE (-2)      /* layer out of range, length bound past the table */
+#define PKV_EFORMAT (-3)     /* write format differs from the store, dtype not accepted */
+#define PKV_ENOMEM (-4)      /* pool exhausted, workspace too small */
+#define PKV_EHIP (-5)        /* a HIP launch failed */
+#define PKV_EDOUBLEFREE (-6) /* release of a page that is not in use */
+
+/* ---- device status bits (OR-ed into the cache's status word) ------------ */
+#define PKV_DEV_WRITE_PAGE 1u   /* a written row's table entry is outside [0, n_pages) */
+#define PKV_DEV_WRITE_TABLE 2u  /* a written row's position is negative or past the table row */
+#define PKV_DEV_READ_PAGE 4u    /* attend/gather met a table entry outside [0, n_pages) */
+#define PKV_DEV_LEN 8u          /* attend met lens[b] < 0 or > max_len (clamped) */
+
+typedef enum { PKV_FMT_F32 = 0, PKV_FMT_BF16 = 1, PKV_FMT_INT8 = 2 } pkv_format;
+typedef enum { PKV_DT_F32 = 0, PKV_DT_BF16 = 1 } pkv_dtype;
+
+/* pkv_paged_attend flags */
+#define PKV_ATTEND_VALU 1u /* force the vector-ALU kernel even where the matrix-core one applies */
+
+typedef struct pkv_layout {
+  int32_t n_layers;
+  int32_t n_pages;
+  int32_t page_size;  /* tokens per page, >= 1 */
+  int32_t n_kv_heads;
+  int32_t head_dim;   /* multiple of 16, at most 256 */
+  int32_t format;     /* pkv_format */
+} pkv_layout;
+
+typedef struct pkv_cache pkv_cache;
+
+/* Bytes of one K (or V) page array and of one K (or V) scale array for this
+ * layout (scale bytes are 0 unless the format is int8).  EINVAL on a bad
+ * layout. */
+int pkv_layout_bytes(const pkv_layout* layout, uint64_t* kv_bytes, uint64_t* scale_bytes);
+
+/* Bind caller-owned device page arrays to a cache handle (the PagedStore /
+ * Arena pair of libmir-metal paged/mod.rs).  k_pages/v_pages: device, the
+ * layout above.  k_scales/v_scales: device float32, required for int8 and
+ * ignored otherwise.  dev_status: device int32 status word (the caller
+ * zeroes it; kernels only OR bits into it).  The handle keeps the pointers
+ * until pkv_cache_destroy. */
+int pkv_cache_create(const pkv_layout* layout, void* k_pages, void* v_pages, float* k_scales,
+                     float* v_scales, int32_t* dev_status, pkv_cache** out);
+void pkv_cache_destroy(pkv_cache* cache);
+
+/* paged_write(layer, table, start_pos, k, v, format).
+ * Row i of sequence b (rows cu_new[b] .. cu_new[b+1]-1 of k and v) is stored
+ * at position t = start_pos[b] + (i - cu_new[b]), i.e. in page
+ * table[b * table_stride + t / page_size], slot t % page_size (AstrAI
+ * cache.py PagedCache.write, with one start position per sequence as in
+ * tiny-llm paged_kv.py's per-slot lengths).  No other slot is touched.
+ *   table      device int32 [batch][table_stride]; entries past the rows a
+ *              write reaches are never read.
+ *   start_pos  device int32 [batch]; cu_new device int32 [batch + 1],
+ *              non-decreasing, cu_new[0] = 0, cu_new[batch] = total_new.
+ *   k, v       device [total_new][n_kv_heads][head_dim] of in_dtype.
+ *   format     must equal the store's format (EFORMAT otherwise).
+ * F32 pages take f32 rows and BF16 pages bf16 rows, copied bit for bit.
+ * INT8 pages take bf16 or f32 rows and quantize each (token, KV head) row of
+ * K and of V on its own: scale = max|x| / 127 (one IEEE float32 division),
+ * code = clamp(rint(x / scale), -127, 127) with ties to even; an all-zero row
+ * stores scale 0 and codes 0 (the KvPageFormat::Int8PerTokenHead of
+ * libmir-metal paged/mod.rs; the rule itself is not printed there). */
+int pkv_paged_write(pkv_cache* cache, int32_t layer, const int32_t* table, int32_t table_stride,
+                    int32_t batch, const int32_t* start_pos, const int32_t* cu_new,
+                    int32_t total_new, const void* k, const void* v, int32_t in_dtype,
+                    int32_t format, void* stream);
+
+/* Split size (tokens per split-K partition) that pkv_paged_attend uses when
+ * called with split_tokens = 0; a multiple of 64 and of page_size. */
+int pkv_attend_split(const pkv_cache* cache, int32_t batch, int32_t n_q_heads, int32_t max_len,
+                     int32_t* split_tokens);
+
+/* Workspace bytes pkv_paged_attend needs for these sizes (split_tokens 0 =
+ * the automatic split). */
+int pkv_attend_workspace_size(const pkv_cache* cache, int32_t batch, int32_t n_q_heads,
+                              int32_t max_len, int32_t split_tokens, uint64_t* bytes);
+
+/* paged_attend(q, table, lens, scale): one decode query per sequence.
+ * For sequence b and query head h (KV head g = h / (n_q_heads / n_kv_heads)):
+ *   out[b][h] = sum_{t < lens[b]} softmax_t(scale * <q[b][h], k_t>) v_t
+ * with k_t, v_t read in place from the pages of table row b (int8: code times
+ * its per-token scale).  lens[b] counts every stored token, including one
+ * written in the same step, and no other mask applies (tiny-llm paged_kv.py
+ * begin_step masks positions <= the pre-step length).  lens[b] = 0 gives
+ * zeros.  Work is split over tokens in partitions of split_tokens (0 =
+ * automatic) and the partial results (running max, sum and weighted V) are
+ * combined by a second kernel; the result of a sequence depends only on its
+ * own tokens and the split size.
+ *   q          device [batch][n_q_heads][head_dim] of q_dtype; out has the
+ *              same shape and dtype (bf16 rounded to nearest even).
+ *   table      device int32 [batch][table_stride].
+ *   lens       device int32 [batch]; max_len is a host upper bound on them,
+ *              at most table_stride * page_size (ERANGE otherwise).
+ *   scale      softmax scale (float32).
+ *   workspace  device scratch of at least pkv_attend_workspace_size bytes
+ *              (ENOMEM otherwise), 256-byte aligned.
+ *   flags      0 or PKV_ATTEND_VALU. */
+int pkv_paged_attend(pkv_cache* cache, int32_t layer, const void* q, int32_t q_dtype,
+                     int32_t n_q_heads, const int32_t* table, int32_t table_stride,
+                     const int32_t* lens, int32_t batch, int32_t max_len, float scale, void* out,
+                     void* workspace, uint64_t workspace_bytes, int32_t split_tokens,
+                     uint32_t flags, void* stream);
+
+/* gather(table, len): rows 0 .. len-1 of one sequence copied out in token
+ * order (AstrAI cache.py PagedCache.gather truncated by CacheView;
+ * libmir-metal PagedStore::context).  k_out, v_out: device
+ * [len][n_kv_heads][head_dim] in the page element type (int8 pages give raw
+ * codes); k_scale_out, v_scale_out: device float32 [len][n_kv_heads], int8
+ * only (ignored otherwise).  Only table_row[0 .. ceil(len/page_size)-1] is
+ * read.  Kept to compare the in-place read against a gather-first one. */
+int pkv_gather(pkv_cache* cache, int32_t layer, const int32_t* table_row, int32_t len,
+               void* k_out, void* v_out, float* k_scale_out, float* v_scale_out, void* stream);
+
+/* Apply n block-table updates: table[upd[3i] * table_stride + upd[3i+1]] =
+ * upd[3i+2], with upd a device int32 [n][3] list (sequence, logical block,
+ * physical page), as tiny-llm paged_kv.py's begin_step mirrors newly
+ * allocated blocks into its device table.  Entries outside the table are
+ * skipped. */
+int pkv_table_apply(int32_t* table, int32_t table_stride, int32_t batch, const int32_t* upd,
+                    int32_t n, void* stream);
+
+const char* pkv_last_error(void);
+
+/* ---- host page pool (refcounted) ---------------------------------------
+ * AstrAI cache.py PagedCache.alloc / alloc_n / free: the lowest free page is
+ * handed out with count 1; alloc_n is all-or-nothing; release drops one
+ * reference and the page is free again at zero.  retain adds one (the
+ * sharing of libmir-metal PagedStore::snapshot).  Releasing or retaining a
+ * page that is not in use is EDOUBLEFREE / EINVAL (tiny-llm BlockAllocator).
+ * One pool is used from one thread at a time. */
+typedef struct pkv_pool pkv_pool;
+int pkv_pool_create(int32_t n_pages, pkv_pool** out);
+void pkv_pool_destroy(pkv_pool* pool);
+int pkv_pool_alloc(pkv_pool* pool, int32_t* id);                /* ENOMEM when full */
+int pkv_pool_alloc_n(pkv_pool* pool, int32_t n, int32_t* ids); /* host ids[n]; ENOMEM, nothing granted */
+int pkv_pool_retain(pkv_pool* pool, int32_t id);
+int pkv_pool_release(pkv_pool* pool, int32_t id);
+int32_t pkv_pool_refcount(const pkv_pool* pool, int32_t id);    /* -1 for an id outside the pool */
+int32_t pkv_pool_num_free(const pkv_pool* pool);
+
+/* ---- host block tables over a pool --------------------------------------
+ * batch sequences, each with a host table row of table_stride entries (-1
+ * past its pages) and a length.  Growth allocates pages from the pool as a
+ * sequence's length crosses a page boundary (tiny-llm begin_step;
+ * libmir-metal allocation::ensure), sharing retains another sequence's
+ * pages, release returns them.  Every change to a table entry is also queued
+ * as an update triple for pkv_table_apply, so the device copy of the table
+ * follows without re-sending the whole table. */
+typedef struct pkv_seqs pkv_seqs;
+int pkv_seqs_create(pkv_pool* pool, int32_t batch, int32_t table_stride, int32_t page_size,
+                    pkv_seqs** out);
+void pkv_seqs_destroy(pkv_seqs* seqs); /* releases every page still held */
+/* Grow sequence b by n tokens (allocating pages as needed, all or nothing):
+ * ENOMEM leaves the sequence unchanged, ERANGE if the row would overflow. */
+int pkv_seqs_append(pkv_seqs* seqs, int32_t b, int32_t n);
+/* Sequence dst (which must be empty) shares the first n_pages pages of src:
+ * each gets one more reference.  Its length becomes n_pages * page_size. */
+int pkv_seqs_share(pkv_seqs* seqs, int32_t dst, int32_t src, int32_t n_pages);
+int pkv_seqs_release(pkv_seqs* seqs, int32_t b);
+const int32_t* pkv_seqs_table(const pkv_seqs* seqs); /* host [batch][table_stride] */
+const int32_t* pkv_seqs_lens(const pkv_seqs* seqs);  /* host [batch] */
+/* Move up to cap queued update triples into host upd[cap][3]; returns the
+ * number moved (the rest stay queued), or a negative status. */
+int32_t pkv_seqs_take_updates(pkv_seqs* seqs, int32_t* upd, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

@@ -1,0 +1,465 @@
+// Host side of the C ABI: argument validation, the split-K planner, kernel
+// launches, the refcounted page pool and the host block tables.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+#include <set>
+#include <vector>
+
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int check_layout(const pkv_layout* l) {
+  if (!l) return fail(PKV_EINVAL, "layout is null");
+  if (l->n_layers < 1 || l->n_pages < 1 || l->page_size < 1 || l->n_kv_heads < 1)
+    return fail(PKV_EINVAL, "layout sizes must be positive");
+  if (l->head_dim < 16 || l->head_dim > 256 || l->head_dim % 16)
+    return fail(PKV_EINVAL, "head_dim must be a multiple of 16 in [16, 256], got %d", l->head_dim);
+  if (l->format < PKV_FMT_F32 || l->format > PKV_FMT_INT8)
+    return fail(PKV_EINVAL, "unknown page format %d", l->format);
+  return PKV_OK;
+}
+
+int64_t gcd64(int64_t a, int64_t b) { return b ? gcd64(b, a % b) : a; }
+
+// Split granularity: a multiple of 64 (the vector kernel's token tile) and of
+// the page size (so a split never starts inside a page).
+int64_t split_unit(int page_size) { return 64 / gcd64(64, page_size) * page_size; }
+
+int plan_split(const pkv_cache* c, int batch, int n_q_heads, int max_len) {
+  // Aim for about 2048 workgroups over the chip (8 per compute unit) and
+  // keep every split between 256 and 1024 tokens, so a long sequence is cut
+  // into many partitions and short ones are not over-split.
+  const int64_t unit = split_unit(c->L.page_size);
+  const int64_t work = (int64_t)std::max(batch, 1) * c->L.n_kv_heads * std::max(max_len, 1);
+  int64_t want = (work + 2047) / 2048;
+  want = std::min<int64_t>(std::max<int64_t>(want, 256), 1024);
+  int64_t split = (want + unit - 1) / unit * unit;
+  (void)n_q_heads;
+  return (int)split;
+}
+
+int check_split(const pkv_cache* c, int32_t split) {
+  if (split < 0) return fail(PKV_EINVAL, "split_tokens must be >= 0");
+  if (split > 0 && split % split_unit(c->L.page_size))
+    return fail(PKV_EINVAL, "split_tokens %d must be a multiple of %lld", split,
+                (long long)split_unit(c->L.page_size));
+  return PKV_OK;
+}
+
+struct WsLayout {
+  uint64_t o_bytes, ml_off, total;
+};
+
+WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_split) {
+  WsLayout w;
+  const uint64_t rows = (uint64_t)batch * n_q_heads * n_split;
+  w.o_bytes = rows * head_dim * sizeof(float);
+  w.ml_off = (w.o_bytes + 255) / 256 * 256;
+  w.total = w.ml_off + rows * 2 * sizeof(float);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_err; }
+
+int pkv_layout_bytes(const pkv_layout* l, uint64_t* kv_bytes, uint64_t* scale_bytes) {
+  if (int e = check_layout(l)) return e;
+  const uint64_t slots = (uint64_t)l->n_layers * l->n_pages * l->n_kv_heads * l->page_size;
+  if (kv_bytes) *kv_bytes = slots * l->head_dim * pkv::format_bytes(l->format);
+  if (scale_bytes) *scale_bytes = l->format == PKV_FMT_INT8 ? slots * sizeof(float) : 0;
+  return PKV_OK;
+}
+
+int pkv_cache_create(const pkv_layout* l, void* k_pages, void* v_pages, float* k_scales,
+                     float* v_scales, int32_t* dev_status, pkv_cache** out) {
+  if (int e = check_layout(l)) return e;
+  if (!out) return fail(PKV_EINVAL, "out is null");
+  if (!k_pages || !v_pages) return fail(PKV_EINVAL, "page arrays are null");
+  if (l->format == PKV_FMT_INT8 && (!k_scales || !v_scales))
+    return fail(PKV_EINVAL, "int8 pages need scale arrays");
+  if ((reinterpret_cast<uintptr_t>(k_pages) | reinterpret_cast<uintptr_t>(v_pages)) & 15)
+    return fail(PKV_EINVAL, "page arrays must be 16-byte aligned");
+  pkv_cache* c = new (std::nothrow) pkv_cache;
+  if (!c) return fail(PKV_ENOMEM, "out of host memory");
+  c->L = *l;
+  c->k_pages = k_pages;
+  c->v_pages = v_pages;
+  c->k_scales = l->format == PKV_FMT_INT8 ? k_scales : nullptr;
+  c->v_scales = l->format == PKV_FMT_INT8 ? v_scales : nullptr;
+  c->status = dev_status;
+  *out = c;
+  return PKV_OK;
+}
+
+void pkv_cache_destroy(pkv_cache* c) { delete c; }
+
+int pkv_paged_write(pkv_cache* c, int32_t layer, const int32_t* table, int32_t table_stride,
+                    int32_t batch, const int32_t* start_pos, const int32_t* cu_new,
+                    int32_t total_new, const void* k, const void* v, int32_t in_dtype,
+                    int32_t format, void* stream) {
+  if (!c) return fail(PKV_EINVAL, "cache is null");
+  if (layer < 0 || layer >= c->L.n_layers)
+    return fail(PKV_ERANGE, "layer %d outside [0, %d)", layer, c->L.n_layers);
+  if (format != c->L.format)
+    return fail(PKV_EFORMAT, "write format %d differs from the store's %d", format, c->L.format);
+  if (in_dtype != PKV_DT_F32 && in_dtype != PKV_DT_BF16)
+    return fail(PKV_EINVAL, "unknown input dtype %d", in_dtype);
+  if ((c->L.format == PKV_FMT_F32 && in_dtype != PKV_DT_F32) ||
+      (c->L.format == PKV_FMT_BF16 && in_dtype != PKV_DT_BF16))
+    return fail(PKV_EFORMAT, "native pages take rows of their own dtype");
+  if (batch < 0 || total_new < 0 || table_stride < 1)
+    return fail(PKV_EINVAL, "negative batch/total_new or table_stride < 1");
+  if (total_new == 0) return PKV_OK;
+  if (batch == 0) return fail(PKV_EINVAL, "rows given for an empty batch");
+  if (!table || !start_pos || !cu_new || !k || !v) return fail(PKV_EINVAL, "null device pointer");
+  if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15)
+    return fail(PKV_EINVAL, "k and v must be 16-byte aligned");
+  pkv::WriteArgs a;
+  a.k_pages = c->k_pages;
+  a.v_pages = c->v_pages;
+  a.k_scales = c->k_scales;
+  a.v_scales = c->v_scales;
+  a.status = c->status;
+  a.table = table;
+  a.start_pos = start_pos;
+  a.cu_new = cu_new;
+  a.k_in = k;
+  a.v_in = v;
+  a.layer_page0 = (int64_t)layer * c->L.n_pages;
+  a.n_pages = c->L.n_pages;
+  a.page_size = c->L.page_size;
+  a.n_kv_heads = c->L.n_kv_heads;
+  a.head_dim = c->L.head_dim;
+  a.table_stride = table_stride;
+  a.batch = batch;
+  a.total_new = total_new;
+  hipError_t e = pkv::launch_write(a, c->L.format, in_dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_EHIP, "write launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+int pkv_attend_split(const pkv_cache* c, int32_t batch, int32_t n_q_heads, int32_t max_len,
+                     int32_t* split_tokens) {
+  if (!c || !split_tokens) return fail(PKV_EINVAL, "null argument");
+  *split_tokens = plan_split(c, batch, n_q_heads, max_len);
+  return PKV_OK;
+}
+
+int pkv_attend_workspace_size(const pkv_cache* c, int32_t batch, int32_t n_q_heads,
+                              int32_t max_len, int32_t split_tokens, uint64_t* bytes) {
+  if (!c || !bytes) return fail(PKV_EINVAL, "null argument");
+  if (batch < 0 || n_q_heads < 1 || max_len < 0) return fail(PKV_EINVAL, "bad sizes");
+  if (int e = check_split(c, split_tokens)) return e;
+  const int split = split_tokens ? split_tokens : plan_split(c, batch, n_q_heads, max_len);
+  const int n_split = std::max(1, (max_len + split - 1) / split);
+  *bytes = ws_layout(batch, n_q_heads, c->L.head_dim, n_split).total;
+  return PKV_OK;
+}
+
+int pkv_paged_attend(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype,
+                     int32_t n_q_heads, const int32_t* table, int32_t table_stride,
+                     const int32_t* lens, int32_t batch, int32_t max_len, float scale, void* out,
+                     void* workspace, uint64_t workspace_bytes, int32_t split_tokens,
+                     uint32_t flags, void* stream) {
+  if (!c) return fail(PKV_EINVAL, "cache is null");
+  if (layer < 0 || layer >= c->L.n_layers)
+    return fail(PKV_ERANGE, "layer %d outside [0, %d)", layer, c->L.n_layers);
+  if (q_dtype != PKV_DT_F32 && q_dtype != PKV_DT_BF16)
+    return fail(PKV_EINVAL, "unknown q dtype %d", q_dtype);
+  if (n_q_heads < 1 || n_q_heads % c->L.n_kv_heads)
+    return fail(PKV_EINVAL, "n_q_heads %d is not a positive multiple of n_kv_heads %d",
+                n_q_heads, c->L.n_kv_heads);
+  if (batch < 0 || max_len < 0 || table_stride < 1)
+    return fail(PKV_EINVAL, "negative batch/max_len or table_stride < 1");
+  if ((int64_t)max_len > (int64_t)table_stride * c->L.page_size)
+    return fail(PKV_ERANGE, "max_len %d exceeds the table row (%d pages of %d)", max_len,
+                table_stride, c->L.page_size);
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "scale is not finite");
+  if (flags & ~PKV_ATTEND_VALU) return fail(PKV_EINVAL, "unknown flags 0x%x", flags);
+  if (int e = check_split(c, split_tokens)) return e;
+  if (batch == 0) return PKV_OK;
+  if (!q || !out || !table || !lens || !workspace) return fail(PKV_EINVAL, "null device pointer");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
+  const int split = split_tokens ? split_tokens : plan_split(c, batch, n_q_heads, max_len);
+  const int n_split = std::max(1, (max_len + split - 1) / split);
+  const WsLayout w = ws_layout(batch, n_q_heads, c->L.head_dim, n_split);
+  if (workspace_bytes < w.total)
+    return fail(PKV_ENOMEM, "workspace holds %llu bytes, %llu needed",
+                (unsigned long long)workspace_bytes, (unsigned long long)w.total);
+
+  pkv::AttendArgs a;
+  a.q = q;
+  a.out = out;
+  a.k_pages = c->k_pages;
+  a.v_pages = c->v_pages;
+  a.k_scales = c->k_scales;
+  a.v_scales = c->v_scales;
+  a.status = c->status;
+  a.table = table;
+  a.lens = lens;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.ml_off);
+  a.layer_page0 = (int64_t)layer * c->L.n_pages;
+  a.qk_scale_log2 = scale * pkv::kLog2eHost;
+  a.n_pages = c->L.n_pages;
+  a.page_size = c->L.page_size;
+  a.n_kv_heads = c->L.n_kv_heads;
+  a.head_dim = c->L.head_dim;
+  a.n_q_heads = n_q_heads;
+  a.group = n_q_heads / c->L.n_kv_heads;
+  a.table_stride = table_stride;
+  a.batch = batch;
+  a.max_len = max_len;
+  a.split_tokens = split;
+  a.n_split = n_split;
+  a.q_bf16 = q_dtype == PKV_DT_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (max_len > 0) {
+    const bool mfma = !(flags & PKV_ATTEND_VALU) &&
+                      pkv::mfma_supported(c->L.format, a.q_bf16, a.head_dim, a.page_size, a.group);
+    e = mfma ? pkv::launch_attend_mfma(a, c->L.format, s)
+             : pkv::launch_attend_valu(a, c->L.format, s);
+    if (e != hipSuccess) return fail(PKV_EHIP, "attend launch failed: %s", hipGetErrorString(e));
+  }
+  e = pkv::launch_reduce(a, s);
+  if (e != hipSuccess) return fail(PKV_EHIP, "reduce launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+int pkv_gather(pkv_cache* c, int32_t layer, const int32_t* table_row, int32_t len, void* k_out,
+               void* v_out, float* k_scale_out, float* v_scale_out, void* stream) {
+  if (!c) return fail(PKV_EINVAL, "cache is null");
+  if (layer < 0 || layer >= c->L.n_layers)
+    return fail(PKV_ERANGE, "layer %d outside [0, %d)", layer, c->L.n_layers);
+  if (len < 0) return fail(PKV_EINVAL, "negative len");
+  if (len == 0) return PKV_OK;
+  if (!table_row || !k_out || !v_out) return fail(PKV_EINVAL, "null device pointer");
+  if (c->L.format == PKV_FMT_INT8 && (!k_scale_out || !v_scale_out))
+    return fail(PKV_EINVAL, "int8 gather needs scale outputs");
+  if ((reinterpret_cast<uintptr_t>(k_out) | reinterpret_cast<uintptr_t>(v_out)) & 15)
+    return fail(PKV_EINVAL, "outputs must be 16-byte aligned");
+  pkv::GatherArgs a;
+  a.k_pages = c->k_pages;
+  a.v_pages = c->v_pages;
+  a.k_scales = c->k_scales;
+  a.v_scales = c->v_scales;
+  a.status = c->status;
+  a.table_row = table_row;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.ks_out = k_scale_out;
+  a.vs_out = v_scale_out;
+  a.layer_page0 = (int64_t)layer * c->L.n_pages;
+  a.n_pages = c->L.n_pages;
+  a.page_size = c->L.page_size;
+  a.n_kv_heads = c->L.n_kv_heads;
+  a.head_dim = c->L.head_dim;
+  a.len = len;
+  hipError_t e = pkv::launch_gather(a, c->L.format, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_EHIP, "gather launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+int pkv_table_apply(int32_t* table, int32_t table_stride, int32_t batch, const int32_t* upd,
+                    int32_t n, void* stream) {
+  if (n < 0 || table_stride < 1 || batch < 0) return fail(PKV_EINVAL, "bad sizes");
+  if (n == 0) return PKV_OK;
+  if (!table || !upd) return fail(PKV_EINVAL, "null device pointer");
+  hipError_t e = pkv::launch_table_apply(table, table_stride, batch, upd, n,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_EHIP, "table update launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- pool ----
+
+struct pkv_pool {
+  std::vector<int32_t> refs;
+  std::set<int32_t> free_ids;  // ordered: begin() is the lowest free page
+};
+
+extern "C" {
+
+int pkv_pool_create(int32_t n_pages, pkv_pool** out) {
+  if (!out || n_pages < 1) return fail(PKV_EINVAL, "bad pool size or null out");
+  pkv_pool* p = new (std::nothrow) pkv_pool;
+  if (!p) return fail(PKV_ENOMEM, "out of host memory");
+  p->refs.assign(n_pages, 0);
+  for (int32_t i = 0; i < n_pages; ++i) p->free_ids.insert(p->free_ids.end(), i);
+  *out = p;
+  return PKV_OK;
+}
+
+void pkv_pool_destroy(pkv_pool* p) { delete p; }
+
+int pkv_pool_alloc(pkv_pool* p, int32_t* id) {
+  if (!p || !id) return fail(PKV_EINVAL, "null argument");
+  if (p->free_ids.empty()) return fail(PKV_ENOMEM, "all %zu pages in use", p->refs.size());
+  const int32_t i = *p->free_ids.begin();
+  p->free_ids.erase(p->free_ids.begin());
+  p->refs[i] = 1;
+  *id = i;
+  return PKV_OK;
+}
+
+int pkv_pool_alloc_n(pkv_pool* p, int32_t n, int32_t* ids) {
+  if (!p || n < 0 || (n > 0 && !ids)) return fail(PKV_EINVAL, "bad arguments");
+  if ((size_t)n > p->free_ids.size())
+    return fail(PKV_ENOMEM, "%d pages asked, %zu free", n, p->free_ids.size());
+  for (int32_t k = 0; k < n; ++k) {
+    const int32_t i = *p->free_ids.begin();
+    p->free_ids.erase(p->free_ids.begin());
+    p->refs[i] = 1;
+    ids[k] = i;
+  }
+  return PKV_OK;
+}
+
+int pkv_pool_retain(pkv_pool* p, int32_t id) {
+  if (!p || id < 0 || (size_t)id >= p->refs.size()) return fail(PKV_EINVAL, "page id out of range");
+  if (p->refs[id] == 0) return fail(PKV_EINVAL, "page %d is not in use", id);
+  ++p->refs[id];
+  return PKV_OK;
+}
+
+int pkv_pool_release(pkv_pool* p, int32_t id) {
+  if (!p || id < 0 || (size_t)id >= p->refs.size()) return fail(PKV_EINVAL, "page id out of range");
+  if (p->refs[id] == 0) return fail(PKV_EDOUBLEFREE, "page %d released twice or never allocated", id);
+  if (--p->refs[id] == 0) p->free_ids.insert(id);
+  return PKV_OK;
+}
+
+int32_t pkv_pool_refcount(const pkv_pool* p, int32_t id) {
+  if (!p || id < 0 || (size_t)id >= p->refs.size()) return -1;
+  return p->refs[id];
+}
+
+int32_t pkv_pool_num_free(const pkv_pool* p) { return p ? (int32_t)p->free_ids.size() : -1; }
+
+}  // extern "C"
+
+// ------------------------------------------------------------ block tables --
+
+struct pkv_seqs {
+  pkv_pool* pool;
+  int32_t batch, stride, page_size;
+  std::vector<int32_t> table, lens, npages;
+  std::vector<int32_t> updates;  // queued (b, j, page) triples, oldest first
+  size_t upd_head = 0;
+  void set(int32_t b, int32_t j, int32_t page) {
+    table[(size_t)b * stride + j] = page;
+    updates.push_back(b);
+    updates.push_back(j);
+    updates.push_back(page);
+  }
+};
+
+extern "C" {
+
+int pkv_seqs_create(pkv_pool* pool, int32_t batch, int32_t table_stride, int32_t page_size,
+                    pkv_seqs** out) {
+  if (!pool || !out || batch < 1 || table_stride < 1 || page_size < 1)
+    return fail(PKV_EINVAL, "bad arguments");
+  pkv_seqs* s = new (std::nothrow) pkv_seqs;
+  if (!s) return fail(PKV_ENOMEM, "out of host memory");
+  s->pool = pool;
+  s->batch = batch;
+  s->stride = table_stride;
+  s->page_size = page_size;
+  s->table.assign((size_t)batch * table_stride, -1);
+  s->lens.assign(batch, 0);
+  s->npages.assign(batch, 0);
+  *out = s;
+  return PKV_OK;
+}
+
+int pkv_seqs_release(pkv_seqs* s, int32_t b) {
+  if (!s || b < 0 || b >= s->batch) return fail(PKV_EINVAL, "bad sequence");
+  for (int32_t j = 0; j < s->npages[b]; ++j) {
+    int e = pkv_pool_release(s->pool, s->table[(size_t)b * s->stride + j]);
+    if (e) return e;
+    s->set(b, j, -1);
+  }
+  s->npages[b] = 0;
+  s->lens[b] = 0;
+  return PKV_OK;
+}
+
+void pkv_seqs_destroy(pkv_seqs* s) {
+  if (!s) return;
+  for (int32_t b = 0; b < s->batch; ++b) pkv_seqs_release(s, b);
+  delete s;
+}
+
+int pkv_seqs_append(pkv_seqs* s, int32_t b, int32_t n) {
+  if (!s || b < 0 || b >= s->batch || n < 0) return fail(PKV_EINVAL, "bad arguments");
+  const int64_t new_len = (int64_t)s->lens[b] + n;
+  const int64_t need = (new_len + s->page_size - 1) / s->page_size;
+  if (need > s->stride)
+    return fail(PKV_ERANGE, "sequence %d would need %lld pages, the row holds %d", b,
+                (long long)need, s->stride);
+  const int32_t extra = (int32_t)(need - s->npages[b]);
+  if (extra > 0) {
+    std::vector<int32_t> ids(extra);
+    if (int e = pkv_pool_alloc_n(s->pool, extra, ids.data())) return e;
+    for (int32_t k = 0; k < extra; ++k) s->set(b, s->npages[b] + k, ids[k]);
+    s->npages[b] += extra;
+  }
+  s->lens[b] = (int32_t)new_len;
+  return PKV_OK;
+}
+
+int pkv_seqs_share(pkv_seqs* s, int32_t dst, int32_t src, int32_t n_pages) {
+  if (!s || dst < 0 || dst >= s->batch || src < 0 || src >= s->batch || dst == src || n_pages < 0)
+    return fail(PKV_EINVAL, "bad arguments");
+  if (s->npages[dst] != 0) return fail(PKV_EINVAL, "sequence %d is not empty", dst);
+  if ((int64_t)n_pages * s->page_size > s->lens[src])
+    return fail(PKV_EINVAL, "only full pages of sequence %d can be shared", src);
+  for (int32_t j = 0; j < n_pages; ++j) {
+    const int32_t page = s->table[(size_t)src * s->stride + j];
+    if (int e = pkv_pool_retain(s->pool, page)) return e;
+    s->set(dst, j, page);
+  }
+  s->npages[dst] = n_pages;
+  s->lens[dst] = n_pages * s->page_size;
+  return PKV_OK;
+}
+
+const int32_t* pkv_seqs_table(const pkv_seqs* s) { return s ? s->table.data() : nullptr; }
+const int32_t* pkv_seqs_lens(const pkv_seqs* s) { return s ? s->lens.data() : nullptr; }
+
+int32_t pkv_seqs_take_updates(pkv_seqs* s, int32_t* upd, int32_t cap) {
+  if (!s || cap < 0 || (cap > 0 && !upd)) return fail(PKV_EINVAL, "bad arguments");
+  const size_t avail = (s->updates.size() - s->upd_head) / 3;
+  const size_t n = std::min<size_t>(avail, (size_t)cap);
+  std::copy(s->updates.begin() + s->upd_head, s->updates.begin() + s->upd_head + 3 * n, upd);
+  s->upd_head += 3 * n;
+  if (s->upd_head == s->updates.size()) {
+    s->updates.clear();
+    s->upd_head = 0;
+  }
+  return (int32_t)n;
+}
+
+}  // extern "C"

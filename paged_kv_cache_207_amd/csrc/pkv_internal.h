@@ -1,0 +1,88 @@
+// Internal declarations shared by the host library and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pkv.h"
+
+struct pkv_cache {
+  pkv_layout L;
+  void* k_pages;
+  void* v_pages;
+  float* k_scales;
+  float* v_scales;
+  int32_t* status;
+};
+
+namespace pkv {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// Arguments of the page-write kernel (one launch = one paged_write call).
+struct WriteArgs {
+  void* k_pages;
+  void* v_pages;
+  float* k_scales;
+  float* v_scales;
+  int32_t* status;
+  const int32_t* table;
+  const int32_t* start_pos;
+  const int32_t* cu_new;
+  const void* k_in;
+  const void* v_in;
+  int64_t layer_page0;  // layer * n_pages
+  int32_t n_pages, page_size, n_kv_heads, head_dim;
+  int32_t table_stride, batch, total_new;
+};
+
+// Arguments shared by the split-K attention kernels and the reduce kernel.
+struct AttendArgs {
+  const void* q;
+  void* out;
+  const void* k_pages;
+  const void* v_pages;
+  const float* k_scales;
+  const float* v_scales;
+  int32_t* status;
+  const int32_t* table;
+  const int32_t* lens;
+  float* ws_o;   // [batch][n_q_heads][n_split][head_dim] unnormalised partial outputs
+  float* ws_ml;  // [batch][n_q_heads][n_split][2] running max (log2 units) and sum
+  int64_t layer_page0;
+  float qk_scale_log2;  // softmax scale * log2(e)
+  int32_t n_pages, page_size, n_kv_heads, head_dim, n_q_heads, group;
+  int32_t table_stride, batch, max_len, split_tokens, n_split;
+  int32_t q_bf16;  // 1: q and out are bf16, 0: float32
+};
+
+struct GatherArgs {
+  const void* k_pages;
+  const void* v_pages;
+  const float* k_scales;
+  const float* v_scales;
+  int32_t* status;
+  const int32_t* table_row;
+  void* k_out;
+  void* v_out;
+  float* ks_out;
+  float* vs_out;
+  int64_t layer_page0;
+  int32_t n_pages, page_size, n_kv_heads, head_dim, len;
+};
+
+// Element size of a page format in bytes.
+inline int format_bytes(int fmt) { return fmt == PKV_FMT_F32 ? 4 : fmt == PKV_FMT_BF16 ? 2 : 1; }
+
+// Launchers (return the hipError_t of the launch).
+hipError_t launch_write(const WriteArgs& a, int fmt, int in_dtype, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, int fmt, hipStream_t s);
+hipError_t launch_attend_valu(const AttendArgs& a, int fmt, hipStream_t s);
+// Returns hipErrorNotSupported when the shape has no matrix-core variant.
+hipError_t launch_attend_mfma(const AttendArgs& a, int fmt, hipStream_t s);
+bool mfma_supported(int fmt, int q_bf16, int head_dim, int page_size, int group);
+hipError_t launch_reduce(const AttendArgs& a, hipStream_t s);
+hipError_t launch_table_apply(int32_t* table, int32_t stride, int32_t batch, const int32_t* upd,
+                              int32_t n, hipStream_t s);
+
+}  // namespace pkv

@@ -140,10 +140,13 @@ def test_attend_parity(name, split, flags):
     assert c.status() == 0
 
 
+@pytest.mark.parametrize("fill", [0x5A, 0xFF], ids=["finite", "nan"])
 @pytest.mark.parametrize("fmt,D", [("f32", 64), ("bf16", 128), ("bf16", 64), ("int8", 128)])
-def test_attend_edge_lengths(fmt, D):
+def test_attend_edge_lengths(fmt, D, fill):
     """Lengths 0, 1, one short of / exactly / one past a page, a tile and a
-    split; max_len larger than every length."""
+    split; max_len larger than every length.  With fill 0xFF every slot no
+    write reached holds NaN (f32/bf16) or a NaN scale (int8): slots past a
+    length must never reach the result."""
     require_gpu()
     bs, Hkv, Hq = 16, 2, 16
     lens = np.array([0, 1, 15, 16, 17, 63, 64, 65, 255, 256, 257, 700], np.int32)
@@ -160,7 +163,9 @@ def test_attend_edge_lengths(fmt, D):
     dt = torch.float32 if fmt == "f32" else torch.bfloat16
     w = W.Workload("edge", P, bs, Hkv, D, Hq, fmt, dt, dt, float(np.float32(D ** -0.5)), tables,
                    lens, 77)
-    c, tdev = _run_fill(w)
+    c = make_cache(w, sentinel=fill)
+    tdev = dev(w.tables)
+    gpu_write(c, tdev, w.rounds())
     o = sentinel_oracle(w)
     oracle_write_rounds(o, w, w.rounds())
     q = w.query()
@@ -278,7 +283,7 @@ def test_device_status_flags_without_fault():
     o = sentinel_oracle(w)
     good = r.cu_new.copy()
     # the oracle writes everything except sequence 1's second page
-    o.write(0, w.tables, r.start_pos[:1], good[:2], np_bits(r.k), np_bits(r.v), "f32")
+    o.write(0, w.tables, r.start_pos[:1], good[:2], np_bits(r.k)[:37], np_bits(r.v)[:37], "f32")
     k1 = np_bits(r.k)[37:]
     v1 = np_bits(r.v)[37:]
     keep = [i for i in range(50) if not 16 <= i < 32]

@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Paged KV cache decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_bf16]
+
+A step is one pass of the hot path over the batch: paged_write of one new
+K/V row per sequence (at position len-1, the newest token) followed by
+paged_attend (split-K partial pass + combine) of one query per sequence over
+all len tokens, read in place through a fully fragmented block table.  The
+K/V pages are filled once before timing.  Prints one JSON line (stdout);
+details go to stderr.
+
+value = KV bytes the attention reads per step / step time (GB/s);
+roofline = the split-K partial kernel (the dominant one): its algorithmic
+bytes (K/V pages + table entries + queries) / its average duration from HIP
+events recorded by the library around each launch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from paged_kv_cache_207_amd import pkv  # noqa: E402
+from paged_kv_cache_207_amd import workloads as W  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "paged decode attention KV GB/s (% of HBM peak) and decode tokens/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_split_long_bf16_traffic.json")
+KERNEL_SOURCES = ["paged_kv_cache_207_amd/csrc/attend_mfma.hip",
+                  "paged_kv_cache_207_amd/csrc/pkv_device.h"]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kv_bytes(w) -> int:
+    elem = {"f32": 4, "bf16": 2, "int8": 1}[w.kv_format]
+    per_tok = w.n_kv_heads * w.head_dim * elem * 2
+    if w.kv_format == "int8":
+        per_tok += w.n_kv_heads * 4 * 2
+    return int(w.lens.astype(np.int64).sum()) * per_tok
+
+
+def split_kernel_bytes(w) -> int:
+    """Algorithmic bytes of one split-pass launch: K/V pages of every token,
+    the table entries that map them, and the queries."""
+    npages = sum(-(-int(n) // w.page_size) for n in w.lens)
+    qb = w.batch * w.n_q_heads * w.head_dim * (2 if w.q_dtype == torch.bfloat16 else 4)
+    return kv_bytes(w) + 4 * npages + qb
+
+
+def fill(w, cache, device):
+    """Write every row of every sequence (untimed); returns the host rows."""
+    table = torch.as_tensor(w.tables).to(device)
+    ks, vs = [], []
+    for b in range(w.batch):
+        k, v = w.seq_kv(b)
+        ks.append(k)
+        vs.append(v)
+        # one write call per sequence: its own table row, start 0
+        cache.write(table[b:b + 1].contiguous(), torch.zeros(1, dtype=torch.int32, device=device),
+                    torch.tensor([0, ks[b].shape[0]], dtype=torch.int32, device=device),
+                    ks[b].to(device), vs[b].to(device))
+    torch.cuda.synchronize()
+    return table, ks, vs
+
+
+def read_probe(device, nbytes=1 << 30, reps=5) -> float:
+    src = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    src.fill_(1)
+    sink = torch.empty(pkv.lib().pkv_probe_blocks(nbytes), dtype=torch.float32, device=device)
+    pkv.probe_stream(src, sink=sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        pkv.probe_stream(src, sink=sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src
+    return gbps
+
+
+def calibration_copy(device, nbytes=256 << 20) -> float:
+    """A plain copy of known size (read nbytes, write nbytes): the reference
+    dispatch for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    src.fill_(3)
+    pkv.probe_stream(src, dst)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    pkv.probe_stream(src, dst)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * nbytes / (e0.elapsed_time(e1) / 1e3) / 1e9
+
+
+def load_traffic():
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sources_sha256_16") != kernel_hash():
+        return None  # the kernel changed since the counters were taken
+    return t.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, ks, vs, q, budget_s: float):
+    """The oracle, as it stands, on a bounded sample: whole sequences, one
+    decode step each (the oracle write of the step's row + its fp64 gather
+    and attention over every query head), until about budget_s of CPU work."""
+    from oracle import OracleCache, attend
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    qb = bits(q)
+    elapsed, done, kv_done = 0.0, 0, 0
+    for b in range(w.batch):
+        L = int(w.lens[b])
+        npg = -(-L // w.page_size)
+        oc = OracleCache(1, npg, w.page_size, w.n_kv_heads, w.head_dim, w.kv_format)
+        table = np.arange(npg, dtype=np.int32)[None]
+        kb, vb = bits(ks[b]), bits(vs[b])
+        oc.write(0, table, [0], [0, L - 1], kb[:L - 1], vb[:L - 1], "bf16")  # untimed fill
+        t0 = time.perf_counter()
+        oc.write(0, table, [L - 1], [0, 1], kb[L - 1:L], vb[L - 1:L], "bf16")
+        attend(oc, 0, qb[b:b + 1], "bf16", table, np.array([L]), w.scale)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        kv_done += L * w.n_kv_heads * w.head_dim * 2 * 2
+        if elapsed >= budget_s:
+            break
+    return {"value": round(kv_done / elapsed / 1e9, 4), "unit": "GB/s",
+            "tokens_per_s": round(done / elapsed, 4), "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {w.batch} sequences ({int(w.lens[0])} tokens, all "
+                      f"{w.n_q_heads} query heads), one decode step each: oracle page write of "
+                      f"the step's row + float64 gather and attention; {elapsed:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_bf16")
+    ap.add_argument("--split", type=int, default=0, help="split tokens (0 = library plan)")
+    ap.add_argument("--flush", type=int, default=1,
+                    help="1: overwrite a 512 MiB buffer between timed steps (outside the events)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this library has no "
+              "multi-GPU path: run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    device = torch.device("cuda:0")
+    w = W.by_name(args.workload)
+    if isinstance(w, W.SharedPrefix):
+        raise SystemExit("the step benchmark takes a single-query-per-sequence workload")
+    log(f"workload {w.name}: B={w.batch} lens={int(w.lens.min())}..{int(w.lens.max())} "
+        f"Hq={w.n_q_heads} Hkv={w.n_kv_heads} D={w.head_dim} bs={w.page_size} P={w.n_pages}")
+
+    read_gbps = read_probe(device)
+    copy_gbps = calibration_copy(device)
+    log(f"probe: streaming read {read_gbps:.0f} GB/s, copy {copy_gbps:.0f} GB/s")
+
+    cache = pkv.PagedKVCache(w.n_pages, w.page_size, w.n_kv_heads, w.head_dim, w.kv_format,
+                             device=device)
+    t0 = time.perf_counter()
+    table, ks, vs = fill(w, cache, device)
+    log(f"filled {kv_bytes(w) / 2**30:.2f} GiB of pages in {time.perf_counter() - t0:.1f} s")
+
+    B = w.batch
+    lens = torch.as_tensor(w.lens).to(device)
+    start = (lens - 1).contiguous()
+    cu = torch.arange(B + 1, dtype=torch.int32, device=device)
+    k_new = torch.stack([ks[b][int(w.lens[b]) - 1] for b in range(B)]).to(device)
+    v_new = torch.stack([vs[b][int(w.lens[b]) - 1] for b in range(B)]).to(device)
+    q_host = w.query()
+    q = q_host.to(device)
+    out = torch.empty_like(q)
+    max_len = w.max_len
+    split = args.split or cache.split_for(B, w.n_q_heads, max_len)
+    ws = cache.workspace(B, w.n_q_heads, max_len, split)
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=device) if args.flush else None
+
+    def step():
+        cache.write(table, start, cu, k_new, v_new)
+        cache.attend(q, table, lens, max_len, w.scale, out=out, workspace=ws, split_tokens=split)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    cache.status() == 0 or sys.exit("device status flags set during warmup")
+
+    cache.timing(True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush_buf is not None:
+            flush_buf.fill_(i & 0xff)
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    cache.timing(False)
+    t = cache.timing_read()
+    step_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_per_step = float(np.mean(step_ms))
+    split_ms, split_n = t["attend_split"]
+    comb_ms, comb_n = t["attend_combine"]
+    wr_ms, wr_n = t["write"]
+    split_avg = split_ms / max(split_n, 1)
+    log(f"step: {ms_per_step * 1e3:.1f} us (min {min(step_ms) * 1e3:.1f}); split pass "
+        f"{split_avg * 1e3:.1f} us, combine {comb_ms / max(comb_n, 1) * 1e3:.1f} us, write "
+        f"{wr_ms / max(wr_n, 1) * 1e3:.1f} us; wall {wall * 1e3 / args.steps:.1f} us/step "
+        f"incl. flush; split_tokens={split}")
+
+    kvb = kv_bytes(w)
+    value = kvb / (ms_per_step / 1e3) / 1e9
+    achieved = split_kernel_bytes(w) / (split_avg / 1e3) / 1e9
+    traffic = load_traffic()
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "seq_len": int(w.lens.max()),
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "page_size": w.page_size, "n_pages": w.n_pages,
+                   "table": "seeded random permutation of the pool",
+                   "step": "paged_write 1 row/seq + paged_attend", "split_tokens": split,
+                   "l2_flush_between_steps": bool(args.flush)},
+        "tokens_per_s": round(B / (ms_per_step / 1e3), 1),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "kv_bytes_per_step": kvb,
+        "achievable_read_GBps": round(read_gbps, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "attend_mfma (split-K partial pass)",
+                     "avg_launch_us": round(split_avg * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, ks, vs, q_host, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

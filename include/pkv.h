@@ -180,6 +180,30 @@ int pkv_table_apply(int32_t* table, int32_t table_stride, int32_t batch, const i
 
 const char* pkv_last_error(void);
 
+/* ---- measurement -----------------------------------------------------------
+ * Kernel timing: while enabled on a cache, pkv_paged_write, pkv_paged_attend
+ * and pkv_gather record HIP events (host-allocated, on the call's stream)
+ * around each kernel pass they enqueue; nothing else changes.
+ * pkv_timing_read waits for the recorded events, returns the summed
+ * milliseconds and the number of passes timed per kind (PKV_T_*), then
+ * forgets them.  ms[] and counts[] are host arrays of PKV_T_COUNT entries. */
+#define PKV_T_WRITE 0
+#define PKV_T_ATTEND_SPLIT 1  /* the split-K partial pass */
+#define PKV_T_ATTEND_COMBINE 2
+#define PKV_T_GATHER 3
+#define PKV_T_COUNT 4
+int pkv_timing_enable(pkv_cache* cache, int32_t on);
+int pkv_timing_read(pkv_cache* cache, double* ms, int32_t* counts);
+
+/* Streaming probes, the denominators of a bandwidth figure: mode 0 reads
+ * `bytes` from src (16-byte loads, every byte once; one float per workgroup
+ * goes to sink[blocks]); mode 1 copies src to dst.  bytes must be a multiple
+ * of 16 and both pointers 16-byte aligned.  pkv_probe_blocks gives the sink
+ * length mode 0 needs. */
+int32_t pkv_probe_blocks(uint64_t bytes);
+int pkv_probe_stream(const void* src, void* dst, float* sink, uint64_t bytes, int32_t mode,
+                     void* stream);
+
 /* ---- host page pool (refcounted) ---------------------------------------
  * AstrAI cache.py PagedCache.alloc / alloc_n / free: the lowest free page is
  * handed out with count 1; alloc_n is all-or-nothing; release drops one

@@ -73,11 +73,76 @@ WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_split) {
   return w;
 }
 
+// Timing: an event pair around one kernel pass, recorded only while enabled.
+struct Timer {
+  pkv_cache* c;
+  int kind;
+  hipStream_t s;
+  hipEvent_t e0 = nullptr;
+  Timer(pkv_cache* c_, int kind_, hipStream_t s_) : c(c_), kind(kind_), s(s_) {
+    if (c->timing && hipEventCreate(&e0) == hipSuccess) hipEventRecord(e0, s);
+  }
+  void stop() {
+    if (!e0) return;
+    hipEvent_t e1;
+    if (hipEventCreate(&e1) == hipSuccess) {
+      hipEventRecord(e1, s);
+      c->events[kind].emplace_back(e0, e1);
+    } else {
+      hipEventDestroy(e0);
+    }
+    e0 = nullptr;
+  }
+};
+
 }  // namespace
 
 extern "C" {
 
 const char* pkv_last_error(void) { return g_err; }
+
+int pkv_timing_enable(pkv_cache* c, int32_t on) {
+  if (!c) return fail(PKV_EINVAL, "cache is null");
+  c->timing = on != 0;
+  return PKV_OK;
+}
+
+int pkv_timing_read(pkv_cache* c, double* ms, int32_t* counts) {
+  if (!c || !ms || !counts) return fail(PKV_EINVAL, "null argument");
+  int rc = PKV_OK;
+  for (int k = 0; k < PKV_T_COUNT; ++k) {
+    double sum = 0.0;
+    for (auto& e : c->events[k]) {
+      float t = 0.f;
+      if (hipEventSynchronize(e.second) != hipSuccess ||
+          hipEventElapsedTime(&t, e.first, e.second) != hipSuccess)
+        rc = fail(PKV_EHIP, "event query failed");
+      sum += t;
+      hipEventDestroy(e.first);
+      hipEventDestroy(e.second);
+    }
+    ms[k] = sum;
+    counts[k] = (int32_t)c->events[k].size();
+    c->events[k].clear();
+  }
+  return rc;
+}
+
+int32_t pkv_probe_blocks(uint64_t bytes) { return pkv::probe_blocks(bytes); }
+
+int pkv_probe_stream(const void* src, void* dst, float* sink, uint64_t bytes, int32_t mode,
+                     void* stream) {
+  if (mode != 0 && mode != 1) return fail(PKV_EINVAL, "mode must be 0 or 1");
+  if (bytes == 0) return PKV_OK;
+  if (bytes % 16) return fail(PKV_EINVAL, "bytes must be a multiple of 16");
+  if (!src || (mode == 1 && !dst) || (mode == 0 && !sink))
+    return fail(PKV_EINVAL, "null device pointer");
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15)
+    return fail(PKV_EINVAL, "pointers must be 16-byte aligned");
+  hipError_t e = pkv::launch_probe(src, dst, sink, bytes, mode, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_EHIP, "probe launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
 
 int pkv_layout_bytes(const pkv_layout* l, uint64_t* kv_bytes, uint64_t* scale_bytes) {
   if (int e = check_layout(l)) return e;
@@ -108,7 +173,15 @@ int pkv_cache_create(const pkv_layout* l, void* k_pages, void* v_pages, float* k
   return PKV_OK;
 }
 
-void pkv_cache_destroy(pkv_cache* c) { delete c; }
+void pkv_cache_destroy(pkv_cache* c) {
+  if (!c) return;
+  for (auto& v : c->events)
+    for (auto& e : v) {
+      hipEventDestroy(e.first);
+      hipEventDestroy(e.second);
+    }
+  delete c;
+}
 
 int pkv_paged_write(pkv_cache* c, int32_t layer, const int32_t* table, int32_t table_stride,
                     int32_t batch, const int32_t* start_pos, const int32_t* cu_new,
@@ -150,7 +223,9 @@ int pkv_paged_write(pkv_cache* c, int32_t layer, const int32_t* table, int32_t t
   a.table_stride = table_stride;
   a.batch = batch;
   a.total_new = total_new;
+  Timer tm(c, PKV_T_WRITE, static_cast<hipStream_t>(stream));
   hipError_t e = pkv::launch_write(a, c->L.format, in_dtype, static_cast<hipStream_t>(stream));
+  tm.stop();
   if (e != hipSuccess) return fail(PKV_EHIP, "write launch failed: %s", hipGetErrorString(e));
   return PKV_OK;
 }
@@ -236,11 +311,15 @@ int pkv_paged_attend(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype
   if (max_len > 0) {
     const bool mfma = !(flags & PKV_ATTEND_VALU) &&
                       pkv::mfma_supported(c->L.format, a.q_bf16, a.head_dim, a.page_size, a.group);
+    Timer tm(c, PKV_T_ATTEND_SPLIT, s);
     e = mfma ? pkv::launch_attend_mfma(a, c->L.format, s)
              : pkv::launch_attend_valu(a, c->L.format, s);
+    tm.stop();
     if (e != hipSuccess) return fail(PKV_EHIP, "attend launch failed: %s", hipGetErrorString(e));
   }
+  Timer tm(c, PKV_T_ATTEND_COMBINE, s);
   e = pkv::launch_reduce(a, s);
+  tm.stop();
   if (e != hipSuccess) return fail(PKV_EHIP, "reduce launch failed: %s", hipGetErrorString(e));
   return PKV_OK;
 }
@@ -274,7 +353,9 @@ int pkv_gather(pkv_cache* c, int32_t layer, const int32_t* table_row, int32_t le
   a.n_kv_heads = c->L.n_kv_heads;
   a.head_dim = c->L.head_dim;
   a.len = len;
+  Timer tm(c, PKV_T_GATHER, static_cast<hipStream_t>(stream));
   hipError_t e = pkv::launch_gather(a, c->L.format, static_cast<hipStream_t>(stream));
+  tm.stop();
   if (e != hipSuccess) return fail(PKV_EHIP, "gather launch failed: %s", hipGetErrorString(e));
   return PKV_OK;
 }

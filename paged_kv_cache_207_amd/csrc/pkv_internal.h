@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+#include <vector>
+
 #include "../../include/pkv.h"
 
 struct pkv_cache {
@@ -13,6 +16,8 @@ struct pkv_cache {
   float* k_scales;
   float* v_scales;
   int32_t* status;
+  bool timing = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> events[PKV_T_COUNT];  // (start, end) per pass
 };
 
 namespace pkv {
@@ -82,6 +87,9 @@ hipError_t launch_attend_valu(const AttendArgs& a, int fmt, hipStream_t s);
 hipError_t launch_attend_mfma(const AttendArgs& a, int fmt, hipStream_t s);
 bool mfma_supported(int fmt, int q_bf16, int head_dim, int page_size, int group);
 hipError_t launch_reduce(const AttendArgs& a, hipStream_t s);
+hipError_t launch_probe(const void* src, void* dst, float* sink, uint64_t bytes, int mode,
+                        hipStream_t s);
+int probe_blocks(uint64_t bytes);
 hipError_t launch_table_apply(int32_t* table, int32_t stride, int32_t batch, const int32_t* upd,
                               int32_t n, hipStream_t s);
 

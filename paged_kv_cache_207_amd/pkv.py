@@ -19,6 +19,7 @@ FMT_F32, FMT_BF16, FMT_INT8 = 0, 1, 2
 DT_F32, DT_BF16 = 0, 1
 DEV_WRITE_PAGE, DEV_WRITE_TABLE, DEV_READ_PAGE, DEV_LEN = 1, 2, 4, 8
 ATTEND_VALU = 1
+T_WRITE, T_ATTEND_SPLIT, T_ATTEND_COMBINE, T_GATHER, T_COUNT = 0, 1, 2, 3, 4
 
 FORMAT_CODE = {"f32": FMT_F32, "bf16": FMT_BF16, "int8": FMT_INT8}
 DTYPE_CODE = {torch.float32: DT_F32, torch.bfloat16: DT_BF16}
@@ -39,6 +40,10 @@ SYMBOLS = [
     ("pkv_gather", C.c_int, [_P, _I32, _P, _I32, _P, _P, _P, _P, _P]),
     ("pkv_table_apply", C.c_int, [_P, _I32, _I32, _P, _I32, _P]),
     ("pkv_last_error", C.c_char_p, []),
+    ("pkv_timing_enable", C.c_int, [_P, _I32]),
+    ("pkv_timing_read", C.c_int, [_P, C.POINTER(C.c_double), _PI32]),
+    ("pkv_probe_blocks", C.c_int32, [_U64]),
+    ("pkv_probe_stream", C.c_int, [_P, _P, _P, _U64, _I32, _P]),
     ("pkv_pool_create", C.c_int, [_I32, C.POINTER(_P)]),
     ("pkv_pool_destroy", None, [_P]),
     ("pkv_pool_alloc", C.c_int, [_P, _PI32]),
@@ -209,6 +214,19 @@ class PagedKVCache:
             _stream(self.device)))
         return out
 
+    # -- kernel timing -----------------------------------------------------------
+    def timing(self, on: bool = True):
+        _check(lib().pkv_timing_enable(self._h, int(on)))
+
+    def timing_read(self) -> dict:
+        """{kind: (total_ms, passes)} for write, attend_split, attend_combine,
+        gather since the last read (waits for the recorded events)."""
+        ms = (C.c_double * T_COUNT)()
+        n = (C.c_int32 * T_COUNT)()
+        _check(lib().pkv_timing_read(self._h, ms, n))
+        names = ["write", "attend_split", "attend_combine", "gather"]
+        return {k: (ms[i], n[i]) for i, k in enumerate(names)}
+
     # -- gather ------------------------------------------------------------------
     def gather(self, table_row, length: int, layer: int = 0):
         shape = (length, self.n_kv_heads, self.head_dim)
@@ -221,6 +239,19 @@ class PagedKVCache:
         _check(lib().pkv_gather(self._h, layer, _dev(table_row, torch.int32, "table_row"), length,
                                 _dev(k), _dev(v), _dev(ks), _dev(vs), _stream(self.device)))
         return k, v, ks, vs
+
+
+def probe_stream(src: torch.Tensor, dst: torch.Tensor | None = None,
+                 sink: torch.Tensor | None = None) -> None:
+    """Read every byte of src (dst None) or copy src to dst, on the current stream."""
+    nbytes = src.numel() * src.element_size()
+    if dst is None:
+        if sink is None or sink.numel() < lib().pkv_probe_blocks(nbytes):
+            raise ValueError("sink must hold pkv_probe_blocks(bytes) floats")
+        _check(lib().pkv_probe_stream(_dev(src), None, _dev(sink, torch.float32), nbytes, 0,
+                                      _stream(src.device)))
+    else:
+        _check(lib().pkv_probe_stream(_dev(src), _dev(dst), None, nbytes, 1, _stream(src.device)))
 
 
 def table_apply(table: torch.Tensor, upd: torch.Tensor) -> None:

@@ -61,15 +61,19 @@ __device__ __forceinline__ uint2 codes_to_bf16(uint32_t w) {
   return r;
 }
 
-template <int FMT, int D>
+template <int FMT, int D, int BS>
 __global__ __launch_bounds__(64) void attend_mfma_kernel(AttendArgs a) {
   using S = Step<FMT, D>;
+  using KT = typename S::KT;
+  using VT = typename S::VT;
   constexpr int NC = S::NC, ND = S::ND;
+  constexpr int ESZ = FMT == PKV_FMT_BF16 ? 2 : 1;
   const int lane = threadIdx.x;
   const int n = lane & 15;  // head column (B/C operands), row (A operands)
   const int j = lane >> 4;  // k group (A/B operands), row quad (C operand)
   const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int G = a.group, bs = a.page_size;
+  const int G = a.group;
+  const int bs = BS ? BS : a.page_size;
 
   const int len = clamp_len(a.lens[b], a.max_len, sp == 0 && g == 0 ? a.status : nullptr,
                             PKV_DEV_LEN);
@@ -90,67 +94,11 @@ __global__ __launch_bounds__(64) void attend_mfma_kernel(AttendArgs a) {
     }
   }
 
-  // ---- the split's table entries, 64 logical pages per lane-vector ----
-  const int pg_last = (t_end - 1) / bs;
-  const int32_t* trow = a.table + (int64_t)b * a.table_stride;
-  int pg_window = t_begin / bs;
-  auto load_pages = [&](int base) -> int {
-    const int lp = base + lane;
-    int pg = -1;
-    if (lp <= pg_last) {
-      pg = trow[lp];
-      if (pg < 0 || pg >= a.n_pages) {
-        report(a.status, PKV_DEV_READ_PAGE);
-        pg = -1;
-      }
-    }
-    return pg;
-  };
-  int vpage = load_pages(pg_window);
-
-  const int64_t slab_elems = (int64_t)bs * D;
+  const int64_t slab_bytes = (int64_t)bs * D * ESZ;
   const char* kp = static_cast<const char*>(a.k_pages);
   const char* vp = static_cast<const char*>(a.v_pages);
-  constexpr int ESZ = FMT == PKV_FMT_BF16 ? 2 : 1;
-
-  auto load_step = [&](int ts, S& r) {
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      const int tb = ts + 16 * tau;
-      const int lp = tb / bs;
-      if (lp - pg_window >= 64) {  // uniform: next window of table entries
-        pg_window += 64;
-        vpage = load_pages(pg_window);
-      }
-      const int page = tb < t_end ? __builtin_amdgcn_readlane(vpage, lp - pg_window) : -1;
-      r.live[tau] = page >= 0;
-      if (page >= 0) {
-        const int slot0 = tb - lp * bs;
-        const int64_t slab = (a.layer_page0 + page) * a.n_kv_heads + g;
-        const char* kb = kp + (slab * slab_elems + (int64_t)(slot0 + n) * D + 8 * j) * ESZ;
-        const char* vb = vp + (slab * slab_elems + slot0 + 4 * j) * ESZ;
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-          r.k[tau][c] = *reinterpret_cast<const typename S::KT*>(kb + 32 * c * ESZ);
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt)
-          r.v[dt][tau] =
-              *reinterpret_cast<const typename S::VT*>(vb + (int64_t)(16 * dt + n) * bs * ESZ);
-        if (FMT == PKV_FMT_INT8) {
-          const int64_t si = slab * bs + slot0 + 4 * j;
-          r.ks[tau] = *reinterpret_cast<const f32x4*>(a.k_scales + si);
-          r.vs[tau] = *reinterpret_cast<const f32x4*>(a.v_scales + si);
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) r.k[tau][c] = {};
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) r.v[dt][tau] = {};
-        r.ks[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
-        r.vs[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-  };
+  const int32_t* trow = a.table + (int64_t)b * a.table_stride;
+  const int pg_last = (t_end - 1) / bs;
 
   f32x4 o[ND];
 #pragma unroll
@@ -158,93 +106,142 @@ __global__ __launch_bounds__(64) void attend_mfma_kernel(AttendArgs a) {
   float m = -INFINITY, l = 0.f;
   const float qs = a.qk_scale_log2;
 
-  auto compute_step = [&](int ts, S& r) {
-    // S^T tiles: rows = tokens 16*tau + 4j + i, columns = heads
-    f32x4 sacc[2];
+  // The split is walked in windows of at most 64 logical pages: one table
+  // entry per lane, picked out with a lane read (uniform) per tile.
+  const int tokens_per_window = 64 * bs;
+  for (int w0 = t_begin; w0 < t_end; w0 += tokens_per_window) {
+    const int w_end = min(w0 + tokens_per_window, t_end);
+    const int pg0 = w0 / bs;
+    int vpage = -1;
+    {
+      const int lp = pg0 + lane;
+      if (lp <= pg_last) {
+        const int pg = trow[lp];
+        if (pg < 0 || pg >= a.n_pages) report(a.status, PKV_DEV_READ_PAGE);
+        else vpage = pg;
+      }
+    }
+
+    // Loads are unconditional: a tile with no page (past the length or a bad
+    // entry) reads page 0 of the array instead and is masked afterwards, so
+    // the compiler can keep the next step's loads in flight.
+    auto load_step = [&](int ts, S& r) {
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      sacc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int tau = 0; tau < 2; ++tau) {
+        const int tb = ts + 16 * tau;
+        const int lp = tb / bs;
+        const int page = tb < w_end ? __builtin_amdgcn_readlane(vpage, lp - pg0) : -1;
+        r.live[tau] = page >= 0;
+        const int slot0 = tb - lp * bs;
+        const int64_t slab = (a.layer_page0 + (page >= 0 ? page : 0)) * a.n_kv_heads + g;
+        const char* kslab = kp + slab * slab_bytes;  // uniform
+        const char* vslab = vp + slab * slab_bytes;
+        const int koff = ((slot0 + n) * D + 8 * j) * ESZ;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        bf16x8 ka;
-        if constexpr (FMT == PKV_FMT_BF16) {
-          ka = as_bf16x8(r.k[tau][c]);
-        } else {
-          const uint2 lo = codes_to_bf16(r.k[tau][c].x), hi = codes_to_bf16(r.k[tau][c].y);
-          ka = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
+        for (int c = 0; c < NC; ++c)
+          r.k[tau][c] = *reinterpret_cast<const KT*>(kslab + koff + 32 * c * ESZ);
+        const int voff = (n * bs + slot0 + 4 * j) * ESZ;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+          r.v[dt][tau] = *reinterpret_cast<const VT*>(vslab + voff + 16 * dt * bs * ESZ);
+        if (FMT == PKV_FMT_INT8) {
+          const float* kss = a.k_scales + slab * bs;
+          const float* vss = a.v_scales + slab * bs;
+          r.ks[tau] = *reinterpret_cast<const f32x4*>(kss + slot0 + 4 * j);
+          r.vs[tau] = *reinterpret_cast<const f32x4*>(vss + slot0 + 4 * j);
         }
-        sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[c], sacc[tau], 0, 0, 0);
       }
-    }
-    float sv[8];
-    bool ok[8];
-    float mx = -INFINITY;
+    };
+
+    auto compute_step = [&](int ts, S& r) {
+      // S^T tiles: rows = tokens 16*tau + 4j + i, columns = heads
+      f32x4 sacc[2];
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
+      for (int tau = 0; tau < 2; ++tau) {
+        sacc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = ts + 16 * tau + 4 * j + i;
-        ok[4 * tau + i] = r.live[tau] && t < t_end;
-        float x = sacc[tau][i] * qs;
-        if (FMT == PKV_FMT_INT8) x *= r.ks[tau][i];
-        sv[4 * tau + i] = ok[4 * tau + i] ? x : -INFINITY;
-        mx = fmaxf(mx, sv[4 * tau + i]);
+        for (int c = 0; c < NC; ++c) {
+          bf16x8 ka;
+          if constexpr (FMT == PKV_FMT_BF16) {
+            ka = as_bf16x8(r.k[tau][c]);
+          } else {
+            const uint2 lo = codes_to_bf16(r.k[tau][c].x), hi = codes_to_bf16(r.k[tau][c].y);
+            ka = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
+          }
+          sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[c], sacc[tau], 0, 0, 0);
+        }
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-    float psum = 0.f;
-    bf16x8 pb;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = ok[i] ? __builtin_amdgcn_exp2f(sv[i] - m_use) : 0.f;
-      psum += p;
-      float pw = p;
-      if (FMT == PKV_FMT_INT8) pw = ok[i] ? p * r.vs[i >> 2][i & 3] : 0.f;
-      pb[i] = (__bf16)pw;
-    }
-    l = l * alpha + psum;
-    m = m_new;
-    // V^T A operands; in the last step zero the slots past the length (bf16
-    // garbage there may be NaN; int8 codes are finite and already weighted 0)
-    const bool ragged = FMT == PKV_FMT_BF16 && ts + 32 > t_end;
-    uint32_t keep[2][2] = {{~0u, ~0u}, {~0u, ~0u}};
-    if (ragged) {
+      float sv[8];
+      bool ok[8];
+      float mx = -INFINITY;
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-        for (int w = 0; w < 2; ++w)
-          keep[tau][w] = (ok[4 * tau + 2 * w] ? 0x0000ffffu : 0u) |
-                         (ok[4 * tau + 2 * w + 1] ? 0xffff0000u : 0u);
-    }
+        for (int i = 0; i < 4; ++i) {
+          const int t = ts + 16 * tau + 4 * j + i;
+          ok[4 * tau + i] = r.live[tau] && t < w_end;
+          float x = sacc[tau][i] * qs;
+          if (FMT == PKV_FMT_INT8) x *= r.ks[tau][i];
+          sv[4 * tau + i] = ok[4 * tau + i] ? x : -INFINITY;
+          mx = fmaxf(mx, sv[4 * tau + i]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+      float psum = 0.f;
+      bf16x8 pb;
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      o[dt] *= alpha;
-      uint4 va;
-      if constexpr (FMT == PKV_FMT_BF16) {
-        va = uint4{r.v[dt][0].x & keep[0][0], r.v[dt][0].y & keep[0][1],
-                   r.v[dt][1].x & keep[1][0], r.v[dt][1].y & keep[1][1]};
-      } else {
-        const uint2 lo = codes_to_bf16(r.v[dt][0]), hi = codes_to_bf16(r.v[dt][1]);
-        va = uint4{lo.x, lo.y, hi.x, hi.y};
+      for (int i = 0; i < 8; ++i) {
+        const float p = ok[i] ? __builtin_amdgcn_exp2f(sv[i] - m_use) : 0.f;
+        psum += p;
+        float pw = p;
+        if (FMT == PKV_FMT_INT8) pw = ok[i] ? p * r.vs[i >> 2][i & 3] : 0.f;
+        pb[i] = (__bf16)pw;
       }
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pb, o[dt], 0, 0, 0);
-    }
-  };
+      l = l * alpha + psum;
+      m = m_new;
+      // V^T A operands.  Where a slot of the step is dead (past the length or
+      // on a missing page) zero its bf16 value: it may hold NaN, and 0 * NaN
+      // would reach the sum.  int8 codes are finite and carry weight 0 there.
+      const bool mask_v = FMT == PKV_FMT_BF16 && (ts + 32 > w_end || !r.live[0] || !r.live[1]);
+      uint32_t keep[2][2] = {{~0u, ~0u}, {~0u, ~0u}};
+      if (mask_v) {
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+          for (int w = 0; w < 2; ++w)
+            keep[tau][w] = (ok[4 * tau + 2 * w] ? 0x0000ffffu : 0u) |
+                           (ok[4 * tau + 2 * w + 1] ? 0xffff0000u : 0u);
+      }
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        o[dt] *= alpha;
+        uint4 va;
+        if constexpr (FMT == PKV_FMT_BF16) {
+          va = uint4{r.v[dt][0].x & keep[0][0], r.v[dt][0].y & keep[0][1],
+                     r.v[dt][1].x & keep[1][0], r.v[dt][1].y & keep[1][1]};
+        } else {
+          const uint2 lo = codes_to_bf16(r.v[dt][0]), hi = codes_to_bf16(r.v[dt][1]);
+          va = uint4{lo.x, lo.y, hi.x, hi.y};
+        }
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pb, o[dt], 0, 0, 0);
+      }
+    };
 
-  // ---- main loop: two register sets, loads one step ahead ----
-  const int n_steps = (t_end - t_begin + 31) / 32;
-  S r0, r1;
-  load_step(t_begin, r0);
-  for (int st = 0; st < n_steps; st += 2) {
-    const int ts = t_begin + 32 * st;
-    if (st + 1 < n_steps) load_step(ts + 32, r1);
-    compute_step(ts, r0);
-    if (st + 1 < n_steps) {
-      if (st + 2 < n_steps) load_step(ts + 64, r0);
-      compute_step(ts + 32, r1);
+    // ---- two register sets, loads one step ahead ----
+    const int n_steps = (w_end - w0 + 31) / 32;
+    S r0, r1;
+    load_step(w0, r0);
+    for (int st = 0; st < n_steps; st += 2) {
+      const int ts = w0 + 32 * st;
+      if (st + 1 < n_steps) load_step(ts + 32, r1);
+      compute_step(ts, r0);
+      if (st + 1 < n_steps) {
+        if (st + 2 < n_steps) load_step(ts + 64, r0);
+        compute_step(ts + 32, r1);
+      }
     }
   }
 
@@ -263,14 +260,21 @@ __global__ __launch_bounds__(64) void attend_mfma_kernel(AttendArgs a) {
   }
 }
 
+template <int FMT, int D>
+hipError_t launch_d(const AttendArgs& a, hipStream_t s) {
+  dim3 grid(a.n_split, a.n_kv_heads, a.batch);
+  if (a.page_size == 16)
+    hipLaunchKernelGGL((attend_mfma_kernel<FMT, D, 16>), grid, dim3(64), 0, s, a);
+  else if (a.page_size == 32)
+    hipLaunchKernelGGL((attend_mfma_kernel<FMT, D, 32>), grid, dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL((attend_mfma_kernel<FMT, D, 0>), grid, dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int FMT>
 hipError_t launch_fmt(const AttendArgs& a, hipStream_t s) {
-  dim3 grid(a.n_split, a.n_kv_heads, a.batch);
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL((attend_mfma_kernel<FMT, 128>), grid, dim3(64), 0, s, a);
-  else
-    hipLaunchKernelGGL((attend_mfma_kernel<FMT, 64>), grid, dim3(64), 0, s, a);
-  return hipGetLastError();
+  return a.head_dim == 128 ? launch_d<FMT, 128>(a, s) : launch_d<FMT, 64>(a, s);
 }
 
 }  // namespace

@@ -14,7 +14,11 @@
 namespace pkv {
 namespace {
 
+// One wave per (sequence, query head).  The split weights 2^(m_s - M) / L
+// are computed once into LDS; then each lane owns pairs of dims and sums the
+// splits' partial outputs with 8 loads in flight.
 __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
+  extern __shared__ float wsplit[];  // [n_split] weights
   const int lane = threadIdx.x;
   const int bh = blockIdx.x;  // b * n_q_heads + h
   const int b = bh / a.n_q_heads;
@@ -23,30 +27,48 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
   len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
   const int n = (len + a.split_tokens - 1) / a.split_tokens;
   const int64_t row0 = (int64_t)bh * a.n_split;
+  const float* ml = a.ws_ml + row0 * 2;
 
   float M = -INFINITY;
-  for (int s = lane; s < n; s += 64) M = fmaxf(M, a.ws_ml[(row0 + s) * 2]);
+  for (int s = lane; s < n; s += 64) M = fmaxf(M, ml[2 * s]);
   M = wave_max(M);
   float L = 0.f;
   for (int s = lane; s < n; s += 64) {
-    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + (row0 + s) * 2);
-    L += exp2f(ml.x - M) * ml.y;
+    const float2 x = *reinterpret_cast<const float2*>(ml + 2 * s);
+    const float w = exp2f(x.x - M);
+    wsplit[s] = w;
+    L = fmaf(w, x.y, L);
   }
   L = wave_sum(L);
+  __syncthreads();
   const float inv = n > 0 ? 1.f / L : 0.f;
 
-  for (int d = lane; d < D; d += 64) {
-    float acc = 0.f;
-    for (int s = 0; s < n; ++s) {
-      const float w = exp2f(a.ws_ml[(row0 + s) * 2] - M);
-      acc = fmaf(w, a.ws_o[(row0 + s) * D + d], acc);
+  const float* po = a.ws_o + row0 * D;
+  for (int d2 = lane; 2 * d2 < D; d2 += 64) {
+    float2 acc = {0.f, 0.f};
+    int s = 0;
+    for (; s + 8 <= n; s += 8) {
+      float2 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const float2*>(po + (int64_t)(s + u) * D + 2 * d2);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc.x = fmaf(wsplit[s + u], x[u].x, acc.x);
+        acc.y = fmaf(wsplit[s + u], x[u].y, acc.y);
+      }
     }
-    const float r = acc * inv;
-    const int64_t oi = (int64_t)bh * D + d;
+    for (; s < n; ++s) {
+      const float2 x = *reinterpret_cast<const float2*>(po + (int64_t)s * D + 2 * d2);
+      acc.x = fmaf(wsplit[s], x.x, acc.x);
+      acc.y = fmaf(wsplit[s], x.y, acc.y);
+    }
+    const float r0 = acc.x * inv, r1 = acc.y * inv;
+    const int64_t oi = (int64_t)bh * D + 2 * d2;
     if (a.q_bf16)
-      static_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16_bits(r);
+      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + oi) =
+          f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
     else
-      static_cast<float*>(a.out)[oi] = r;
+      *reinterpret_cast<float2*>(static_cast<float*>(a.out) + oi) = float2{r0, r1};
   }
 }
 
@@ -63,7 +85,8 @@ __global__ void table_apply_kernel(int32_t* table, int32_t stride, int32_t batch
 
 hipError_t launch_reduce(const AttendArgs& a, hipStream_t s) {
   if (a.batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL(reduce_kernel, dim3(a.batch * a.n_q_heads), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(reduce_kernel, dim3(a.batch * a.n_q_heads), dim3(64),
+                     (size_t)a.n_split * sizeof(float), s, a);
   return hipGetLastError();
 }
 

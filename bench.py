@@ -70,19 +70,27 @@ def split_kernel_bytes(w) -> int:
 
 
 def fill(w, cache, device):
-    """Write every row of every sequence (untimed); returns the host rows."""
+    """Write every row of every sequence through the workload's write rounds
+    (one round from position 0, or the unaligned head chunk then 512-row
+    rounds for int8 pages), timed by the library's events; returns the table,
+    the host rows and the fill's write timing."""
     table = torch.as_tensor(w.tables).to(device)
-    ks, vs = [], []
-    for b in range(w.batch):
-        k, v = w.seq_kv(b)
-        ks.append(k)
-        vs.append(v)
-        # one write call per sequence: its own table row, start 0
-        cache.write(table[b:b + 1].contiguous(), torch.zeros(1, dtype=torch.int32, device=device),
-                    torch.tensor([0, ks[b].shape[0]], dtype=torch.int32, device=device),
-                    ks[b].to(device), vs[b].to(device))
+    kv = {b: w.seq_kv(b) for b in range(w.batch)}
+    rounds = w.rounds(kv=kv)
+    cache.timing_read()
+    cache.timing(True)
+    for r in rounds:
+        cache.write(table, torch.as_tensor(r.start_pos).to(device),
+                    torch.as_tensor(r.cu_new).to(device), r.k.to(device), r.v.to(device))
+    cache.timing(False)
     torch.cuda.synchronize()
-    return table, ks, vs
+    ms, n = cache.timing_read()["write"]
+    in_elem = 2 if w.in_dtype == torch.bfloat16 else 4
+    rows = int(w.lens.astype(np.int64).sum())
+    moved = rows * w.n_kv_heads * w.head_dim * 2 * in_elem + kv_bytes(w)  # rows in + pages out
+    info = {"rounds": len(rounds), "write_us": round(ms * 1e3, 1),
+            "write_GBps_in_plus_out": round(moved / (ms / 1e3) / 1e9, 1)}
+    return table, [kv[b][0] for b in range(w.batch)], [kv[b][1] for b in range(w.batch)], info
 
 
 def read_probe(device, nbytes=1 << 30, reps=5) -> float:
@@ -139,7 +147,11 @@ def cpu_baseline(w, ks, vs, q, budget_s: float):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = 1
-    bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    def bits(t):
+        t = t.contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+    in_dt = "bf16" if w.in_dtype == torch.bfloat16 else "f32"
+    q_dt = "bf16" if w.q_dtype == torch.bfloat16 else "f32"
     qb = bits(q)
     caches = []
     for b in range(w.batch):  # untimed: the pages as the GPU holds them before the step
@@ -148,23 +160,170 @@ def cpu_baseline(w, ks, vs, q, budget_s: float):
         oc = OracleCache(1, npg, w.page_size, w.n_kv_heads, w.head_dim, w.kv_format)
         table = np.arange(npg, dtype=np.int32)[None]
         kb, vb = bits(ks[b]), bits(vs[b])
-        oc.write(0, table, [0], [0, L - 1], kb[:L - 1], vb[:L - 1], "bf16")
+        oc.write(0, table, [0], [0, L - 1], kb[:L - 1], vb[:L - 1], in_dt)
         caches.append((oc, table, kb[L - 1:L], vb[L - 1:L], L))
+    per_tok = kv_bytes(w) // max(int(w.lens.astype(np.int64).sum()), 1)  # K/V (+ scales) bytes
     elapsed, steps, kv_done = 0.0, 0, 0
     while elapsed < budget_s:
         for b, (oc, table, kr, vr, L) in enumerate(caches):
             t0 = time.perf_counter()
-            oc.write(0, table, [L - 1], [0, 1], kr, vr, "bf16")
-            attend(oc, 0, qb[b:b + 1], "bf16", table, np.array([L]), w.scale)
+            oc.write(0, table, [L - 1], [0, 1], kr, vr, in_dt)
+            attend(oc, 0, qb[b:b + 1], q_dt, table, np.array([L]), w.scale)
             elapsed += time.perf_counter() - t0
             steps += 1
-            kv_done += L * w.n_kv_heads * w.head_dim * 2 * 2
+            kv_done += L * per_tok
     return {"value": round(kv_done / elapsed / 1e9, 4), "unit": "GB/s",
             "tokens_per_s": round(steps / elapsed, 3), "cores": int(threads), "kind": "oracle",
             "sample": f"{steps} sequence decode steps over the {w.batch} sequences of the "
-                      f"workload ({int(w.lens[0])} tokens, all {w.n_q_heads} query heads each): "
+                      f"workload ({int(w.lens.min())}..{int(w.lens.max())} tokens, all "
+                      f"{w.n_q_heads} query heads each): "
                       f"oracle page write of the step's row + float64 gather and attention; "
                       f"{elapsed:.1f} s of CPU time"}
+
+
+def gather_compare(w, cache, table, device, reps=5):
+    """Time the gather-first alternative's extra copy: every sequence's K/V
+    copied out of its pages into a contiguous buffer (one pkv_gather per
+    sequence), the copy an in-place read avoids."""
+    outs = []
+    for b in range(w.batch):
+        L = int(w.lens[b])
+        kb = torch.empty((L, w.n_kv_heads, w.head_dim), dtype=pkv.PAGE_DTYPE[w.kv_format],
+                         device=device)
+        sc = (torch.empty((L, w.n_kv_heads), dtype=torch.float32, device=device)
+              if w.kv_format == "int8" else None)
+        outs.append((kb, torch.empty_like(kb), sc, None if sc is None else torch.empty_like(sc)))
+
+    def run():
+        for b in range(w.batch):
+            k, v, ks, vs = outs[b]
+            pkv._check(pkv.lib().pkv_gather(cache._h, 0, pkv._dev(table[b]), int(w.lens[b]),
+                                            pkv._dev(k), pkv._dev(v), pkv._dev(ks), pkv._dev(vs),
+                                            pkv._stream(device)))
+    run()
+    torch.cuda.synchronize()
+    cache.timing_read()
+    cache.timing(True)
+    for _ in range(reps):
+        run()
+    cache.timing(False)
+    ms, n = cache.timing_read()["gather"]
+    per_batch_ms = ms / reps
+    moved = 2 * kv_bytes(w)  # read the pages, write the copy
+    del outs
+    return {"gather_us_per_batch": round(per_batch_ms * 1e3, 2),
+            "gather_GBps_read_plus_write": round(moved / (per_batch_ms / 1e3) / 1e9, 1)}
+
+
+def run_shared_prefix(args, device):
+    """The shared-prefix workload as one job of n_steps decode steps after the
+    fill.  Each step = host table growth (pool-backed block tables: a sequence
+    whose length reaches a page boundary gets the lowest free page; the new
+    entries go to the device as update triples) + paged_write of one row per
+    sequence at its length + paged_attend over length + 1 tokens.  Every timed
+    job starts from the same rebuilt pool state (untimed)."""
+    sp = W.shared_prefix()
+    w = sp.base
+    B, bs = w.batch, w.page_size
+
+    def build_tables():
+        pool = pkv.PagePool(w.n_pages)
+        seqs = pkv.SeqTables(pool, B, w.table_stride, bs)
+        seqs.append(0, sp.prefix_tokens)
+        for b in range(1, B):
+            seqs.share(b, 0, sp.prefix_pages)
+        for b in range(B):
+            seqs.append(b, int(sp.suffix[b]))
+        return pool, seqs
+
+    table = torch.full((B, w.table_stride), -1, dtype=torch.int32, device=device)
+    pool, seqs = build_tables()
+    pkv.table_apply(table, seqs.take_updates().to(device))
+    prefix_refs = pool.refcount(seqs.table()[0][0])
+    cache = pkv.PagedKVCache(w.n_pages, bs, w.n_kv_heads, w.head_dim, w.kv_format, device=device)
+    for r in sp.fill_rounds():
+        cache.write(table, torch.as_tensor(r.start_pos).to(device),
+                    torch.as_tensor(r.cu_new).to(device), r.k.to(device), r.v.to(device))
+    ks, vs = sp.step_rows_all()
+    ks, vs = ks.to(device), vs.to(device)
+    qs = torch.stack([w.query(step=s) for s in range(sp.n_steps)]).to(device)
+    cu = torch.arange(B + 1, dtype=torch.int32, device=device)
+    lens_all = torch.stack([torch.as_tensor(sp.step_lens(s)) for s in range(sp.n_steps)]).to(device)
+    start_all = (lens_all - 1).contiguous()
+    max_len = int(sp.step_lens(sp.n_steps - 1).max())
+    split = cache.split_for(B, w.n_q_heads, max_len)
+    ws = cache.workspace(B, w.n_q_heads, max_len, split)
+    out = torch.empty_like(qs[0])
+    upd_host = torch.empty((B + 8, 3), dtype=torch.int32).pin_memory()
+    upd_dev = torch.empty((B + 8, 3), dtype=torch.int32, device=device)
+    torch.cuda.synchronize()
+
+    def job(seqs):
+        for s in range(sp.n_steps):
+            for b in range(B):
+                seqs.append(b, 1)
+            n = seqs.take_updates(upd_host).shape[0]
+            if n:
+                upd_dev[:n].copy_(upd_host[:n], non_blocking=True)
+                pkv.table_apply(table, upd_dev[:n])
+            cache.write(table, start_all[s], cu, ks[s], vs[s])
+            cache.attend(qs[s], table, lens_all[s], max_len, w.scale, out=out, workspace=ws,
+                         split_tokens=split)
+
+    jobs = max(1, args.steps)
+    times = []
+    for rep in range(args.warmup + jobs):
+        if rep:
+            seqs.close()
+            pool.close()
+            pool, seqs = build_tables()
+            table.fill_(-1)
+            pkv.table_apply(table, seqs.take_updates().to(device))
+        torch.cuda.synchronize()
+        if rep == args.warmup:
+            cache.timing_read()
+            cache.timing(True)
+        t0 = time.perf_counter()
+        job(seqs)
+        torch.cuda.synchronize()
+        if rep >= args.warmup:
+            times.append(time.perf_counter() - t0)
+        if rep == 0:
+            assert seqs.lens() == [int(x) for x in sp.step_lens(sp.n_steps - 1)]
+            assert cache.status() == 0
+    cache.timing(False)
+    t = cache.timing_read()
+    seqs.close()
+    pool.close()
+    job_s = float(np.mean(times))
+    lens_steps = [sp.step_lens(s).astype(np.int64) for s in range(sp.n_steps)]
+    per_tok = w.n_kv_heads * w.head_dim * 2 * 2
+    logical = sum(int(l.sum()) for l in lens_steps) * per_tok
+    unique = sum(int((l - sp.prefix_tokens).sum()) + sp.prefix_tokens for l in lens_steps) * per_tok
+    split_ms, split_n = t["attend_split"]
+    log(f"shared_prefix job: {job_s * 1e3:.3f} ms for {sp.n_steps} steps; split pass "
+        f"{split_ms / split_n * 1e3:.1f} us avg; prefix page refcount {prefix_refs}")
+    line = {
+        "metric": METRIC, "value": round(unique / job_s / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": jobs, "warmup": args.warmup, "ms_per_step": round(job_s * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "page_size": bs,
+                   "prefix_pages": sp.prefix_pages, "suffix": "uniform [16, 2048]",
+                   "step": f"one job = {sp.n_steps} decode steps (host table growth + "
+                           "paged_write 1 row/seq + paged_attend)",
+                   "split_tokens": split, "value_bytes": "unique KV bytes (shared prefix once)"},
+        "tokens_per_s": round(B * sp.n_steps / job_s, 1),
+        "logical_kv_GBps": round(logical / job_s / 1e9, 2),
+        "pct_hbm_peak": round(100 * unique / job_s / 1e9 / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": None, "traffic": None,
+                     "avg_launch_us": round(split_ms / split_n * 1e3, 2),
+                     "note": "split pass average over steps of different lengths"},
+        "cpu_baseline": None,
+    }
+    return line
 
 
 def main():
@@ -178,6 +337,8 @@ def main():
                     help="1: overwrite a 512 MiB buffer between timed steps (outside the events)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gather-compare", type=int, default=1,
+                    help="1: also time gathering every sequence into a contiguous copy")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -186,9 +347,10 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
     device = torch.device("cuda:0")
+    if args.workload == "shared_prefix":
+        print(json.dumps(run_shared_prefix(args, device)), flush=True)
+        return
     w = W.by_name(args.workload)
-    if isinstance(w, W.SharedPrefix):
-        raise SystemExit("the step benchmark takes a single-query-per-sequence workload")
     log(f"workload {w.name}: B={w.batch} lens={int(w.lens.min())}..{int(w.lens.max())} "
         f"Hq={w.n_q_heads} Hkv={w.n_kv_heads} D={w.head_dim} bs={w.page_size} P={w.n_pages}")
 
@@ -199,8 +361,9 @@ def main():
     cache = pkv.PagedKVCache(w.n_pages, w.page_size, w.n_kv_heads, w.head_dim, w.kv_format,
                              device=device)
     t0 = time.perf_counter()
-    table, ks, vs = fill(w, cache, device)
-    log(f"filled {kv_bytes(w) / 2**30:.2f} GiB of pages in {time.perf_counter() - t0:.1f} s")
+    table, ks, vs, fill_info = fill(w, cache, device)
+    log(f"filled {kv_bytes(w) / 2**30:.2f} GiB of pages in {time.perf_counter() - t0:.1f} s: "
+        f"{fill_info}")
 
     B = w.batch
     lens = torch.as_tensor(w.lens).to(device)
@@ -258,7 +421,7 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.kv_format,
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "seq_len": int(w.lens.max()),
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
@@ -270,11 +433,17 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "kv_bytes_per_step": kvb,
         "achievable_read_GBps": round(read_gbps, 1),
+        "fill_write": fill_info,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": "attend_mfma (split-K partial pass)",
                      "avg_launch_us": round(split_avg * 1e3, 2)},
     }
+    if args.gather_compare:
+        line["gather_compare"] = gather_compare(w, cache, table, device)
+        line["gather_compare"]["inplace_attend_us"] = round(
+            (split_avg + comb_ms / max(comb_n, 1)) * 1e3, 2)
+        log(f"gather compare: {line['gather_compare']}")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, ks, vs, q_host, args.cpu_seconds)
     else:

@@ -97,7 +97,7 @@ class Workload:
         q = torch.randn((self.batch, self.n_q_heads, self.head_dim), generator=g)
         return q.to(self.q_dtype)
 
-    def rounds(self, seqs: list[int] | None = None) -> list[WriteRound]:
+    def rounds(self, seqs: list[int] | None = None, kv: dict | None = None) -> list[WriteRound]:
         """The write rounds that fill every sequence to ``lens``.
 
         Single-round workloads write all rows from position 0 in one call.
@@ -105,7 +105,8 @@ class Workload:
         ``chunk`` rows, so every later round starts off a page boundary.
         """
         seqs = list(range(self.batch)) if seqs is None else seqs
-        kv = {b: self.seq_kv(b) for b in seqs}
+        if kv is None:
+            kv = {b: self.seq_kv(b) for b in seqs}
         bounds: list[list[tuple[int, int]]] = []
         for b in range(self.batch):
             L = int(self.lens[b])

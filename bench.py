@@ -254,7 +254,10 @@ def run_shared_prefix(args, device):
     split = cache.split_for(B, w.n_q_heads, max_len)
     ws = cache.workspace(B, w.n_q_heads, max_len, split)
     out = torch.empty_like(qs[0])
-    upd_host = torch.empty((B + 8, 3), dtype=torch.int32).pin_memory()
+    # one pinned buffer per step: a step's host-to-device copy may still be
+    # pending when the host prepares the next step's updates
+    upd_host = [torch.empty((B + 8, 3), dtype=torch.int32).pin_memory()
+                for _ in range(sp.n_steps)]
     upd_dev = torch.empty((B + 8, 3), dtype=torch.int32, device=device)
     torch.cuda.synchronize()
 
@@ -262,9 +265,9 @@ def run_shared_prefix(args, device):
         for s in range(sp.n_steps):
             for b in range(B):
                 seqs.append(b, 1)
-            n = seqs.take_updates(upd_host).shape[0]
+            n = seqs.take_updates(upd_host[s]).shape[0]
             if n:
-                upd_dev[:n].copy_(upd_host[:n], non_blocking=True)
+                upd_dev[:n].copy_(upd_host[s][:n], non_blocking=True)
                 pkv.table_apply(table, upd_dev[:n])
             cache.write(table, start_all[s], cu, ks[s], vs[s])
             cache.attend(qs[s], table, lens_all[s], max_len, w.scale, out=out, workspace=ws,

@@ -1,6 +1,6 @@
 // Paged decode attention, split-K partial pass, matrix-core (MFMA) version
-// for bf16 and int8 pages, head_dim 64 or 128, page sizes that are multiples
-// of 16 and query groups of up to 16 heads.
+// for bf16 and int8 pages, head_dim 64 or 128, page size 16 or a multiple of
+// 32, and query groups of up to 16 heads.
 //
 // What it computes is the same as the vector-ALU kernel: per (sequence b, KV
 // head g, split s) and per query head h of the group, the running maximum m
@@ -17,13 +17,15 @@
 // computed transposed, S^T = K Q^T, whose accumulator layout (lane = head +
 // 16 * token quad) is exactly the B-operand layout the P.V product needs, so
 // the softmax weights never move between lanes.  P.V is computed as
-// O^T = V^T P^T, with V read from the dim-major page slab (each lane loads 4
-// consecutive slots of one dim).  The reduction order of the P.V k-slots is
-// a fixed permutation of the 32 tokens of a step (tile 0 quad j, then tile 1
-// quad j), applied identically to P and V.  A step covers 32 tokens (two
-// 16-token tiles); the loads of step i+1 are issued before step i is
+// O^T = V^T P^T, with V read from the dim-major page slab.  Row r of score
+// tile t (t = 0, 1) holds token 8 * (r / 4) + 4 * t + r % 4 of the 32-token
+// step, so the accumulator lanes of k group j hold tokens 8j .. 8j+7 of the
+// step in order: the P.V k-slots are the tokens in their natural order and
+// each lane's V operand is 8 consecutive slots of one dim, one 16-byte load
+// (8 bytes for int8).  The loads of step i+1 are issued before step i is
 // computed.  int8 pages are converted to bf16 exactly (|code| <= 127); the
 // per-token K scale multiplies the score and the V scale the weight.
+#include <algorithm>
 #include <type_traits>
 
 #include "pkv_device.h"
@@ -39,19 +41,18 @@ template <int FMT, int D>
 struct Step {
   static constexpr int NC = D / 32;  // 32-wide k chunks of the Q.K product
   static constexpr int ND = D / 16;  // 16-row dim tiles of the P.V product
-  // bf16: 8 values per (tile, chunk); int8: 8 codes
+  // K: bf16 8 values / int8 8 codes per (tile, chunk); V: 8 tokens per dim tile
   using KT = typename std::conditional<FMT == PKV_FMT_BF16, uint4, uint2>::type;
-  // bf16: 4 values per (dim tile, tile); int8: 4 codes
-  using VT = typename std::conditional<FMT == PKV_FMT_BF16, uint2, uint32_t>::type;
+  using VT = KT;
   // the same bytes as raw 32-bit vectors, for non-temporal loads
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   using NKT = typename std::conditional<sizeof(KT) == 16, u32x4, u32x2>::type;
-  using NVT = typename std::conditional<sizeof(VT) == 8, u32x2, unsigned int>::type;
+  using NVT = NKT;
   KT k[2][NC];
-  VT v[ND][2];
-  f32x4 ks[2], vs[2];  // int8 only: scales of the lane's 4 tokens per tile
-  bool live[2];        // tile has a valid page and at least one token
+  VT v[ND];
+  f32x4 ks[2], vs[2];  // int8 only: scales of the lane's tokens 8j+4t .. 8j+4t+3
+  bool live_a, live_b;  // the step's first / second 16 tokens sit on a valid page
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -74,8 +75,63 @@ __device__ __forceinline__ uint2 codes_to_bf16(uint32_t w) {
   return r;
 }
 
+// Write 4 consecutive outputs (bf16 rounded to nearest even, or f32).
+__device__ __forceinline__ void store_out4(const AttendArgs& a, int64_t oi, f32x4 r) {
+  if (a.q_bf16) {
+    const uint2 w = {f32_to_bf16_bits(r[0]) | (f32_to_bf16_bits(r[1]) << 16),
+                     f32_to_bf16_bits(r[2]) | (f32_to_bf16_bits(r[3]) << 16)};
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oi) = w;
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + oi) = r;
+  }
+}
+
+// Combine the n split partials (m_s, l_s, o_s) of every query head of KV
+// group g of sequence b: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
+// merged split by split with a running maximum.  One lane per (head, 4 dims).
+template <int D>
+__device__ __forceinline__ void combine_group(const AttendArgs& a, int b, int g, int n, int lane) {
+  constexpr int Q4 = D / 4;
+  for (int idx = lane; idx < a.group * Q4; idx += 64) {
+    const int hh = idx / Q4, d4 = idx - hh * Q4;
+    const int64_t hrow = (int64_t)b * a.n_q_heads + (int64_t)g * a.group + hh;
+    const float* ml = a.ws_ml + hrow * a.n_split * 2;
+    const float* po = a.ws_o + hrow * a.n_split * D + 4 * d4;
+    float M = -INFINITY, L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + 4 <= n; s += 4) {
+      float2 x[4];
+      f32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        x[u] = *reinterpret_cast<const float2*>(ml + 2 * (s + u));
+        v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)(s + u) * D);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float Mn = fmaxf(M, x[u].x);
+        const float al = __builtin_amdgcn_exp2f(M - Mn), w = __builtin_amdgcn_exp2f(x[u].x - Mn);
+        acc = acc * al + v[u] * w;
+        L = L * al + x[u].y * w;
+        M = Mn;
+      }
+    }
+    for (; s < n; ++s) {
+      const float2 x = *reinterpret_cast<const float2*>(ml + 2 * s);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(po + (int64_t)s * D);
+      const float Mn = fmaxf(M, x.x);
+      const float al = __builtin_amdgcn_exp2f(M - Mn), w = __builtin_amdgcn_exp2f(x.x - Mn);
+      acc = acc * al + v * w;
+      L = L * al + x.y * w;
+      M = Mn;
+    }
+    store_out4(a, hrow * D + 4 * d4, acc * (1.f / L));
+  }
+}
+
 template <int FMT, int D, int BS>
-__global__ __launch_bounds__(64) void attend_mfma_kernel(AttendArgs a) {
+__global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
   using S = Step<FMT, D>;
   using KT = typename S::KT;
   using VT = typename S::VT;
@@ -84,15 +140,91 @@ __global__ __launch_bounds__(64) void attend_mfma_kernel(AttendArgs a) {
   const int lane = threadIdx.x;
   const int n = lane & 15;  // head column (B/C operands), row (A operands)
   const int j = lane >> 4;  // k group (A/B operands), row quad (C operand)
-  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.group;
   const int bs = BS ? BS : a.page_size;
+  const int C = a.split_tokens;
+  const int B = a.batch;
 
-  const int len = clamp_len(a.lens[b], a.max_len, sp == 0 && g == 0 ? a.status : nullptr,
-                            PKV_DEV_LEN);
-  const int t_begin = sp * a.split_tokens;
-  if (t_begin >= len) return;
-  const int t_end = min(t_begin + a.split_tokens, len);
+  // ---- work list (LDS): exclusive prefix sums over the sequences of their
+  // full splits and of their partial last splits, and the clamped lengths.
+  // Work items are (split, KV head) pairs, full splits first, so the longest
+  // items are handed out first; each workgroup takes items blockIdx.x,
+  // blockIdx.x + gridDim.x, ...
+  extern __shared__ int32_t wl[];
+  int32_t* fpre = wl;            // [B + 1]
+  int32_t* qpre = wl + B + 1;    // [B + 1]
+  int32_t* lens = wl + 2 * B + 2;  // [B]
+  {
+    int carry_f = 0, carry_q = 0;
+    for (int b0 = 0; b0 < B; b0 += 256) {
+      int lv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int bb = b0 + 64 * u + lane;
+        lv[u] = bb < B ? a.lens[bb] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int bb = b0 + 64 * u + lane;
+        const int len = clamp_len(lv[u], a.max_len, blockIdx.x == 0 ? a.status : nullptr,
+                                  PKV_DEV_LEN);
+        const int f = bb < B ? len / C : 0;
+        const int q = bb < B && len % C != 0 ? 1 : 0;
+        int sf = f, sq = q;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int tf = __shfl_up(sf, o, 64), tq = __shfl_up(sq, o, 64);
+          if (lane >= o) {
+            sf += tf;
+            sq += tq;
+          }
+        }
+        if (bb < B) {
+          fpre[bb] = carry_f + sf - f;
+          qpre[bb] = carry_q + sq - q;
+          lens[bb] = len;
+        }
+        carry_f += __shfl(sf, 63, 64);
+        carry_q += __shfl(sq, 63, 64);
+      }
+    }
+    if (lane == 0) {
+      fpre[B] = carry_f;
+      qpre[B] = carry_q;
+    }
+  }
+  __syncthreads();
+  const int n_full = fpre[B];
+  const int n_items = (n_full + qpre[B]) * a.n_kv_heads;
+
+  // sequences with no tokens have no work item: their output is zero
+  for (int b = blockIdx.x; b < B; b += gridDim.x) {
+    if (lens[b] != 0) continue;
+    for (int i = lane; i < a.n_q_heads * D / 4; i += 64)
+      store_out4(a, (int64_t)b * a.n_q_heads * D + 4 * i, f32x4{0.f, 0.f, 0.f, 0.f});
+  }
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  const int pair = item / a.n_kv_heads;
+  const int g = item - pair * a.n_kv_heads;
+  int b, sp;
+  {
+    // largest b whose prefix is <= the index: that sequence owns it
+    const int32_t* pre = pair < n_full ? fpre : qpre;
+    const int idx = pair < n_full ? pair : pair - n_full;
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= idx) lo = mid;
+      else hi = mid - 1;
+    }
+    b = lo;
+    sp = pair < n_full ? idx - fpre[b] : fpre[b + 1] - fpre[b];
+  }
+  const int len = lens[b];
+  const int n_splits_b = (len + C - 1) / C;
+  const int t_begin = sp * C;
+  const int t_end = min(t_begin + C, len);
 
   // ---- query group as the B operand of S^T = K Q^T (zeros past the group) ----
   bf16x8 qf[NC];
@@ -135,39 +267,53 @@ __global__ __launch_bounds__(64) void attend_mfma_kernel(AttendArgs a) {
       }
     }
 
-    // Loads are unconditional: a tile with no page (past the length or a bad
-    // entry) reads page 0 of the array instead and is masked afterwards, so
-    // the compiler can keep the next step's loads in flight.
+    // Loads are unconditional: a 16-token half with no page (past the length
+    // or a bad entry) reads page 0 of the array instead and is masked
+    // afterwards, so the compiler can keep the next step's loads in flight.
+    // With 16-token pages a step spans pages A (tokens 0-15) and B (16-31);
+    // with larger pages both halves sit on page A.
     auto load_step = [&](int ts, S& r) {
+      const int lp = ts / bs;
+      const int page_a = ts < w_end ? __builtin_amdgcn_readlane(vpage, lp - pg0) : -1;
+      int page_b = page_a;
+      if (BS == 16) page_b = ts + 16 < w_end ? __builtin_amdgcn_readlane(vpage, lp + 1 - pg0) : -1;
+      r.live_a = page_a >= 0;
+      r.live_b = page_b >= 0;
+      const int slot0 = ts - lp * bs;  // 0 for 16-token pages
+      const int64_t slab_a = (a.layer_page0 + (page_a >= 0 ? page_a : 0)) * a.n_kv_heads + g;
+      const int64_t slab_b = (a.layer_page0 + (page_b >= 0 ? page_b : 0)) * a.n_kv_heads + g;
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        const int tb = ts + 16 * tau;
-        const int lp = tb / bs;
-        const int page = tb < w_end ? __builtin_amdgcn_readlane(vpage, lp - pg0) : -1;
-        r.live[tau] = page >= 0;
-        const int slot0 = tb - lp * bs;
-        const int64_t slab = (a.layer_page0 + (page >= 0 ? page : 0)) * a.n_kv_heads + g;
-        const char* kslab = kp + slab * slab_bytes;  // uniform
-        const char* vslab = vp + slab * slab_bytes;
-        const int koff = ((slot0 + n) * D + 8 * j) * ESZ;
+        // this lane's K row: token 8 * (n / 4) + 4 * tau + n % 4 of the step
+        const int tok = 8 * (n >> 2) + 4 * tau + (n & 3);
+        const bool on_b = BS == 16 && tok >= 16;
+        const char* kb = kp + (on_b ? slab_b : slab_a) * slab_bytes;
+        const int row = BS == 16 ? (tok & 15) : slot0 + tok;
+        const int koff = (row * D + 8 * j) * ESZ;
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-          r.k[tau][c] = stream_load<KT, typename S::NKT>(kslab + koff + 32 * c * ESZ);
-        const int voff = (n * bs + slot0 + 4 * j) * ESZ;
+          r.k[tau][c] = stream_load<KT, typename S::NKT>(kb + koff + 32 * c * ESZ);
+      }
+      // V operand: tokens 8j .. 8j+7 of dim 16 * dt + n
+      const bool v_on_b = BS == 16 && j >= 2;
+      const char* vb = vp + (v_on_b ? slab_b : slab_a) * slab_bytes;
+      const int col = BS == 16 ? 8 * (j & 1) : slot0 + 8 * j;
+      const int voff = (n * bs + col) * ESZ;
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt)
-          r.v[dt][tau] = stream_load<VT, typename S::NVT>(vslab + voff + 16 * dt * bs * ESZ);
-        if (FMT == PKV_FMT_INT8) {
-          const float* kss = a.k_scales + slab * bs;
-          const float* vss = a.v_scales + slab * bs;
-          r.ks[tau] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kss + slot0 + 4 * j));
-          r.vs[tau] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(vss + slot0 + 4 * j));
+      for (int dt = 0; dt < ND; ++dt)
+        r.v[dt] = stream_load<VT, typename S::NVT>(vb + voff + 16 * dt * bs * ESZ);
+      if (FMT == PKV_FMT_INT8) {
+        const int64_t ss = (v_on_b ? slab_b : slab_a) * bs + col;
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+          r.ks[tau] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.k_scales + ss + 4 * tau));
+          r.vs[tau] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.v_scales + ss + 4 * tau));
         }
       }
     };
 
     auto compute_step = [&](int ts, S& r) {
-      // S^T tiles: rows = tokens 16*tau + 4j + i, columns = heads
+      // S^T tiles: accumulator row 4j + i of tile tau = token 8j + 4 * tau + i
       f32x4 sacc[2];
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
@@ -184,20 +330,18 @@ __global__ __launch_bounds__(64) void attend_mfma_kernel(AttendArgs a) {
           sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[c], sacc[tau], 0, 0, 0);
         }
       }
+      const bool lane_live = BS == 16 && j >= 2 ? r.live_b : r.live_a;
       float sv[8];
-      bool ok[8];
+      bool ok[8];  // token 8j + x of the step is real
       float mx = -INFINITY;
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = ts + 16 * tau + 4 * j + i;
-          ok[4 * tau + i] = r.live[tau] && t < w_end;
-          float x = sacc[tau][i] * qs;
-          if (FMT == PKV_FMT_INT8) x *= r.ks[tau][i];
-          sv[4 * tau + i] = ok[4 * tau + i] ? x : -INFINITY;
-          mx = fmaxf(mx, sv[4 * tau + i]);
-        }
+      for (int x = 0; x < 8; ++x) {
+        ok[x] = lane_live && ts + 8 * j + x < w_end;
+        float y = sacc[x >> 2][x & 3] * qs;
+        if (FMT == PKV_FMT_INT8) y *= r.ks[x >> 2][x & 3];
+        sv[x] = ok[x] ? y : -INFINITY;
+        mx = fmaxf(mx, sv[x]);
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m, mx);
@@ -206,37 +350,34 @@ __global__ __launch_bounds__(64) void attend_mfma_kernel(AttendArgs a) {
       float psum = 0.f;
       bf16x8 pb;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p = ok[i] ? __builtin_amdgcn_exp2f(sv[i] - m_use) : 0.f;
+      for (int x = 0; x < 8; ++x) {
+        const float p = ok[x] ? __builtin_amdgcn_exp2f(sv[x] - m_use) : 0.f;
         psum += p;
         float pw = p;
-        if (FMT == PKV_FMT_INT8) pw = ok[i] ? p * r.vs[i >> 2][i & 3] : 0.f;
-        pb[i] = (__bf16)pw;
+        if (FMT == PKV_FMT_INT8) pw = ok[x] ? p * r.vs[x >> 2][x & 3] : 0.f;
+        pb[x] = (__bf16)pw;
       }
       l = l * alpha + psum;
       m = m_new;
       // V^T A operands.  Where a slot of the step is dead (past the length or
       // on a missing page) zero its bf16 value: it may hold NaN, and 0 * NaN
       // would reach the sum.  int8 codes are finite and carry weight 0 there.
-      const bool mask_v = FMT == PKV_FMT_BF16 && (ts + 32 > w_end || !r.live[0] || !r.live[1]);
-      uint32_t keep[2][2] = {{~0u, ~0u}, {~0u, ~0u}};
+      const bool mask_v = FMT == PKV_FMT_BF16 && (ts + 32 > w_end || !r.live_a || !r.live_b);
+      uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
       if (mask_v) {
 #pragma unroll
-        for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-          for (int w = 0; w < 2; ++w)
-            keep[tau][w] = (ok[4 * tau + 2 * w] ? 0x0000ffffu : 0u) |
-                           (ok[4 * tau + 2 * w + 1] ? 0xffff0000u : 0u);
+        for (int w = 0; w < 4; ++w)
+          keep[w] = (ok[2 * w] ? 0x0000ffffu : 0u) | (ok[2 * w + 1] ? 0xffff0000u : 0u);
       }
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) {
         o[dt] *= alpha;
         uint4 va;
         if constexpr (FMT == PKV_FMT_BF16) {
-          va = uint4{r.v[dt][0].x & keep[0][0], r.v[dt][0].y & keep[0][1],
-                     r.v[dt][1].x & keep[1][0], r.v[dt][1].y & keep[1][1]};
+          va = uint4{r.v[dt].x & keep[0], r.v[dt].y & keep[1], r.v[dt].z & keep[2],
+                     r.v[dt].w & keep[3]};
         } else {
-          const uint2 lo = codes_to_bf16(r.v[dt][0]), hi = codes_to_bf16(r.v[dt][1]);
+          const uint2 lo = codes_to_bf16(r.v[dt].x), hi = codes_to_bf16(r.v[dt].y);
           va = uint4{lo.x, lo.y, hi.x, hi.y};
         }
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pb, o[dt], 0, 0, 0);
@@ -258,31 +399,78 @@ __global__ __launch_bounds__(64) void attend_mfma_kernel(AttendArgs a) {
     }
   }
 
-  // ---- partial results: O^T lane layout = dims 16*dt + 4j + i of head n ----
+  // ---- results: O^T lane layout = dims 16*dt + 4j + i of head n ----
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  if (n < G) {
-    const int64_t row = ((int64_t)b * a.n_q_heads + (int64_t)g * G + n) * a.n_split + sp;
-    float* wo = a.ws_o + row * D + 4 * j;
+  const int64_t hrow = (int64_t)b * a.n_q_heads + (int64_t)g * G + n;  // (b, h) row
+  if (n_splits_b == 1) {
+    // the only split of the sequence: normalise and write the output here
+    if (n < G) {
+      const float inv = 1.f / l;
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) *reinterpret_cast<f32x4*>(wo + 16 * dt) = o[dt];
-    if (j == 0) {
-      a.ws_ml[row * 2] = m;
-      a.ws_ml[row * 2 + 1] = l;
+      for (int dt = 0; dt < ND; ++dt)
+        store_out4(a, hrow * D + 16 * dt + 4 * j, o[dt] * inv);
+    }
+  } else {
+    if (n < G) {
+      const int64_t row = hrow * a.n_split + sp;
+      float* wo = a.ws_o + row * D + 4 * j;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) *reinterpret_cast<f32x4*>(wo + 16 * dt) = o[dt];
+      if (j == 0) *reinterpret_cast<float2*>(a.ws_ml + row * 2) = float2{m, l};
+    }
+    // Publish the partials, then count this split in; the workgroup that
+    // brings the count to the sequence's number of splits combines them
+    // (agent-scope release / acquire: the partials may come from other XCDs).
+    __threadfence();
+    unsigned old = 0;
+    uint32_t* counter = a.counters + (int64_t)b * a.n_kv_heads + g;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0, 64);
+    if (old == (unsigned)(n_splits_b - 1)) {
+      __threadfence();
+      combine_group<D>(a, b, g, n_splits_b, lane);
+      if (lane == 0) *counter = 0u;  // ready for the next call
     }
   }
+  }  // work items
+}
+
+// Persistent launch: as many workgroups as the chip holds at once for this
+// kernel (occupancy x compute units), capped by the number of work items
+// the host can bound (every sequence at max_len).
+template <typename K>
+int resident_workgroups(K kernel, size_t lds) {
+  static thread_local int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64, lds) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  return per_cu * cus;
+}
+
+template <int FMT, int D, int BS>
+hipError_t launch_bs(const AttendArgs& a, hipStream_t s) {
+  auto kernel = attend_mfma_kernel<FMT, D, BS>;
+  const size_t lds = (size_t)(3 * a.batch + 2) * sizeof(int32_t);
+  const int64_t bound = (int64_t)a.n_kv_heads * a.batch * a.n_split;
+  const int64_t grid = std::min<int64_t>(bound, resident_workgroups(kernel, lds));
+  hipLaunchKernelGGL(kernel, dim3((unsigned)std::max<int64_t>(grid, 1)), dim3(64), lds, s, a);
+  return hipGetLastError();
 }
 
 template <int FMT, int D>
 hipError_t launch_d(const AttendArgs& a, hipStream_t s) {
-  dim3 grid(a.n_split, a.n_kv_heads, a.batch);
-  if (a.page_size == 16)
-    hipLaunchKernelGGL((attend_mfma_kernel<FMT, D, 16>), grid, dim3(64), 0, s, a);
-  else if (a.page_size == 32)
-    hipLaunchKernelGGL((attend_mfma_kernel<FMT, D, 32>), grid, dim3(64), 0, s, a);
-  else
-    hipLaunchKernelGGL((attend_mfma_kernel<FMT, D, 0>), grid, dim3(64), 0, s, a);
-  return hipGetLastError();
+  if (a.page_size == 16) return launch_bs<FMT, D, 16>(a, s);
+  if (a.page_size == 32) return launch_bs<FMT, D, 32>(a, s);
+  return launch_bs<FMT, D, 0>(a, s);
 }
 
 template <int FMT>
@@ -292,13 +480,14 @@ hipError_t launch_fmt(const AttendArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool mfma_supported(int fmt, int q_bf16, int head_dim, int page_size, int group) {
+bool mfma_supported(int fmt, int q_bf16, int head_dim, int page_size, int group, int batch) {
   return (fmt == PKV_FMT_BF16 || fmt == PKV_FMT_INT8) && q_bf16 &&
-         (head_dim == 64 || head_dim == 128) && page_size % 16 == 0 && group >= 1 && group <= 16;
+         (head_dim == 64 || head_dim == 128) && (page_size == 16 || page_size % 32 == 0) &&
+         group >= 1 && group <= 16 && batch >= 1 && batch <= kMaxMfmaBatch;
 }
 
 hipError_t launch_attend_mfma(const AttendArgs& a, int fmt, hipStream_t s) {
-  if (!mfma_supported(fmt, a.q_bf16, a.head_dim, a.page_size, a.group))
+  if (!mfma_supported(fmt, a.q_bf16, a.head_dim, a.page_size, a.group, a.batch))
     return hipErrorNotSupported;
   return fmt == PKV_FMT_BF16 ? launch_fmt<PKV_FMT_BF16>(a, s) : launch_fmt<PKV_FMT_INT8>(a, s);
 }

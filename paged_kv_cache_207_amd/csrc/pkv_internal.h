@@ -54,6 +54,7 @@ struct AttendArgs {
   const int32_t* lens;
   float* ws_o;   // [batch][n_q_heads][n_split][head_dim] unnormalised partial outputs
   float* ws_ml;  // [batch][n_q_heads][n_split][2] running max (log2 units) and sum
+  uint32_t* counters;  // [batch][n_kv_heads] splits finished (zero between calls)
   int64_t layer_page0;
   float qk_scale_log2;  // softmax scale * log2(e)
   int32_t n_pages, page_size, n_kv_heads, head_dim, n_q_heads, group;
@@ -83,9 +84,11 @@ inline int format_bytes(int fmt) { return fmt == PKV_FMT_F32 ? 4 : fmt == PKV_FM
 hipError_t launch_write(const WriteArgs& a, int fmt, int in_dtype, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, int fmt, hipStream_t s);
 hipError_t launch_attend_valu(const AttendArgs& a, int fmt, hipStream_t s);
+// The matrix-core kernel also combines the splits itself (no reduce launch).
 // Returns hipErrorNotSupported when the shape has no matrix-core variant.
 hipError_t launch_attend_mfma(const AttendArgs& a, int fmt, hipStream_t s);
-bool mfma_supported(int fmt, int q_bf16, int head_dim, int page_size, int group);
+constexpr int kMaxMfmaBatch = 4096;  // the work list lives in LDS: 12 bytes per sequence
+bool mfma_supported(int fmt, int q_bf16, int head_dim, int page_size, int group, int batch);
 hipError_t launch_reduce(const AttendArgs& a, hipStream_t s);
 hipError_t launch_probe(const void* src, void* dst, float* sink, uint64_t bytes, int mode,
                         hipStream_t s);

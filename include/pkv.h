@@ -143,10 +143,9 @@ int pkv_attend_workspace_size(const pkv_cache* cache, int32_t batch, int32_t n_q
  * begin_step masks positions <= the pre-step length).  lens[b] = 0 gives
  * zeros.  Work is split over tokens in partitions of split_tokens (0 =
  * automatic) and the partial results (running max, sum and weighted V) are
- * combined (by the matrix-core kernel itself, through per-(sequence, KV
- * head) counters in the workspace, or by a second kernel on the vector-ALU
- * path); the result of a sequence depends only on its own tokens and the
- * split size.
+ * combined by a second kernel (a sequence that fits in one split is
+ * finished by the first); the result of a sequence depends only on its own
+ * tokens and the split size.
  *   q          device [batch][n_q_heads][head_dim] of q_dtype; out has the
  *              same shape and dtype (bf16 rounded to nearest even).
  *   table      device int32 [batch][table_stride].
@@ -154,11 +153,8 @@ int pkv_attend_workspace_size(const pkv_cache* cache, int32_t batch, int32_t n_q
  *              at most table_stride * page_size (ERANGE otherwise).
  *   scale      softmax scale (float32).
  *   workspace  device scratch of at least pkv_attend_workspace_size bytes
- *              (ENOMEM otherwise), 256-byte aligned.  Its tail holds split
- *              counters that must be zero before the first call (zero the
- *              whole buffer once); every completed call leaves them zero,
- *              so one workspace serves call after call on one stream.
- *              Calls that may overlap need separate workspaces.
+ *              (ENOMEM otherwise), 256-byte aligned; no initial contents are
+ *              needed.  Calls that may overlap need separate workspaces.
  *   flags      0 or PKV_ATTEND_VALU.
  * The matrix-core kernel serves bf16/int8 pages with a bf16 query, head_dim
  * 64 or 128, page_size 16 or a multiple of 32, up to 16 query heads per KV

@@ -25,6 +25,12 @@
 // (8 bytes for int8).  The loads of step i+1 are issued before step i is
 // computed.  int8 pages are converted to bf16 exactly (|code| <= 127); the
 // per-token K scale multiplies the score and the V scale the weight.
+//
+// Work distribution: a persistent grid (as many single-wave workgroups as
+// the chip holds at once) walks a work list of (split, KV head) items built
+// in LDS from the lengths, full splits first.  A sequence that fits in one
+// split gets its output written here; the partials of longer sequences are
+// combined by the combine kernel, which skips the single-split sequences.
 #include <algorithm>
 #include <type_traits>
 
@@ -83,50 +89,6 @@ __device__ __forceinline__ void store_out4(const AttendArgs& a, int64_t oi, f32x
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oi) = w;
   } else {
     *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + oi) = r;
-  }
-}
-
-// Combine the n split partials (m_s, l_s, o_s) of every query head of KV
-// group g of sequence b: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
-// merged split by split with a running maximum.  One lane per (head, 4 dims).
-template <int D>
-__device__ __forceinline__ void combine_group(const AttendArgs& a, int b, int g, int n, int lane) {
-  constexpr int Q4 = D / 4;
-  for (int idx = lane; idx < a.group * Q4; idx += 64) {
-    const int hh = idx / Q4, d4 = idx - hh * Q4;
-    const int64_t hrow = (int64_t)b * a.n_q_heads + (int64_t)g * a.group + hh;
-    const float* ml = a.ws_ml + hrow * a.n_split * 2;
-    const float* po = a.ws_o + hrow * a.n_split * D + 4 * d4;
-    float M = -INFINITY, L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    int s = 0;
-    for (; s + 4 <= n; s += 4) {
-      float2 x[4];
-      f32x4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        x[u] = *reinterpret_cast<const float2*>(ml + 2 * (s + u));
-        v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)(s + u) * D);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float Mn = fmaxf(M, x[u].x);
-        const float al = __builtin_amdgcn_exp2f(M - Mn), w = __builtin_amdgcn_exp2f(x[u].x - Mn);
-        acc = acc * al + v[u] * w;
-        L = L * al + x[u].y * w;
-        M = Mn;
-      }
-    }
-    for (; s < n; ++s) {
-      const float2 x = *reinterpret_cast<const float2*>(ml + 2 * s);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(po + (int64_t)s * D);
-      const float Mn = fmaxf(M, x.x);
-      const float al = __builtin_amdgcn_exp2f(M - Mn), w = __builtin_amdgcn_exp2f(x.x - Mn);
-      acc = acc * al + v * w;
-      L = L * al + x.y * w;
-      M = Mn;
-    }
-    store_out4(a, hrow * D + 4 * d4, acc * (1.f / L));
   }
 }
 
@@ -384,18 +346,27 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
       }
     };
 
-    // ---- two register sets, loads one step ahead ----
+    // ---- two register sets, loads one step ahead.  The loop body issues its
+    // prefetches unconditionally and the last one or two steps are peeled:
+    // a load under a condition would make the compiler wait for every
+    // outstanding load (the prefetch included) before each step.
     const int n_steps = (w_end - w0 + 31) / 32;
     S r0, r1;
     load_step(w0, r0);
-    for (int st = 0; st < n_steps; st += 2) {
+    int st = 0;
+    for (; st + 2 < n_steps; st += 2) {
       const int ts = w0 + 32 * st;
-      if (st + 1 < n_steps) load_step(ts + 32, r1);
+      load_step(ts + 32, r1);
       compute_step(ts, r0);
-      if (st + 1 < n_steps) {
-        if (st + 2 < n_steps) load_step(ts + 64, r0);
-        compute_step(ts + 32, r1);
-      }
+      load_step(ts + 64, r0);
+      compute_step(ts + 32, r1);
+    }
+    if (st + 1 < n_steps) {
+      load_step(w0 + 32 * (st + 1), r1);
+      compute_step(w0 + 32 * st, r0);
+      compute_step(w0 + 32 * (st + 1), r1);
+    } else {
+      compute_step(w0 + 32 * st, r0);
     }
   }
 
@@ -411,28 +382,13 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
       for (int dt = 0; dt < ND; ++dt)
         store_out4(a, hrow * D + 16 * dt + 4 * j, o[dt] * inv);
     }
-  } else {
-    if (n < G) {
-      const int64_t row = hrow * a.n_split + sp;
-      float* wo = a.ws_o + row * D + 4 * j;
+  } else if (n < G) {
+    // one of several splits: leave the partial for the combine kernel
+    const int64_t row = hrow * a.n_split + sp;
+    float* wo = a.ws_o + row * D + 4 * j;
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) *reinterpret_cast<f32x4*>(wo + 16 * dt) = o[dt];
-      if (j == 0) *reinterpret_cast<float2*>(a.ws_ml + row * 2) = float2{m, l};
-    }
-    // Publish the partials, then count this split in; the workgroup that
-    // brings the count to the sequence's number of splits combines them
-    // (agent-scope release / acquire: the partials may come from other XCDs).
-    __threadfence();
-    unsigned old = 0;
-    uint32_t* counter = a.counters + (int64_t)b * a.n_kv_heads + g;
-    if (lane == 0)
-      old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    old = __shfl(old, 0, 64);
-    if (old == (unsigned)(n_splits_b - 1)) {
-      __threadfence();
-      combine_group<D>(a, b, g, n_splits_b, lane);
-      if (lane == 0) *counter = 0u;  // ready for the next call
-    }
+    for (int dt = 0; dt < ND; ++dt) *reinterpret_cast<f32x4*>(wo + 16 * dt) = o[dt];
+    if (j == 0) *reinterpret_cast<float2*>(a.ws_ml + row * 2) = float2{m, l};
   }
   }  // work items
 }

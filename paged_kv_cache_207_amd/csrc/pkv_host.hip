@@ -62,19 +62,16 @@ int check_split(const pkv_cache* c, int32_t split) {
   return PKV_OK;
 }
 
-// Workspace: split partials o [B][Hq][S][D] f32, (m, l) [B][Hq][S][2] f32,
-// then the per-(sequence, KV head) split counters [B][Hkv] u32, which must be
-// zero before the first call and are left zero by every call.
+// Workspace: split partials o [B][Hq][S][D] f32, then (m, l) [B][Hq][S][2] f32.
 struct WsLayout {
-  uint64_t ml_off, cnt_off, total;
+  uint64_t ml_off, total;
 };
 
-WsLayout ws_layout(int batch, int n_q_heads, int n_kv_heads, int head_dim, int n_split) {
+WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_split) {
   WsLayout w;
   const uint64_t rows = (uint64_t)batch * n_q_heads * n_split;
   w.ml_off = (rows * head_dim * sizeof(float) + 255) / 256 * 256;
-  w.cnt_off = (w.ml_off + rows * 2 * sizeof(float) + 255) / 256 * 256;
-  w.total = w.cnt_off + (uint64_t)batch * n_kv_heads * sizeof(uint32_t);
+  w.total = w.ml_off + rows * 2 * sizeof(float);
   return w;
 }
 
@@ -252,7 +249,7 @@ int pkv_attend_workspace_size(const pkv_cache* c, int32_t batch, int32_t n_q_hea
   if (n_split > kMaxSplits)
     return fail(PKV_EINVAL, "%d splits of %d tokens exceed %d per sequence", n_split, split,
                 kMaxSplits);
-  *bytes = ws_layout(batch, n_q_heads, c->L.n_kv_heads, c->L.head_dim, n_split).total;
+  *bytes = ws_layout(batch, n_q_heads, c->L.head_dim, n_split).total;
   return PKV_OK;
 }
 
@@ -286,7 +283,7 @@ int pkv_paged_attend(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype
   if (n_split > kMaxSplits)
     return fail(PKV_EINVAL, "%d splits of %d tokens exceed %d per sequence", n_split, split,
                 kMaxSplits);
-  const WsLayout w = ws_layout(batch, n_q_heads, c->L.n_kv_heads, c->L.head_dim, n_split);
+  const WsLayout w = ws_layout(batch, n_q_heads, c->L.head_dim, n_split);
   if (workspace_bytes < w.total)
     return fail(PKV_ENOMEM, "workspace holds %llu bytes, %llu needed",
                 (unsigned long long)workspace_bytes, (unsigned long long)w.total);
@@ -303,7 +300,6 @@ int pkv_paged_attend(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype
   a.lens = lens;
   a.ws_o = static_cast<float*>(workspace);
   a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.ml_off);
-  a.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + w.cnt_off);
   a.layer_page0 = (int64_t)layer * c->L.n_pages;
   a.qk_scale_log2 = scale * pkv::kLog2eHost;
   a.n_pages = c->L.n_pages;
@@ -318,18 +314,19 @@ int pkv_paged_attend(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype
   a.split_tokens = split;
   a.n_split = n_split;
   a.q_bf16 = q_dtype == PKV_DT_BF16;
+  a.single_done = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   const bool mfma = !(flags & PKV_ATTEND_VALU) &&
                     pkv::mfma_supported(c->L.format, a.q_bf16, a.head_dim, a.page_size, a.group,
                                         batch);
+  a.single_done = mfma && max_len > 0;
   if (max_len > 0) {
     Timer tm(c, PKV_T_ATTEND_SPLIT, s);
     e = mfma ? pkv::launch_attend_mfma(a, c->L.format, s)
              : pkv::launch_attend_valu(a, c->L.format, s);
     tm.stop();
     if (e != hipSuccess) return fail(PKV_EHIP, "attend launch failed: %s", hipGetErrorString(e));
-    if (mfma) return PKV_OK;  // the matrix-core kernel combined the splits itself
   }
   Timer tm(c, PKV_T_ATTEND_COMBINE, s);
   e = pkv::launch_reduce(a, s);

@@ -54,12 +54,12 @@ struct AttendArgs {
   const int32_t* lens;
   float* ws_o;   // [batch][n_q_heads][n_split][head_dim] unnormalised partial outputs
   float* ws_ml;  // [batch][n_q_heads][n_split][2] running max (log2 units) and sum
-  uint32_t* counters;  // [batch][n_kv_heads] splits finished (zero between calls)
   int64_t layer_page0;
   float qk_scale_log2;  // softmax scale * log2(e)
   int32_t n_pages, page_size, n_kv_heads, head_dim, n_q_heads, group;
   int32_t table_stride, batch, max_len, split_tokens, n_split;
   int32_t q_bf16;  // 1: q and out are bf16, 0: float32
+  int32_t single_done;  // 1: the split pass wrote the output of single-split sequences
 };
 
 struct GatherArgs {
@@ -84,7 +84,6 @@ inline int format_bytes(int fmt) { return fmt == PKV_FMT_F32 ? 4 : fmt == PKV_FM
 hipError_t launch_write(const WriteArgs& a, int fmt, int in_dtype, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, int fmt, hipStream_t s);
 hipError_t launch_attend_valu(const AttendArgs& a, int fmt, hipStream_t s);
-// The matrix-core kernel also combines the splits itself (no reduce launch).
 // Returns hipErrorNotSupported when the shape has no matrix-core variant.
 hipError_t launch_attend_mfma(const AttendArgs& a, int fmt, hipStream_t s);
 constexpr int kMaxMfmaBatch = 4096;  // the work list lives in LDS: 12 bytes per sequence

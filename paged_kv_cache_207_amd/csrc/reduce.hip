@@ -26,6 +26,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
   int len = a.lens[b];
   len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
   const int n = (len + a.split_tokens - 1) / a.split_tokens;
+  if (a.single_done && n == 1) return;  // the split pass wrote this output
   const int64_t row0 = (int64_t)bh * a.n_split;
   const float* ml = a.ws_ml + row0 * 2;
 

@@ -194,10 +194,8 @@ class PagedKVCache:
         return out.value
 
     def workspace(self, batch, n_q_heads, max_len, split_tokens=0) -> torch.Tensor:
-        """A zeroed workspace (its split counters must start at zero; every
-        call leaves them zero, so the buffer can be reused call after call)."""
         n = self.workspace_size(batch, n_q_heads, max_len, split_tokens)
-        return torch.zeros(max(n, 1), dtype=torch.uint8, device=self.device)
+        return torch.empty(max(n, 1), dtype=torch.uint8, device=self.device)
 
     def attend(self, q, table, lens, max_len: int, scale: float, out=None, workspace=None,
                split_tokens: int = 0, flags: int = 0, layer: int = 0) -> torch.Tensor:

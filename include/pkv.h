@@ -74,6 +74,8 @@ typedef enum { PKV_DT_F32 = 0, PKV_DT_BF16 = 1 } pkv_dtype;
 
 /* pkv_paged_attend flags */
 #define PKV_ATTEND_VALU 1u /* force the vector-ALU kernel even where the matrix-core one applies */
+#define PKV_ATTEND_COMBINE_KERNEL 2u /* matrix-core path: combine splits in a second kernel */
+#define PKV_ATTEND_COMBINE_FUSED 4u  /* matrix-core path: combine splits in the split pass */
 
 typedef struct pkv_layout {
   int32_t n_layers;
@@ -125,7 +127,9 @@ int pkv_paged_write(pkv_cache* cache, int32_t layer, const int32_t* table, int32
                     int32_t format, void* stream);
 
 /* Split size (tokens per split-K partition) that pkv_paged_attend uses when
- * called with split_tokens = 0; a multiple of 64 and of page_size. */
+ * called with split_tokens = 0: 1024 tokens (2048 when max_len > 16384),
+ * halved down to 256 while batch * n_kv_heads * splits < 512; rounded up to
+ * a multiple of 64 and of page_size. */
 int pkv_attend_split(const pkv_cache* cache, int32_t batch, int32_t n_q_heads, int32_t max_len,
                      int32_t* split_tokens);
 
@@ -143,9 +147,10 @@ int pkv_attend_workspace_size(const pkv_cache* cache, int32_t batch, int32_t n_q
  * begin_step masks positions <= the pre-step length).  lens[b] = 0 gives
  * zeros.  Work is split over tokens in partitions of split_tokens (0 =
  * automatic) and the partial results (running max, sum and weighted V) are
- * combined by a second kernel (a sequence that fits in one split is
- * finished by the first); the result of a sequence depends only on its own
- * tokens and the split size.
+ * combined by a second kernel or, on the matrix-core path with
+ * PKV_ATTEND_COMBINE_FUSED, by the workgroup that finishes a sequence's last
+ * split (through counters in the workspace).  The result of a sequence
+ * depends only on its own tokens, the split size and that choice.
  *   q          device [batch][n_q_heads][head_dim] of q_dtype; out has the
  *              same shape and dtype (bf16 rounded to nearest even).
  *   table      device int32 [batch][table_stride].
@@ -153,12 +158,18 @@ int pkv_attend_workspace_size(const pkv_cache* cache, int32_t batch, int32_t n_q
  *              at most table_stride * page_size (ERANGE otherwise).
  *   scale      softmax scale (float32).
  *   workspace  device scratch of at least pkv_attend_workspace_size bytes
- *              (ENOMEM otherwise), 256-byte aligned; no initial contents are
- *              needed.  Calls that may overlap need separate workspaces.
- *   flags      0 or PKV_ATTEND_VALU.
+ *              (ENOMEM otherwise), 256-byte aligned.  Its first 1 MiB holds
+ *              split counters that must be zero before the first call: zero
+ *              the buffer once.  Every completed call leaves them zero, so
+ *              one workspace (large enough for the biggest call) serves
+ *              calls of any shape on one stream; calls that may overlap need
+ *              separate workspaces.
+ *   flags      0, or PKV_ATTEND_VALU, and/or one of PKV_ATTEND_COMBINE_KERNEL
+ *              / PKV_ATTEND_COMBINE_FUSED.
  * The matrix-core kernel serves bf16/int8 pages with a bf16 query, head_dim
  * 64 or 128, page_size 16 or a multiple of 32, up to 16 query heads per KV
- * head and batch <= 4096; every other shape runs on the vector-ALU kernel.
+ * head, at most 64 KV heads and batch <= 4096; every other shape runs on the
+ * vector-ALU kernel.
  * A split size gives at most 16384 splits per sequence (EINVAL otherwise). */
 int pkv_paged_attend(pkv_cache* cache, int32_t layer, const void* q, int32_t q_dtype,
                      int32_t n_q_heads, const int32_t* table, int32_t table_stride,

@@ -29,8 +29,10 @@
 // Work distribution: a persistent grid (as many single-wave workgroups as
 // the chip holds at once) walks a work list of (split, KV head) items built
 // in LDS from the lengths, full splits first.  A sequence that fits in one
-// split gets its output written here; the partials of longer sequences are
-// combined by the combine kernel, which skips the single-split sequences.
+// split gets its output written directly.  For longer sequences either the
+// combine kernel merges the partials afterwards, or (fuse_combine, chosen
+// when sequences have few splits) the workgroup that finishes a (sequence,
+// KV head)'s last split merges them, so one launch does the whole attention.
 #include <algorithm>
 #include <type_traits>
 
@@ -89,6 +91,57 @@ __device__ __forceinline__ void store_out4(const AttendArgs& a, int64_t oi, f32x
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oi) = w;
   } else {
     *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + oi) = r;
+  }
+}
+
+// Partials are exchanged between workgroups, which may sit on different XCDs
+// with separate L2 caches.  Writers store them as agent-scope relaxed atomics
+// (sc1 stores, written through to the coherence point) and wait for those
+// stores to complete before counting their split in; the one workgroup that
+// combines a (sequence, KV head) invalidates its caches once (an agent-scope
+// acquire) and then reads the partials with ordinary vector loads.  No
+// L2 write-back is needed: measured, a release/acquire pair per work item
+// doubled the 32k-token split pass.
+__device__ __forceinline__ void put(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Combine the n split partials (m_s, l_s, o_s) of every query head of KV
+// group g of sequence b: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
+// merged split by split with a running maximum.  One lane per (head, 4 dims);
+// 16 splits' loads in flight per lane.
+template <int D>
+__device__ __forceinline__ void combine_group(const AttendArgs& a, int b, int g, int n, int lane) {
+  constexpr int Q4 = D / 4;
+  constexpr int U = 16;
+  for (int idx = lane; idx < a.group * Q4; idx += 64) {
+    const int hh = idx / Q4, d4 = idx - hh * Q4;
+    const int64_t hrow = (int64_t)b * a.n_q_heads + (int64_t)g * a.group + hh;
+    const float* ml = a.ws_ml + hrow * a.n_split * 2;
+    const float* po = a.ws_o + hrow * a.n_split * D + 4 * d4;
+    float M = -INFINITY, L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < n; s0 += U) {
+      float2 x[U];
+      f32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int s = min(s0 + u, n - 1);  // in bounds; repeats are given weight 0 below
+        x[u] = *reinterpret_cast<const float2*>(ml + 2 * s);
+        v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)s * D);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (s0 + u < n) {
+          const float Mn = fmaxf(M, x[u].x);
+          const float al = __builtin_amdgcn_exp2f(M - Mn), w = __builtin_amdgcn_exp2f(x[u].x - Mn);
+          acc = acc * al + v[u] * w;
+          L = L * al + x[u].y * w;
+          M = Mn;
+        }
+      }
+    }
+    store_out4(a, hrow * D + 4 * d4, acc * (1.f / L));
   }
 }
 
@@ -382,13 +435,42 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
       for (int dt = 0; dt < ND; ++dt)
         store_out4(a, hrow * D + 16 * dt + 4 * j, o[dt] * inv);
     }
-  } else if (n < G) {
+  } else if (!a.fuse_combine) {
     // one of several splits: leave the partial for the combine kernel
-    const int64_t row = hrow * a.n_split + sp;
-    float* wo = a.ws_o + row * D + 4 * j;
+    if (n < G) {
+      const int64_t row = hrow * a.n_split + sp;
+      float* wo = a.ws_o + row * D + 4 * j;
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) *reinterpret_cast<f32x4*>(wo + 16 * dt) = o[dt];
-    if (j == 0) *reinterpret_cast<float2*>(a.ws_ml + row * 2) = float2{m, l};
+      for (int dt = 0; dt < ND; ++dt) *reinterpret_cast<f32x4*>(wo + 16 * dt) = o[dt];
+      if (j == 0) *reinterpret_cast<float2*>(a.ws_ml + row * 2) = float2{m, l};
+    }
+  } else {
+    if (n < G) {
+      const int64_t row = hrow * a.n_split + sp;
+      float* wo = a.ws_o + row * D + 4 * j;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) put(wo + 16 * dt + i, o[dt][i]);
+      if (j == 0) {
+        put(a.ws_ml + row * 2, m);
+        put(a.ws_ml + row * 2 + 1, l);
+      }
+    }
+    // count this split in once its partial stores have completed; the
+    // workgroup that brings the count to the sequence's number of splits
+    // combines the group's partials and resets the counter for the next call
+    __builtin_amdgcn_s_waitcnt(0);
+    uint32_t* counter = a.counters + (int64_t)b * a.n_kv_heads + g;
+    unsigned old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0, 64);
+    if (old == (unsigned)(n_splits_b - 1)) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      combine_group<D>(a, b, g, n_splits_b, lane);
+      if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   }  // work items
 }
@@ -436,14 +518,16 @@ hipError_t launch_fmt(const AttendArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool mfma_supported(int fmt, int q_bf16, int head_dim, int page_size, int group, int batch) {
+bool mfma_supported(int fmt, int q_bf16, int head_dim, int page_size, int group, int batch,
+                    int n_kv_heads) {
   return (fmt == PKV_FMT_BF16 || fmt == PKV_FMT_INT8) && q_bf16 &&
          (head_dim == 64 || head_dim == 128) && (page_size == 16 || page_size % 32 == 0) &&
-         group >= 1 && group <= 16 && batch >= 1 && batch <= kMaxMfmaBatch;
+         group >= 1 && group <= 16 && batch >= 1 && batch <= kMaxMfmaBatch &&
+         n_kv_heads <= kMaxMfmaKvHeads;
 }
 
 hipError_t launch_attend_mfma(const AttendArgs& a, int fmt, hipStream_t s) {
-  if (!mfma_supported(fmt, a.q_bf16, a.head_dim, a.page_size, a.group, a.batch))
+  if (!mfma_supported(fmt, a.q_bf16, a.head_dim, a.page_size, a.group, a.batch, a.n_kv_heads))
     return hipErrorNotSupported;
   return fmt == PKV_FMT_BF16 ? launch_fmt<PKV_FMT_BF16>(a, s) : launch_fmt<PKV_FMT_INT8>(a, s);
 }

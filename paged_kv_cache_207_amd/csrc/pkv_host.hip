@@ -40,19 +40,22 @@ int64_t gcd64(int64_t a, int64_t b) { return b ? gcd64(b, a % b) : a; }
 int64_t split_unit(int page_size) { return 64 / gcd64(64, page_size) * page_size; }
 
 int plan_split(const pkv_cache* c, int batch, int n_q_heads, int max_len) {
-  // Aim for about 2048 workgroups over the chip (8 per compute unit) and
-  // keep every split between 256 and 1024 tokens, so a long sequence is cut
-  // into many partitions and short ones are not over-split.
+  // Measured on the matrix-core path (persistent grid, work list): long
+  // splits are best, 1024 tokens up to 16k-token bounds and 2048 beyond
+  // (fewer partials to combine; the work list keeps the chip busy).  Halve
+  // while the batch would give fewer than 512 (split, KV head) items, so a
+  // small batch still spreads over the compute units.
   const int64_t unit = split_unit(c->L.page_size);
-  const int64_t work = (int64_t)std::max(batch, 1) * c->L.n_kv_heads * std::max(max_len, 1);
-  int64_t want = (work + 2047) / 2048;
-  want = std::min<int64_t>(std::max<int64_t>(want, 256), 1024);
-  int64_t split = (want + unit - 1) / unit * unit;
+  int64_t split = max_len > 16384 ? 2048 : 1024;
+  const int64_t heads = (int64_t)std::max(batch, 1) * c->L.n_kv_heads;
+  while (split > 256 && heads * ((std::max(max_len, 1) + split - 1) / split) < 512) split /= 2;
+  split = (split + unit - 1) / unit * unit;
   (void)n_q_heads;
   return (int)split;
 }
 
-constexpr int kMaxSplits = 16384;  // per sequence; the combine keeps one weight per split in LDS
+constexpr int kMaxSplits = 16384;
+constexpr int kFuseMaxSplits = 8;  // in-kernel combine up to this many splits per sequence  // per sequence; the combine keeps one weight per split in LDS
 
 int check_split(const pkv_cache* c, int32_t split) {
   if (split < 0) return fail(PKV_EINVAL, "split_tokens must be >= 0");
@@ -62,15 +65,23 @@ int check_split(const pkv_cache* c, int32_t split) {
   return PKV_OK;
 }
 
-// Workspace: split partials o [B][Hq][S][D] f32, then (m, l) [B][Hq][S][2] f32.
+// Workspace: first a fixed region of split counters (one u32 per (sequence,
+// KV head) for up to kMaxMfmaBatch sequences x kMaxMfmaKvHeads heads), then
+// the split partials o [B][Hq][S][D] f32 and (m, l) [B][Hq][S][2] f32.  The
+// counters must be zero before the first call and every call leaves them
+// zero; their region does not move with the call's shape, so one zeroed
+// workspace serves calls of any batch, length bound or split size.
+constexpr uint64_t kCounterBytes = (uint64_t)pkv::kMaxMfmaBatch * pkv::kMaxMfmaKvHeads * 4;
+
 struct WsLayout {
-  uint64_t ml_off, total;
+  uint64_t o_off, ml_off, total;
 };
 
 WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_split) {
   WsLayout w;
   const uint64_t rows = (uint64_t)batch * n_q_heads * n_split;
-  w.ml_off = (rows * head_dim * sizeof(float) + 255) / 256 * 256;
+  w.o_off = kCounterBytes;
+  w.ml_off = (w.o_off + rows * head_dim * sizeof(float) + 255) / 256 * 256;
   w.total = w.ml_off + rows * 2 * sizeof(float);
   return w;
 }
@@ -272,7 +283,10 @@ int pkv_paged_attend(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype
     return fail(PKV_ERANGE, "max_len %d exceeds the table row (%d pages of %d)", max_len,
                 table_stride, c->L.page_size);
   if (!std::isfinite(scale)) return fail(PKV_EINVAL, "scale is not finite");
-  if (flags & ~PKV_ATTEND_VALU) return fail(PKV_EINVAL, "unknown flags 0x%x", flags);
+  if (flags & ~(PKV_ATTEND_VALU | PKV_ATTEND_COMBINE_KERNEL | PKV_ATTEND_COMBINE_FUSED))
+    return fail(PKV_EINVAL, "unknown flags 0x%x", flags);
+  if ((flags & PKV_ATTEND_COMBINE_KERNEL) && (flags & PKV_ATTEND_COMBINE_FUSED))
+    return fail(PKV_EINVAL, "conflicting combine flags");
   if (int e = check_split(c, split_tokens)) return e;
   if (batch == 0) return PKV_OK;
   if (!q || !out || !table || !lens || !workspace) return fail(PKV_EINVAL, "null device pointer");
@@ -298,7 +312,8 @@ int pkv_paged_attend(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype
   a.status = c->status;
   a.table = table;
   a.lens = lens;
-  a.ws_o = static_cast<float*>(workspace);
+  a.counters = static_cast<uint32_t*>(workspace);
+  a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.o_off);
   a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.ml_off);
   a.layer_page0 = (int64_t)layer * c->L.n_pages;
   a.qk_scale_log2 = scale * pkv::kLog2eHost;
@@ -314,12 +329,16 @@ int pkv_paged_attend(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype
   a.split_tokens = split;
   a.n_split = n_split;
   a.q_bf16 = q_dtype == PKV_DT_BF16;
-  a.single_done = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   const bool mfma = !(flags & PKV_ATTEND_VALU) &&
                     pkv::mfma_supported(c->L.format, a.q_bf16, a.head_dim, a.page_size, a.group,
-                                        batch);
+                                        batch, c->L.n_kv_heads);
+  // The combine kernel by default: measured against the in-kernel combine
+  // it is faster on every workload here (the in-kernel merge is done by one
+  // wave per (sequence, KV head) and lengthens the tail).  Flags can force
+  // either.
+  a.fuse_combine = mfma && (flags & PKV_ATTEND_COMBINE_FUSED) != 0;
   a.single_done = mfma && max_len > 0;
   if (max_len > 0) {
     Timer tm(c, PKV_T_ATTEND_SPLIT, s);
@@ -327,6 +346,7 @@ int pkv_paged_attend(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype
              : pkv::launch_attend_valu(a, c->L.format, s);
     tm.stop();
     if (e != hipSuccess) return fail(PKV_EHIP, "attend launch failed: %s", hipGetErrorString(e));
+    if (a.fuse_combine) return PKV_OK;  // the split pass combined the splits itself
   }
   Timer tm(c, PKV_T_ATTEND_COMBINE, s);
   e = pkv::launch_reduce(a, s);

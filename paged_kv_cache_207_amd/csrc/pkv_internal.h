@@ -54,12 +54,14 @@ struct AttendArgs {
   const int32_t* lens;
   float* ws_o;   // [batch][n_q_heads][n_split][head_dim] unnormalised partial outputs
   float* ws_ml;  // [batch][n_q_heads][n_split][2] running max (log2 units) and sum
+  uint32_t* counters;  // [batch][n_kv_heads] splits finished (zero between calls)
   int64_t layer_page0;
   float qk_scale_log2;  // softmax scale * log2(e)
   int32_t n_pages, page_size, n_kv_heads, head_dim, n_q_heads, group;
   int32_t table_stride, batch, max_len, split_tokens, n_split;
   int32_t q_bf16;  // 1: q and out are bf16, 0: float32
-  int32_t single_done;  // 1: the split pass wrote the output of single-split sequences
+  int32_t fuse_combine;  // matrix-core path: 1 = combine in the split pass, 0 = combine kernel
+  int32_t single_done;   // combine kernel: single-split sequences are already written
 };
 
 struct GatherArgs {
@@ -86,8 +88,10 @@ hipError_t launch_gather(const GatherArgs& a, int fmt, hipStream_t s);
 hipError_t launch_attend_valu(const AttendArgs& a, int fmt, hipStream_t s);
 // Returns hipErrorNotSupported when the shape has no matrix-core variant.
 hipError_t launch_attend_mfma(const AttendArgs& a, int fmt, hipStream_t s);
-constexpr int kMaxMfmaBatch = 4096;  // the work list lives in LDS: 12 bytes per sequence
-bool mfma_supported(int fmt, int q_bf16, int head_dim, int page_size, int group, int batch);
+constexpr int kMaxMfmaBatch = 4096;   // the work list lives in LDS: 12 bytes per sequence
+constexpr int kMaxMfmaKvHeads = 64;  // split counters: a fixed region of the workspace
+bool mfma_supported(int fmt, int q_bf16, int head_dim, int page_size, int group, int batch,
+                    int n_kv_heads);
 hipError_t launch_reduce(const AttendArgs& a, hipStream_t s);
 hipError_t launch_probe(const void* src, void* dst, float* sink, uint64_t bytes, int mode,
                         hipStream_t s);

@@ -18,7 +18,7 @@ OK, EINVAL, ERANGE, EFORMAT, ENOMEM, EHIP, EDOUBLEFREE = 0, -1, -2, -3, -4, -5, 
 FMT_F32, FMT_BF16, FMT_INT8 = 0, 1, 2
 DT_F32, DT_BF16 = 0, 1
 DEV_WRITE_PAGE, DEV_WRITE_TABLE, DEV_READ_PAGE, DEV_LEN = 1, 2, 4, 8
-ATTEND_VALU = 1
+ATTEND_VALU, ATTEND_COMBINE_KERNEL, ATTEND_COMBINE_FUSED = 1, 2, 4
 T_WRITE, T_ATTEND_SPLIT, T_ATTEND_COMBINE, T_GATHER, T_COUNT = 0, 1, 2, 3, 4
 
 FORMAT_CODE = {"f32": FMT_F32, "bf16": FMT_BF16, "int8": FMT_INT8}
@@ -194,8 +194,10 @@ class PagedKVCache:
         return out.value
 
     def workspace(self, batch, n_q_heads, max_len, split_tokens=0) -> torch.Tensor:
+        """A zeroed workspace (its split counters must start at zero; every
+        call leaves them zero, so the buffer can be reused call after call)."""
         n = self.workspace_size(batch, n_q_heads, max_len, split_tokens)
-        return torch.empty(max(n, 1), dtype=torch.uint8, device=self.device)
+        return torch.zeros(max(n, 1), dtype=torch.uint8, device=self.device)
 
     def attend(self, q, table, lens, max_len: int, scale: float, out=None, workspace=None,
                split_tokens: int = 0, flags: int = 0, layer: int = 0) -> torch.Tensor:

@@ -235,13 +235,18 @@ def test_attend_validation():
     assert a(max_len=65) == pkv.ERANGE  # 4 pages of 16
     assert a(scale=float("nan")) == pkv.EINVAL
     assert a(split=48) == pkv.EINVAL  # not a multiple of 64
-    assert a(flags=4) == pkv.EINVAL
+    assert a(flags=8) == pkv.EINVAL  # unknown flag
+    assert a(flags=pkv.ATTEND_COMBINE_KERNEL | pkv.ATTEND_COMBINE_FUSED) == pkv.EINVAL
     assert a(ws_bytes=need.value - 1) == pkv.ENOMEM
     assert a(ws=C.c_void_p(FAKE + 64)) == pkv.EINVAL
     assert a(batch=0) == pkv.OK
     st = C.c_int32()
     assert L.pkv_attend_split(h, 8, 64, 32768, C.byref(st)) == pkv.OK
-    assert st.value % 64 == 0 and 256 <= st.value <= 1024
+    # 2 KV heads: 8 sequences x 2 heads x 16 splits of 2048 < 512 items -> 1024
+    assert st.value == 1024
+    assert L.pkv_attend_split(h, 128, 4, 32768, C.byref(st)) == pkv.OK and st.value == 2048
+    assert L.pkv_attend_split(h, 32, 4, 4096, C.byref(st)) == pkv.OK and st.value == 512
+    assert L.pkv_attend_split(h, 1, 4, 4096, C.byref(st)) == pkv.OK and st.value == 256
     L.pkv_cache_destroy(h)
 
 

@@ -119,7 +119,9 @@ def test_gather_round_trip(name):
 
 # --------------------------------------------------------------- attention --
 
-@pytest.mark.parametrize("flags", [0, pkv.ATTEND_VALU], ids=["auto", "valu"])
+@pytest.mark.parametrize("flags", [0, pkv.ATTEND_VALU, pkv.ATTEND_COMBINE_KERNEL,
+                                   pkv.ATTEND_COMBINE_FUSED],
+                         ids=["auto", "valu", "combine_kernel", "combine_fused"])
 @pytest.mark.parametrize("split", [0, "unit"])
 @pytest.mark.parametrize("name", NAMES)
 def test_attend_parity(name, split, flags):
@@ -170,7 +172,7 @@ def test_attend_edge_lengths(fmt, D, fill):
     oracle_write_rounds(o, w, w.rounds())
     q = w.query()
     max_len = stride * bs
-    for flags in (0, pkv.ATTEND_VALU):
+    for flags in (0, pkv.ATTEND_VALU, pkv.ATTEND_COMBINE_KERNEL, pkv.ATTEND_COMBINE_FUSED):
         for split in (0, 64, 256):
             out = c.attend(q.cuda(), tdev, dev(lens), max_len, w.scale, split_tokens=split,
                            flags=flags)
@@ -192,7 +194,7 @@ def test_split_and_kernel_agreement_and_determinism():
     q = w.query().cuda()
     lens = dev(w.lens)
     outs = {}
-    for flags in (0, pkv.ATTEND_VALU):
+    for flags in (0, pkv.ATTEND_VALU, pkv.ATTEND_COMBINE_KERNEL, pkv.ATTEND_COMBINE_FUSED):
         for split in (64, 256, 1024, 0):
             outs[flags, split] = c.attend(q, tdev, lens, w.max_len, w.scale, split_tokens=split,
                                           flags=flags).float()
@@ -326,3 +328,29 @@ def test_table_apply_and_seq_tables():
     s.release(2)
     pkv.table_apply(table, s.take_updates().cuda())
     assert table.cpu().tolist() == s.table()
+
+
+def test_workspace_reuse_across_calls():
+    """One workspace, many calls: lengths, batch subsets and split sizes change
+    from call to call; every call must match a fresh-workspace call bit for
+    bit (the split counters are left at zero by each call)."""
+    require_gpu()
+    w = W.decode_bf16(batch=12, lo=50, hi=3000, seed=41)
+    c, tdev = _run_fill(w)
+    q = w.query().cuda()
+    rng = np.random.default_rng(5)
+    ws = c.workspace(w.batch, w.n_q_heads, w.max_len, 64)  # largest need: the smallest split
+    for it in range(40):
+        lens = np.minimum(w.lens, rng.integers(0, w.max_len + 1, size=w.batch)).astype(np.int32)
+        lens[rng.integers(0, w.batch)] = w.lens.max() if it % 3 == 0 else lens[0]
+        lens = np.minimum(lens, w.lens)
+        split = [0, 64, 128, 256, 1024][it % 5]
+        B = w.batch if it % 4 else 7
+        fl = [0, pkv.ATTEND_COMBINE_FUSED, pkv.ATTEND_COMBINE_KERNEL][it % 3]
+        ld = dev(lens[:B])
+        out = c.attend(q[:B].contiguous(), tdev[:B].contiguous(), ld, w.max_len, w.scale,
+                       workspace=ws, split_tokens=split, flags=fl)
+        ref = c.attend(q[:B].contiguous(), tdev[:B].contiguous(), ld, w.max_len, w.scale,
+                       split_tokens=split, flags=fl)
+        assert torch.equal(out, ref), it
+    assert c.status() == 0

@@ -269,9 +269,8 @@ def run_shared_prefix(args, device):
             if n:
                 upd_dev[:n].copy_(upd_host[s][:n], non_blocking=True)
                 pkv.table_apply(table, upd_dev[:n])
-            cache.write(table, start_all[s], cu, ks[s], vs[s])
-            cache.attend(qs[s], table, lens_all[s], max_len, w.scale, out=out, workspace=ws,
-                         split_tokens=split)
+            cache.decode_step(table, lens_all[s], max_len, ks[s], vs[s], qs[s], w.scale,
+                              out=out, workspace=ws, split_tokens=split)
 
     jobs = max(1, args.steps)
     times = []
@@ -315,7 +314,7 @@ def run_shared_prefix(args, device):
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "page_size": bs,
                    "prefix_pages": sp.prefix_pages, "suffix": "uniform [16, 2048]",
                    "step": f"one job = {sp.n_steps} decode steps (host table growth + "
-                           "paged_write 1 row/seq + paged_attend)",
+                           "decode_step: paged_write 1 row/seq + paged_attend, one call)",
                    "split_tokens": split, "value_bytes": "unique KV bytes (shared prefix once)"},
         "tokens_per_s": round(B * sp.n_steps / job_s, 1),
         "logical_kv_GBps": round(logical / job_s / 1e9, 2),
@@ -340,6 +339,9 @@ def main():
                     help="1: overwrite a 512 MiB buffer between timed steps (outside the events)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="run the step as pkv_paged_write + pkv_paged_attend instead of one "
+                         "pkv_decode_step call")
     ap.add_argument("--gather-compare", type=int, default=1,
                     help="1: also time gathering every sequence into a contiguous copy")
     args = ap.parse_args()
@@ -383,8 +385,13 @@ def main():
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=device) if args.flush else None
 
     def step():
-        cache.write(table, start, cu, k_new, v_new)
-        cache.attend(q, table, lens, max_len, w.scale, out=out, workspace=ws, split_tokens=split)
+        if args.separate_write:
+            cache.write(table, start, cu, k_new, v_new)
+            cache.attend(q, table, lens, max_len, w.scale, out=out, workspace=ws,
+                         split_tokens=split)
+        else:  # one call: the decode step writes each sequence's row and attends
+            cache.decode_step(table, lens, max_len, k_new, v_new, q, w.scale, out=out,
+                              workspace=ws, split_tokens=split)
 
     for _ in range(args.warmup):
         step()
@@ -430,7 +437,9 @@ def main():
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "page_size": w.page_size, "n_pages": w.n_pages,
                    "table": "seeded random permutation of the pool",
-                   "step": "paged_write 1 row/seq + paged_attend", "split_tokens": split,
+                   "step": ("paged_write 1 row/seq + paged_attend" if args.separate_write else
+                            "decode_step: paged_write 1 row/seq + paged_attend, one call"),
+                   "split_tokens": split,
                    "l2_flush_between_steps": bool(args.flush)},
         "tokens_per_s": round(B / (ms_per_step / 1e3), 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),

@@ -177,6 +177,27 @@ int pkv_paged_attend(pkv_cache* cache, int32_t layer, const void* q, int32_t q_d
                      void* workspace, uint64_t workspace_bytes, int32_t split_tokens,
                      uint32_t flags, void* stream);
 
+/* One decode step: paged_write of one new row per sequence, then
+ * paged_attend, as a single call.  Row b of k_new / v_new (device
+ * [batch][n_kv_heads][head_dim] of in_dtype) is stored at position
+ * lens[b] - 1 of sequence b (lens counts the new token; a sequence with
+ * lens[b] = 0 gets no row and a zero output), then every sequence attends
+ * over its lens[b] tokens exactly as pkv_paged_attend does.  Pages and
+ * outputs equal those of pkv_paged_write (start_pos = lens - 1, one row per
+ * sequence) followed by pkv_paged_attend.  On the matrix-core path with bf16
+ * rows, the workgroup that owns a sequence's last split writes the row and
+ * uses it directly (one launch, no write kernel); otherwise the write kernel
+ * runs first.  The new token's page must not be shared with another
+ * sequence.  Other arguments and errors as pkv_paged_write and
+ * pkv_paged_attend (this tiny-llm paged_kv.py begin_step + update pair
+ * writes each slot's token, then attends). */
+int pkv_decode_step(pkv_cache* cache, int32_t layer, const int32_t* table, int32_t table_stride,
+                    const int32_t* lens, int32_t batch, int32_t max_len, const void* k_new,
+                    const void* v_new, int32_t in_dtype, const void* q, int32_t q_dtype,
+                    int32_t n_q_heads, float scale, void* out, void* workspace,
+                    uint64_t workspace_bytes, int32_t split_tokens, uint32_t flags,
+                    void* stream);
+
 /* gather(table, len): rows 0 .. len-1 of one sequence copied out in token
  * order (AstrAI cache.py PagedCache.gather truncated by CacheView;
  * libmir-metal PagedStore::context).  k_out, v_out: device

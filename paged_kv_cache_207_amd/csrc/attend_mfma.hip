@@ -260,6 +260,11 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
   const int32_t* trow = a.table + (int64_t)b * a.table_stride;
   const int pg_last = (t_end - 1) / bs;
 
+  // ---- decode step: the sequence's new row sits at position len - 1, in
+  // the last step of its last split (see substitute_new below)
+  const bool owns_new = a.k_new != nullptr && sp == n_splits_b - 1;  // item-uniform
+  const int t_new = len - 1;
+
   f32x4 o[ND];
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -399,6 +404,139 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
       }
     };
 
+    // A fused decode step: the item that owns the sequence's last split loads
+    // its head's new row, quantizes it for int8 pages (the page write's own
+    // operations), stores it in its page, and puts it in place of the slot's
+    // old contents in the registers of the step that holds it.  That step is
+    // the item's last, handled after the pipelined loop with no load in
+    // flight behind it, so the row costs no registers during the loop.
+    auto substitute_new = [&](int ts, S& r) {
+      if (!owns_new || t_new < ts || t_new >= ts + 32) return;
+      if (a.lens[b] != len) return;  // an out-of-range length (reported, clamped): no write
+      const int x_new = t_new - ts;                          // slot of the token in the step
+      const int tau_new = (x_new >> 2) & 1;                  // score tile holding it
+      const int n_new = ((x_new >> 3) << 2) | (x_new & 3);  // its K row lane
+      const int j_new = x_new >> 3;                          // its V k-group
+      const uint16_t* kr = static_cast<const uint16_t*>(a.k_new) + ((int64_t)b * a.n_kv_heads + g) * D;
+      const uint16_t* vr = static_cast<const uint16_t*>(a.v_new) + ((int64_t)b * a.n_kv_heads + g) * D;
+      uint4 kb4[NC];
+      uint32_t vnew[ND];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kb4[c] = *reinterpret_cast<const uint4*>(kr + 32 * c + 8 * j);
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) vnew[dt] = vr[16 * dt + n];
+      KT knew[NC];
+      float ks_new = 0.f, vs_new = 0.f;
+      if constexpr (FMT == PKV_FMT_BF16) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) knew[c] = kb4[c];
+      } else {
+        // scale = max|x| / 127 over the row, code = clamp(rint(x / scale), +-127)
+        float mk = 0.f, mv = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const uint32_t w4[4] = {kb4[c].x, kb4[c].y, kb4[c].z, kb4[c].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            mk = fmaxf(mk, fmaxf(fabsf(bf16_bits_to_f32(w4[i] & 0xffffu)),
+                                 fabsf(bf16_bits_to_f32(w4[i] >> 16))));
+        }
+        mk = fmaxf(mk, __shfl_xor(mk, 16, 64));
+        mk = fmaxf(mk, __shfl_xor(mk, 32, 64));
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) mv = fmaxf(mv, fabsf(bf16_bits_to_f32(vnew[dt])));
+#pragma unroll
+        for (int o1 = 1; o1 < 16; o1 <<= 1) mv = fmaxf(mv, __shfl_xor(mv, o1, 64));
+        ks_new = __fdiv_rn(mk, 127.0f);
+        vs_new = __fdiv_rn(mv, 127.0f);
+        auto code = [](float x, float sc) -> uint32_t {
+          if (sc == 0.f) return 0u;
+          const float q = fminf(fmaxf(rintf(__fdiv_rn(x, sc)), -127.f), 127.f);
+          return (uint32_t)(int32_t)q & 0xffu;
+        };
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const uint32_t w4[4] = {kb4[c].x, kb4[c].y, kb4[c].z, kb4[c].w};
+          uint32_t cw[2] = {0u, 0u};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = code(bf16_bits_to_f32(w4[i] & 0xffffu), ks_new);
+            const uint32_t hi = code(bf16_bits_to_f32(w4[i] >> 16), ks_new);
+            cw[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
+          }
+          knew[c] = KT{cw[0], cw[1]};
+        }
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) vnew[dt] = code(bf16_bits_to_f32(vnew[dt]), vs_new);
+      }
+      // the page write
+      const int jp = t_new / bs;
+      const int page = trow[jp];
+      if (page < 0 || page >= a.n_pages) {
+        report(a.status, PKV_DEV_WRITE_PAGE);
+      } else {
+        const int slot = t_new - jp * bs;
+        const int64_t slab = (a.layer_page0 + page) * a.n_kv_heads + g;
+        char* kw = static_cast<char*>(const_cast<void*>(a.k_pages)) + slab * slab_bytes;
+        char* vw = static_cast<char*>(const_cast<void*>(a.v_pages)) + slab * slab_bytes;
+        if (n == 0) {  // lanes j = 0..3 of one row hold the whole K row
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+            *reinterpret_cast<KT*>(kw + ((int64_t)slot * D + 32 * c + 8 * j) * ESZ) = knew[c];
+        }
+        if (j == 0) {  // lanes n = 0..15 hold every dim of the V row
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) {
+            const int64_t e = (int64_t)(16 * dt + n) * bs + slot;
+            if (FMT == PKV_FMT_BF16) reinterpret_cast<uint16_t*>(vw)[e] = (uint16_t)vnew[dt];
+            else reinterpret_cast<uint8_t*>(vw)[e] = (uint8_t)vnew[dt];
+          }
+        }
+        if (FMT == PKV_FMT_INT8 && lane == 0) {
+          const_cast<float*>(a.k_scales)[slab * bs + slot] = ks_new;
+          const_cast<float*>(a.v_scales)[slab * bs + slot] = vs_new;
+        }
+      }
+      // the registers of this step
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          if (tau == tau_new && n == n_new) r.k[tau][c] = knew[c];
+      if (j == j_new) {
+        const int e = x_new & 7;  // element of this lane's 8-token V operand
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+          if constexpr (FMT == PKV_FMT_BF16) {
+            uint32_t w[4] = {r.v[dt].x, r.v[dt].y, r.v[dt].z, r.v[dt].w};
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2)
+              if (q2 == (e >> 1))
+                w[q2] = e & 1 ? (w[q2] & 0x0000ffffu) | (vnew[dt] << 16)
+                              : (w[q2] & 0xffff0000u) | vnew[dt];
+            r.v[dt] = uint4{w[0], w[1], w[2], w[3]};
+          } else {
+            uint32_t w[2] = {r.v[dt].x, r.v[dt].y};
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2)
+              if (q2 == (e >> 2))
+                w[q2] = (w[q2] & ~(0xffu << (8 * (e & 3)))) | (vnew[dt] << (8 * (e & 3)));
+            r.v[dt] = uint2{w[0], w[1]};
+          }
+        }
+        if (FMT == PKV_FMT_INT8) {
+#pragma unroll
+          for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (tau == tau_new && i == (x_new & 3)) {
+                r.ks[tau][i] = ks_new;
+                r.vs[tau][i] = vs_new;
+              }
+        }
+      }
+    };
+
     // ---- two register sets, loads one step ahead.  The loop body issues its
     // prefetches unconditionally and the last one or two steps are peeled:
     // a load under a condition would make the compiler wait for every
@@ -417,8 +555,10 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
     if (st + 1 < n_steps) {
       load_step(w0 + 32 * (st + 1), r1);
       compute_step(w0 + 32 * st, r0);
+      substitute_new(w0 + 32 * (st + 1), r1);
       compute_step(w0 + 32 * (st + 1), r1);
     } else {
+      substitute_new(w0 + 32 * st, r0);
       compute_step(w0 + 32 * st, r0);
     }
   }

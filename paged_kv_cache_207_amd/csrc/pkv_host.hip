@@ -236,6 +236,7 @@ int pkv_paged_write(pkv_cache* c, int32_t layer, const int32_t* table, int32_t t
   a.table_stride = table_stride;
   a.batch = batch;
   a.total_new = total_new;
+  a.decode_lens = nullptr;
   Timer tm(c, PKV_T_WRITE, static_cast<hipStream_t>(stream));
   hipError_t e = pkv::launch_write(a, c->L.format, in_dtype, static_cast<hipStream_t>(stream));
   tm.stop();
@@ -264,11 +265,17 @@ int pkv_attend_workspace_size(const pkv_cache* c, int32_t batch, int32_t n_q_hea
   return PKV_OK;
 }
 
-int pkv_paged_attend(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype,
-                     int32_t n_q_heads, const int32_t* table, int32_t table_stride,
-                     const int32_t* lens, int32_t batch, int32_t max_len, float scale, void* out,
-                     void* workspace, uint64_t workspace_bytes, int32_t split_tokens,
-                     uint32_t flags, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of pkv_paged_attend and pkv_decode_step (k_new/v_new non-null:
+// the decode step's new rows, written at position lens[b] - 1 first).
+int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int32_t n_q_heads,
+                const int32_t* table, int32_t table_stride, const int32_t* lens, int32_t batch,
+                int32_t max_len, float scale, void* out, void* workspace,
+                uint64_t workspace_bytes, int32_t split_tokens, uint32_t flags, void* stream,
+                const void* k_new, const void* v_new, int32_t in_dtype) {
   if (!c) return fail(PKV_EINVAL, "cache is null");
   if (layer < 0 || layer >= c->L.n_layers)
     return fail(PKV_ERANGE, "layer %d outside [0, %d)", layer, c->L.n_layers);
@@ -334,6 +341,39 @@ int pkv_paged_attend(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype
   const bool mfma = !(flags & PKV_ATTEND_VALU) &&
                     pkv::mfma_supported(c->L.format, a.q_bf16, a.head_dim, a.page_size, a.group,
                                         batch, c->L.n_kv_heads);
+  a.k_new = a.v_new = nullptr;
+  if (k_new) {
+    if (mfma && max_len > 0 && in_dtype == PKV_DT_BF16) {
+      a.k_new = k_new;  // the split pass writes and uses the new rows
+      a.v_new = v_new;
+    } else {
+      // write the new rows first (row b at position lens[b] - 1), then attend
+      pkv::WriteArgs w;
+      w.k_pages = c->k_pages;
+      w.v_pages = c->v_pages;
+      w.k_scales = c->k_scales;
+      w.v_scales = c->v_scales;
+      w.status = c->status;
+      w.table = table;
+      w.start_pos = nullptr;
+      w.cu_new = nullptr;
+      w.k_in = k_new;
+      w.v_in = v_new;
+      w.layer_page0 = (int64_t)layer * c->L.n_pages;
+      w.n_pages = c->L.n_pages;
+      w.page_size = c->L.page_size;
+      w.n_kv_heads = c->L.n_kv_heads;
+      w.head_dim = c->L.head_dim;
+      w.table_stride = table_stride;
+      w.batch = batch;
+      w.total_new = batch;
+      w.decode_lens = lens;
+      Timer tw(c, PKV_T_WRITE, s);
+      e = pkv::launch_write(w, c->L.format, in_dtype, s);
+      tw.stop();
+      if (e != hipSuccess) return fail(PKV_EHIP, "write launch failed: %s", hipGetErrorString(e));
+    }
+  }
   // The combine kernel by default: measured against the in-kernel combine
   // it is faster on every workload here (the in-kernel merge is done by one
   // wave per (sequence, KV head) and lengthens the tail).  Flags can force
@@ -353,6 +393,40 @@ int pkv_paged_attend(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype
   tm.stop();
   if (e != hipSuccess) return fail(PKV_EHIP, "reduce launch failed: %s", hipGetErrorString(e));
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attend(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype,
+                     int32_t n_q_heads, const int32_t* table, int32_t table_stride,
+                     const int32_t* lens, int32_t batch, int32_t max_len, float scale, void* out,
+                     void* workspace, uint64_t workspace_bytes, int32_t split_tokens,
+                     uint32_t flags, void* stream) {
+  return attend_impl(c, layer, q, q_dtype, n_q_heads, table, table_stride, lens, batch, max_len,
+                     scale, out, workspace, workspace_bytes, split_tokens, flags, stream, nullptr,
+                     nullptr, 0);
+}
+
+int pkv_decode_step(pkv_cache* c, int32_t layer, const int32_t* table, int32_t table_stride,
+                    const int32_t* lens, int32_t batch, int32_t max_len, const void* k_new,
+                    const void* v_new, int32_t in_dtype, const void* q, int32_t q_dtype,
+                    int32_t n_q_heads, float scale, void* out, void* workspace,
+                    uint64_t workspace_bytes, int32_t split_tokens, uint32_t flags,
+                    void* stream) {
+  if (!c) return fail(PKV_EINVAL, "cache is null");
+  if (in_dtype != PKV_DT_F32 && in_dtype != PKV_DT_BF16)
+    return fail(PKV_EINVAL, "unknown input dtype %d", in_dtype);
+  if ((c->L.format == PKV_FMT_F32 && in_dtype != PKV_DT_F32) ||
+      (c->L.format == PKV_FMT_BF16 && in_dtype != PKV_DT_BF16))
+    return fail(PKV_EFORMAT, "native pages take rows of their own dtype");
+  if (batch > 0 && (!k_new || !v_new)) return fail(PKV_EINVAL, "null device pointer");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+    return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
+  return attend_impl(c, layer, q, q_dtype, n_q_heads, table, table_stride, lens, batch, max_len,
+                     scale, out, workspace, workspace_bytes, split_tokens, flags, stream, k_new,
+                     v_new, in_dtype);
 }
 
 int pkv_gather(pkv_cache* c, int32_t layer, const int32_t* table_row, int32_t len, void* k_out,

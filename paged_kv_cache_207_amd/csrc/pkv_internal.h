@@ -39,6 +39,7 @@ struct WriteArgs {
   int64_t layer_page0;  // layer * n_pages
   int32_t n_pages, page_size, n_kv_heads, head_dim;
   int32_t table_stride, batch, total_new;
+  const int32_t* decode_lens;  // non-null: row b goes to position decode_lens[b] - 1 of sequence b
 };
 
 // Arguments shared by the split-K attention kernels and the reduce kernel.
@@ -55,6 +56,8 @@ struct AttendArgs {
   float* ws_o;   // [batch][n_q_heads][n_split][head_dim] unnormalised partial outputs
   float* ws_ml;  // [batch][n_q_heads][n_split][2] running max (log2 units) and sum
   uint32_t* counters;  // [batch][n_kv_heads] splits finished (zero between calls)
+  const void* k_new;   // decode step: [batch][n_kv_heads][head_dim] bf16 rows at len - 1,
+  const void* v_new;   // written and attended by the matrix-core kernel (null: none)
   int64_t layer_page0;
   float qk_scale_log2;  // softmax scale * log2(e)
   int32_t n_pages, page_size, n_kv_heads, head_dim, n_q_heads, group;

@@ -46,15 +46,23 @@ __global__ __launch_bounds__(64) void write_kernel(WriteArgs a) {
   if (lane < kRows) {
     RowMeta m{-1, 0, 0};
     const int r = row0 + lane;
-    if (r < a.total_new) {
+    int b = -1, t = -1;
+    if (a.decode_lens && r < a.total_new) {
+      // decode step: row r is sequence r's newest token (none if its length is 0)
+      b = r;
+      t = a.decode_lens[b] - 1;
+      if (t < 0) b = -1;
+    } else if (r < a.total_new) {
       // largest b with cu_new[b] <= r, kept inside [0, batch-1]
       int lo = 0, hi = a.batch - 1;
       while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
         if (a.cu_new[mid] <= r) lo = mid; else hi = mid - 1;
       }
-      const int b = lo;
-      const int t = a.start_pos[b] + (r - a.cu_new[b]);
+      b = lo;
+      t = a.start_pos[b] + (r - a.cu_new[b]);
+    }
+    if (b >= 0) {
       const int j = t >= 0 ? t / a.page_size : -1;
       if (t < 0 || j >= a.table_stride) {
         report(a.status, PKV_DEV_WRITE_TABLE);

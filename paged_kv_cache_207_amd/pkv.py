@@ -37,6 +37,9 @@ SYMBOLS = [
     ("pkv_attend_workspace_size", C.c_int, [_P, _I32, _I32, _I32, _I32, C.POINTER(C.c_uint64)]),
     ("pkv_paged_attend", C.c_int,
      [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _I32, _I32, _F, _P, _P, _U64, _I32, _U32, _P]),
+    ("pkv_decode_step", C.c_int,
+     [_P, _I32, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _I32, _I32, _F, _P, _P, _U64, _I32,
+      _U32, _P]),
     ("pkv_gather", C.c_int, [_P, _I32, _P, _I32, _P, _P, _P, _P, _P]),
     ("pkv_table_apply", C.c_int, [_P, _I32, _I32, _P, _I32, _P]),
     ("pkv_last_error", C.c_char_p, []),
@@ -214,6 +217,28 @@ class PagedKVCache:
             max_len, float(scale), _dev(out, q.dtype, "out"), _dev(workspace, name="workspace"),
             workspace.numel() * workspace.element_size(), split_tokens, flags,
             _stream(self.device)))
+        return out
+
+    # -- decode step (write one row per sequence at lens - 1, then attend) -------
+    def decode_step(self, table, lens, max_len: int, k_new, v_new, q, scale: float, out=None,
+                    workspace=None, split_tokens: int = 0, flags: int = 0,
+                    layer: int = 0) -> torch.Tensor:
+        B, Hq, D = q.shape
+        if tuple(k_new.shape) != (B, self.n_kv_heads, self.head_dim) or v_new.shape != k_new.shape:
+            raise ValueError("k_new and v_new must be [batch, n_kv_heads, head_dim]")
+        if k_new.dtype not in DTYPE_CODE or v_new.dtype != k_new.dtype or q.dtype not in DTYPE_CODE:
+            raise ValueError("rows and q must be float32 or bfloat16")
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = self.workspace(B, Hq, max_len, split_tokens)
+        _check(lib().pkv_decode_step(
+            self._h, layer, _dev(table, torch.int32, "table"), table.shape[1],
+            _dev(lens, torch.int32, "lens"), B, max_len, _dev(k_new, name="k_new"),
+            _dev(v_new, name="v_new"), DTYPE_CODE[k_new.dtype], _dev(q, name="q"),
+            DTYPE_CODE[q.dtype], Hq, float(scale), _dev(out, q.dtype, "out"),
+            _dev(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
+            split_tokens, flags, _stream(self.device)))
         return out
 
     # -- kernel timing -----------------------------------------------------------

@@ -37,8 +37,11 @@ from paged_kv_cache_207_amd import workloads as W  # noqa: E402
 HBM_PEAK_GBPS = 8000.0
 METRIC = "paged decode attention KV GB/s (% of HBM peak) and decode tokens/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_split_long_bf16_traffic.json")
+# the split kernel and what decides its launch (split planner, arguments)
 KERNEL_SOURCES = ["paged_kv_cache_207_amd/csrc/attend_mfma.hip",
-                  "paged_kv_cache_207_amd/csrc/pkv_device.h"]
+                  "paged_kv_cache_207_amd/csrc/pkv_device.h",
+                  "paged_kv_cache_207_amd/csrc/pkv_internal.h",
+                  "paged_kv_cache_207_amd/csrc/pkv_host.hip"]
 
 
 def log(msg: str) -> None:
@@ -61,12 +64,18 @@ def kv_bytes(w) -> int:
     return int(w.lens.astype(np.int64).sum()) * per_tok
 
 
-def split_kernel_bytes(w) -> int:
+def split_kernel_bytes(w, fused_write: bool = True) -> int:
     """Algorithmic bytes of one split-pass launch: K/V pages of every token,
-    the table entries that map them, and the queries."""
+    the table entries that map them, and the queries; in a fused decode step
+    also the new K/V rows it reads and stores in their pages."""
     npages = sum(-(-int(n) // w.page_size) for n in w.lens)
     qb = w.batch * w.n_q_heads * w.head_dim * (2 if w.q_dtype == torch.bfloat16 else 4)
-    return kv_bytes(w) + 4 * npages + qb
+    rows = 0
+    if fused_write:
+        in_elem = 2 if w.in_dtype == torch.bfloat16 else 4
+        elem = {"f32": 4, "bf16": 2, "int8": 1}[w.kv_format]
+        rows = w.batch * w.n_kv_heads * w.head_dim * 2 * (in_elem + elem)
+    return kv_bytes(w) + 4 * npages + qb + rows
 
 
 def fill(w, cache, device):
@@ -426,7 +435,7 @@ def main():
 
     kvb = kv_bytes(w)
     value = kvb / (ms_per_step / 1e3) / 1e9
-    achieved = split_kernel_bytes(w) / (split_avg / 1e3) / 1e9
+    achieved = split_kernel_bytes(w, not args.separate_write) / (split_avg / 1e3) / 1e9
     traffic = load_traffic()
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,

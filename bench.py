@@ -3,17 +3,23 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_bf16]
 
-A step is one pass of the hot path over the batch: paged_write of one new
-K/V row per sequence (at position len-1, the newest token) followed by
-paged_attend (split-K partial pass + combine) of one query per sequence over
-all len tokens, read in place through a fully fragmented block table.  The
-K/V pages are filled once before timing.  Prints one JSON line (stdout);
-details go to stderr.
+A step is one pass of the hot path over the batch: one pkv_decode_step call
+that writes one new K/V row per sequence (at position len-1, the newest
+token) and runs paged attention (split-K partial pass + combine) of one query
+per sequence over all len tokens, read in place through a fully fragmented
+block table.  The K/V pages are filled once before timing.  Prints one JSON
+line (stdout); details go to stderr.
+
+Timing: W warmup steps, then K steps back to back between two
+synchronisations (the timed region: value, ms_per_step); then the same K
+steps again with the library's kernel events, whose dispatch-stamped
+durations give the split-K kernel's average (roofline.achieved); then K
+steps each after a 512 MiB read-only sweep of the caches (cold_cache).
 
 value = KV bytes the attention reads per step / step time (GB/s);
 roofline = the split-K partial kernel (the dominant one): its algorithmic
-bytes (K/V pages + table entries + queries) / its average duration from HIP
-events recorded by the library around each launch.
+bytes (K/V pages + table entries + queries + the new rows) / its average
+duration.
 """
 from __future__ import annotations
 
@@ -283,7 +289,9 @@ def run_shared_prefix(args, device):
 
     jobs = max(1, args.steps)
     times = []
-    for rep in range(args.warmup + jobs):
+    # warmup jobs, the timed jobs, then one more job with the library's
+    # kernel events on (for the split-pass duration only)
+    for rep in range(args.warmup + jobs + 1):
         if rep:
             seqs.close()
             pool.close()
@@ -291,13 +299,14 @@ def run_shared_prefix(args, device):
             table.fill_(-1)
             pkv.table_apply(table, seqs.take_updates().to(device))
         torch.cuda.synchronize()
-        if rep == args.warmup:
+        timed = args.warmup <= rep < args.warmup + jobs
+        if rep == args.warmup + jobs:
             cache.timing_read()
             cache.timing(True)
         t0 = time.perf_counter()
         job(seqs)
         torch.cuda.synchronize()
-        if rep >= args.warmup:
+        if timed:
             times.append(time.perf_counter() - t0)
         if rep == 0:
             assert seqs.lens() == [int(x) for x in sp.step_lens(sp.n_steps - 1)]
@@ -344,8 +353,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_bf16")
     ap.add_argument("--split", type=int, default=0, help="split tokens (0 = library plan)")
-    ap.add_argument("--flush", type=int, default=1,
-                    help="1: overwrite a 512 MiB buffer between timed steps (outside the events)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate-write", action="store_true",
@@ -391,7 +398,10 @@ def main():
     max_len = w.max_len
     split = args.split or cache.split_for(B, w.n_q_heads, max_len)
     ws = cache.workspace(B, w.n_q_heads, max_len, split)
-    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=device) if args.flush else None
+    sweep_buf = torch.empty(512 << 20, dtype=torch.uint8, device=device)
+    sweep_buf.fill_(7)
+    sweep_sink = torch.empty(pkv.lib().pkv_probe_blocks(sweep_buf.numel()), dtype=torch.float32,
+                             device=device)
 
     def step():
         if args.separate_write:
@@ -407,31 +417,49 @@ def main():
     torch.cuda.synchronize()
     cache.status() == 0 or sys.exit("device status flags set during warmup")
 
-    cache.timing(True)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # (1) the timed region: K steps back to back between two synchronisations
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    for i in range(args.steps):
-        if flush_buf is not None:
-            flush_buf.fill_(i & 0xff)
-        evs[i][0].record()
+    e0.record()
+    for _ in range(args.steps):
         step()
-        evs[i][1].record()
+    e1.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    wall_ms = (time.perf_counter() - wall0) * 1e3 / args.steps
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    def kernel_times():
+        t = cache.timing_read()
+        return {k: v[0] / max(v[1], 1) for k, v in t.items()}
+
+    # (2) the same K steps with the library's kernel events (each kernel's
+    # dispatch stamps its own start and end): the per-kernel durations
+    cache.timing_read()
+    cache.timing(True)
+    for _ in range(args.steps):
+        step()
     cache.timing(False)
-    t = cache.timing_read()
-    step_ms = [a.elapsed_time(b) for a, b in evs]
-    ms_per_step = float(np.mean(step_ms))
-    split_ms, split_n = t["attend_split"]
-    comb_ms, comb_n = t["attend_combine"]
-    wr_ms, wr_n = t["write"]
-    split_avg = split_ms / max(split_n, 1)
-    log(f"step: {ms_per_step * 1e3:.1f} us (min {min(step_ms) * 1e3:.1f}); split pass "
-        f"{split_avg * 1e3:.1f} us, combine {comb_ms / max(comb_n, 1) * 1e3:.1f} us, write "
-        f"{wr_ms / max(wr_n, 1) * 1e3:.1f} us; wall {wall * 1e6 / args.steps:.1f} us/step "
-        f"incl. flush; split_tokens={split}")
+    kt = kernel_times()
+    split_avg = kt["attend_split"]
+
+    # (3) cold caches: each step after a 512 MiB read-only sweep (which leaves
+    # no dirty lines behind), kernels timed by the library's events: whether
+    # the back-to-back steps gain anything from data left in the caches
+    cache.timing(True)
+    for i in range(args.steps):
+        pkv.probe_stream(sweep_buf, sink=sweep_sink)
+        step()
+    torch.cuda.synchronize()
+    cache.timing(False)
+    kt_cold = kernel_times()
+    assert cache.status() == 0
+    comb_avg, wr_avg = kt["attend_combine"], kt["write"]
+    log(f"step: {ms_per_step * 1e3:.1f} us back to back (wall {wall_ms * 1e3:.1f} us); "
+        f"split pass {split_avg * 1e3:.1f} us, combine {comb_avg * 1e3:.1f} us, write "
+        f"{wr_avg * 1e3:.1f} us; after a cache sweep: split pass "
+        f"{kt_cold['attend_split'] * 1e3:.1f} us, combine "
+        f"{kt_cold['attend_combine'] * 1e3:.1f} us; split_tokens={split}")
 
     kvb = kv_bytes(w)
     value = kvb / (ms_per_step / 1e3) / 1e9
@@ -448,22 +476,26 @@ def main():
                    "table": "seeded random permutation of the pool",
                    "step": ("paged_write 1 row/seq + paged_attend" if args.separate_write else
                             "decode_step: paged_write 1 row/seq + paged_attend, one call"),
-                   "split_tokens": split,
-                   "l2_flush_between_steps": bool(args.flush)},
+                   "split_tokens": split},
         "tokens_per_s": round(B / (ms_per_step / 1e3), 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "kv_bytes_per_step": kvb,
         "achievable_read_GBps": round(read_gbps, 1),
+        "wall_ms_per_step": round(wall_ms, 5),
+        "cold_cache": {"split_pass_us": round(kt_cold["attend_split"] * 1e3, 2),
+                       "combine_us": round(kt_cold["attend_combine"] * 1e3, 2),
+                       "note": "kernel durations when each step follows a 512 MiB read-only "
+                               "sweep of the caches"},
         "fill_write": fill_info,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": "attend_mfma (split-K partial pass)",
-                     "avg_launch_us": round(split_avg * 1e3, 2)},
+                     "avg_launch_us": round(split_avg * 1e3, 2),
+                     "timing": "library kernel events over a second run of the K steps"},
     }
     if args.gather_compare:
         line["gather_compare"] = gather_compare(w, cache, table, device)
-        line["gather_compare"]["inplace_attend_us"] = round(
-            (split_avg + comb_ms / max(comb_n, 1)) * 1e3, 2)
+        line["gather_compare"]["inplace_attend_us"] = round((split_avg + comb_avg) * 1e3, 2)
         log(f"gather compare: {line['gather_compare']}")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, ks, vs, q_host, args.cpu_seconds)

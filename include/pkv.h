@@ -219,9 +219,11 @@ int pkv_table_apply(int32_t* table, int32_t table_stride, int32_t batch, const i
 const char* pkv_last_error(void);
 
 /* ---- measurement -----------------------------------------------------------
- * Kernel timing: while enabled on a cache, pkv_paged_write, pkv_paged_attend
- * and pkv_gather record HIP events (host-allocated, on the call's stream)
- * around each kernel pass they enqueue; nothing else changes.
+ * Kernel timing: while enabled on a cache, pkv_paged_write, pkv_paged_attend,
+ * pkv_decode_step and pkv_gather launch each kernel pass with a pair of HIP
+ * events (created by the library) that the kernel's own dispatch stamps
+ * with its start and end, so no marker packet is added between kernels;
+ * nothing else changes.
  * pkv_timing_read waits for the recorded events, returns the summed
  * milliseconds and the number of passes timed per kind (PKV_T_*), then
  * forgets them.  ms[] and counts[] are host arrays of PKV_T_COUNT entries. */

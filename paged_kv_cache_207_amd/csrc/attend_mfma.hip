@@ -635,25 +635,24 @@ int resident_workgroups(K kernel, size_t lds) {
 }
 
 template <int FMT, int D, int BS>
-hipError_t launch_bs(const AttendArgs& a, hipStream_t s) {
+hipError_t launch_bs(const AttendArgs& a, const Launch& l) {
   auto kernel = attend_mfma_kernel<FMT, D, BS>;
   const size_t lds = (size_t)(3 * a.batch + 2) * sizeof(int32_t);
   const int64_t bound = (int64_t)a.n_kv_heads * a.batch * a.n_split;
   const int64_t grid = std::min<int64_t>(bound, resident_workgroups(kernel, lds));
-  hipLaunchKernelGGL(kernel, dim3((unsigned)std::max<int64_t>(grid, 1)), dim3(64), lds, s, a);
-  return hipGetLastError();
+  return launch1(kernel, dim3((unsigned)std::max<int64_t>(grid, 1)), dim3(64), lds, l, a);
 }
 
 template <int FMT, int D>
-hipError_t launch_d(const AttendArgs& a, hipStream_t s) {
-  if (a.page_size == 16) return launch_bs<FMT, D, 16>(a, s);
-  if (a.page_size == 32) return launch_bs<FMT, D, 32>(a, s);
-  return launch_bs<FMT, D, 0>(a, s);
+hipError_t launch_d(const AttendArgs& a, const Launch& l) {
+  if (a.page_size == 16) return launch_bs<FMT, D, 16>(a, l);
+  if (a.page_size == 32) return launch_bs<FMT, D, 32>(a, l);
+  return launch_bs<FMT, D, 0>(a, l);
 }
 
 template <int FMT>
-hipError_t launch_fmt(const AttendArgs& a, hipStream_t s) {
-  return a.head_dim == 128 ? launch_d<FMT, 128>(a, s) : launch_d<FMT, 64>(a, s);
+hipError_t launch_fmt(const AttendArgs& a, const Launch& l) {
+  return a.head_dim == 128 ? launch_d<FMT, 128>(a, l) : launch_d<FMT, 64>(a, l);
 }
 
 }  // namespace
@@ -666,10 +665,10 @@ bool mfma_supported(int fmt, int q_bf16, int head_dim, int page_size, int group,
          n_kv_heads <= kMaxMfmaKvHeads;
 }
 
-hipError_t launch_attend_mfma(const AttendArgs& a, int fmt, hipStream_t s) {
+hipError_t launch_attend_mfma(const AttendArgs& a, int fmt, const Launch& l) {
   if (!mfma_supported(fmt, a.q_bf16, a.head_dim, a.page_size, a.group, a.batch, a.n_kv_heads))
     return hipErrorNotSupported;
-  return fmt == PKV_FMT_BF16 ? launch_fmt<PKV_FMT_BF16>(a, s) : launch_fmt<PKV_FMT_INT8>(a, s);
+  return fmt == PKV_FMT_BF16 ? launch_fmt<PKV_FMT_BF16>(a, l) : launch_fmt<PKV_FMT_INT8>(a, l);
 }
 
 }  // namespace pkv

@@ -225,16 +225,12 @@ __global__ __launch_bounds__(64) void attend_valu_kernel(AttendArgs a) {
 
 }  // namespace
 
-hipError_t launch_attend_valu(const AttendArgs& a, int fmt, hipStream_t s) {
+hipError_t launch_attend_valu(const AttendArgs& a, int fmt, const Launch& l) {
   const int nhc = (a.group + kHeads - 1) / kHeads;
   dim3 grid(a.n_split, a.n_kv_heads * nhc, a.batch);
-  if (fmt == PKV_FMT_F32)
-    hipLaunchKernelGGL(attend_valu_kernel<PKV_FMT_F32>, grid, dim3(64), 0, s, a);
-  else if (fmt == PKV_FMT_BF16)
-    hipLaunchKernelGGL(attend_valu_kernel<PKV_FMT_BF16>, grid, dim3(64), 0, s, a);
-  else
-    hipLaunchKernelGGL(attend_valu_kernel<PKV_FMT_INT8>, grid, dim3(64), 0, s, a);
-  return hipGetLastError();
+  if (fmt == PKV_FMT_F32) return launch1(attend_valu_kernel<PKV_FMT_F32>, grid, dim3(64), 0, l, a);
+  if (fmt == PKV_FMT_BF16) return launch1(attend_valu_kernel<PKV_FMT_BF16>, grid, dim3(64), 0, l, a);
+  return launch1(attend_valu_kernel<PKV_FMT_INT8>, grid, dim3(64), 0, l, a);
 }
 
 }  // namespace pkv

@@ -109,17 +109,13 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
 
 }  // namespace
 
-hipError_t launch_gather(const GatherArgs& a, int fmt, hipStream_t s) {
+hipError_t launch_gather(const GatherArgs& a, int fmt, const Launch& l) {
   if (a.len <= 0) return hipSuccess;
   dim3 grid((a.len + kTok - 1) / kTok, a.n_kv_heads);
   const size_t shm = kTok * (a.head_dim + 1) * sizeof(uint32_t);
-  if (fmt == PKV_FMT_F32)
-    hipLaunchKernelGGL(gather_kernel<4>, grid, dim3(64), shm, s, a);
-  else if (fmt == PKV_FMT_BF16)
-    hipLaunchKernelGGL(gather_kernel<2>, grid, dim3(64), shm, s, a);
-  else
-    hipLaunchKernelGGL(gather_kernel<1>, grid, dim3(64), shm, s, a);
-  return hipGetLastError();
+  if (fmt == PKV_FMT_F32) return launch1(gather_kernel<4>, grid, dim3(64), shm, l, a);
+  if (fmt == PKV_FMT_BF16) return launch1(gather_kernel<2>, grid, dim3(64), shm, l, a);
+  return launch1(gather_kernel<1>, grid, dim3(64), shm, l, a);
 }
 
 }  // namespace pkv

@@ -86,25 +86,33 @@ WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_split) {
   return w;
 }
 
-// Timing: an event pair around one kernel pass, recorded only while enabled.
+// Timing: while enabled, each kernel pass is launched with an event pair
+// that its dispatch stamps with the kernel's start and end; the pairs are
+// kept for pkv_timing_read.
 struct Timer {
   pkv_cache* c;
   int kind;
-  hipStream_t s;
-  hipEvent_t e0 = nullptr;
-  Timer(pkv_cache* c_, int kind_, hipStream_t s_) : c(c_), kind(kind_), s(s_) {
-    if (c->timing && hipEventCreate(&e0) == hipSuccess) hipEventRecord(e0, s);
-  }
-  void stop() {
-    if (!e0) return;
-    hipEvent_t e1;
-    if (hipEventCreate(&e1) == hipSuccess) {
-      hipEventRecord(e1, s);
-      c->events[kind].emplace_back(e0, e1);
-    } else {
-      hipEventDestroy(e0);
+  pkv::Launch l;
+  Timer(pkv_cache* c_, int kind_, hipStream_t s) : c(c_), kind(kind_) {
+    l.s = s;
+    if (!c->timing) return;
+    if (hipEventCreate(&l.e0) != hipSuccess) {
+      l.e0 = nullptr;
+    } else if (hipEventCreate(&l.e1) != hipSuccess) {
+      hipEventDestroy(l.e0);
+      l.e0 = l.e1 = nullptr;
     }
-    e0 = nullptr;
+  }
+  // after the launch: keep the pair if a kernel was launched with it
+  void stop(hipError_t e) {
+    if (!l.e0) return;
+    if (e == hipSuccess && l.used) {
+      c->events[kind].emplace_back(l.e0, l.e1);
+    } else {
+      hipEventDestroy(l.e0);
+      hipEventDestroy(l.e1);
+    }
+    l.e0 = l.e1 = nullptr;
   }
 };
 
@@ -238,8 +246,8 @@ int pkv_paged_write(pkv_cache* c, int32_t layer, const int32_t* table, int32_t t
   a.total_new = total_new;
   a.decode_lens = nullptr;
   Timer tm(c, PKV_T_WRITE, static_cast<hipStream_t>(stream));
-  hipError_t e = pkv::launch_write(a, c->L.format, in_dtype, static_cast<hipStream_t>(stream));
-  tm.stop();
+  hipError_t e = pkv::launch_write(a, c->L.format, in_dtype, tm.l);
+  tm.stop(e);
   if (e != hipSuccess) return fail(PKV_EHIP, "write launch failed: %s", hipGetErrorString(e));
   return PKV_OK;
 }
@@ -369,8 +377,8 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
       w.total_new = batch;
       w.decode_lens = lens;
       Timer tw(c, PKV_T_WRITE, s);
-      e = pkv::launch_write(w, c->L.format, in_dtype, s);
-      tw.stop();
+      e = pkv::launch_write(w, c->L.format, in_dtype, tw.l);
+      tw.stop(e);
       if (e != hipSuccess) return fail(PKV_EHIP, "write launch failed: %s", hipGetErrorString(e));
     }
   }
@@ -382,15 +390,15 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
   a.single_done = mfma && max_len > 0;
   if (max_len > 0) {
     Timer tm(c, PKV_T_ATTEND_SPLIT, s);
-    e = mfma ? pkv::launch_attend_mfma(a, c->L.format, s)
-             : pkv::launch_attend_valu(a, c->L.format, s);
-    tm.stop();
+    e = mfma ? pkv::launch_attend_mfma(a, c->L.format, tm.l)
+             : pkv::launch_attend_valu(a, c->L.format, tm.l);
+    tm.stop(e);
     if (e != hipSuccess) return fail(PKV_EHIP, "attend launch failed: %s", hipGetErrorString(e));
     if (a.fuse_combine) return PKV_OK;  // the split pass combined the splits itself
   }
   Timer tm(c, PKV_T_ATTEND_COMBINE, s);
-  e = pkv::launch_reduce(a, s);
-  tm.stop();
+  e = pkv::launch_reduce(a, tm.l);
+  tm.stop(e);
   if (e != hipSuccess) return fail(PKV_EHIP, "reduce launch failed: %s", hipGetErrorString(e));
   return PKV_OK;
 }
@@ -459,8 +467,8 @@ int pkv_gather(pkv_cache* c, int32_t layer, const int32_t* table_row, int32_t le
   a.head_dim = c->L.head_dim;
   a.len = len;
   Timer tm(c, PKV_T_GATHER, static_cast<hipStream_t>(stream));
-  hipError_t e = pkv::launch_gather(a, c->L.format, static_cast<hipStream_t>(stream));
-  tm.stop();
+  hipError_t e = pkv::launch_gather(a, c->L.format, tm.l);
+  tm.stop(e);
   if (e != hipSuccess) return fail(PKV_EHIP, "gather launch failed: %s", hipGetErrorString(e));
   return PKV_OK;
 }

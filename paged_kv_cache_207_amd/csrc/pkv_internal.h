@@ -1,6 +1,7 @@
 // Internal declarations shared by the host library and the kernel files.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -85,17 +86,36 @@ struct GatherArgs {
 // Element size of a page format in bytes.
 inline int format_bytes(int fmt) { return fmt == PKV_FMT_F32 ? 4 : fmt == PKV_FMT_BF16 ? 2 : 1; }
 
+// Where a kernel goes: the stream and, while timing is on, two events that
+// the dispatch itself stamps with the kernel's start and end (no marker
+// packets between kernels, so timing does not lengthen a step).  `used` is
+// set once a kernel has been launched with them.
+struct Launch {
+  hipStream_t s = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  mutable bool used = false;
+};
+
+// Launch a kernel whose only parameter is an argument struct.
+template <typename K, typename A>
+inline hipError_t launch1(K kernel, dim3 grid, dim3 block, size_t shm, const Launch& l, A arg) {
+  void* args[] = {&arg};
+  l.used = true;
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, shm, l.s,
+                            l.e0, l.e1, 0);
+}
+
 // Launchers (return the hipError_t of the launch).
-hipError_t launch_write(const WriteArgs& a, int fmt, int in_dtype, hipStream_t s);
-hipError_t launch_gather(const GatherArgs& a, int fmt, hipStream_t s);
-hipError_t launch_attend_valu(const AttendArgs& a, int fmt, hipStream_t s);
+hipError_t launch_write(const WriteArgs& a, int fmt, int in_dtype, const Launch& l);
+hipError_t launch_gather(const GatherArgs& a, int fmt, const Launch& l);
+hipError_t launch_attend_valu(const AttendArgs& a, int fmt, const Launch& l);
 // Returns hipErrorNotSupported when the shape has no matrix-core variant.
-hipError_t launch_attend_mfma(const AttendArgs& a, int fmt, hipStream_t s);
+hipError_t launch_attend_mfma(const AttendArgs& a, int fmt, const Launch& l);
 constexpr int kMaxMfmaBatch = 4096;   // the work list lives in LDS: 12 bytes per sequence
 constexpr int kMaxMfmaKvHeads = 64;  // split counters: a fixed region of the workspace
 bool mfma_supported(int fmt, int q_bf16, int head_dim, int page_size, int group, int batch,
                     int n_kv_heads);
-hipError_t launch_reduce(const AttendArgs& a, hipStream_t s);
+hipError_t launch_reduce(const AttendArgs& a, const Launch& l);
 hipError_t launch_probe(const void* src, void* dst, float* sink, uint64_t bytes, int mode,
                         hipStream_t s);
 int probe_blocks(uint64_t bytes);

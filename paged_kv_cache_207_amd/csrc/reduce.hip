@@ -84,11 +84,10 @@ __global__ void table_apply_kernel(int32_t* table, int32_t stride, int32_t batch
 
 }  // namespace
 
-hipError_t launch_reduce(const AttendArgs& a, hipStream_t s) {
+hipError_t launch_reduce(const AttendArgs& a, const Launch& l) {
   if (a.batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL(reduce_kernel, dim3(a.batch * a.n_q_heads), dim3(64),
-                     (size_t)a.n_split * sizeof(float), s, a);
-  return hipGetLastError();
+  return launch1(reduce_kernel, dim3(a.batch * a.n_q_heads), dim3(64),
+                 (size_t)a.n_split * sizeof(float), l, a);
 }
 
 hipError_t launch_table_apply(int32_t* table, int32_t stride, int32_t batch, const int32_t* upd,

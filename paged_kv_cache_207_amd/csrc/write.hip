@@ -211,20 +211,19 @@ __global__ __launch_bounds__(64) void write_kernel(WriteArgs a) {
 
 }  // namespace
 
-hipError_t launch_write(const WriteArgs& a, int fmt, int in_dtype, hipStream_t s) {
+hipError_t launch_write(const WriteArgs& a, int fmt, int in_dtype, const Launch& l) {
   if (a.total_new <= 0) return hipSuccess;
   dim3 grid((a.total_new + kRows - 1) / kRows, a.n_kv_heads);
   const size_t shm = 2 * kRows * (a.head_dim + 1) * sizeof(uint32_t);
   const bool bf = in_dtype == PKV_DT_BF16;
   if (fmt == PKV_FMT_F32)
-    hipLaunchKernelGGL((write_kernel<PKV_FMT_F32, 0>), grid, dim3(64), shm, s, a);
+    return launch1(write_kernel<PKV_FMT_F32, 0>, grid, dim3(64), shm, l, a);
   else if (fmt == PKV_FMT_BF16)
-    hipLaunchKernelGGL((write_kernel<PKV_FMT_BF16, 1>), grid, dim3(64), shm, s, a);
+    return launch1(write_kernel<PKV_FMT_BF16, 1>, grid, dim3(64), shm, l, a);
   else if (bf)
-    hipLaunchKernelGGL((write_kernel<PKV_FMT_INT8, 1>), grid, dim3(64), shm, s, a);
+    return launch1(write_kernel<PKV_FMT_INT8, 1>, grid, dim3(64), shm, l, a);
   else
-    hipLaunchKernelGGL((write_kernel<PKV_FMT_INT8, 0>), grid, dim3(64), shm, s, a);
-  return hipGetLastError();
+    return launch1(write_kernel<PKV_FMT_INT8, 0>, grid, dim3(64), shm, l, a);
 }
 
 }  // namespace pkv

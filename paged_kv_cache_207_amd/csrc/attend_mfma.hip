@@ -26,6 +26,13 @@
 // computed.  int8 pages are converted to bf16 exactly (|code| <= 127); the
 // per-token K scale multiplies the score and the V scale the weight.
 //
+// Memory instructions, not only bytes, set the pace: every K load covers 64
+// contiguous bytes of each row it touches (int8 lanes load 16 codes at once,
+// see kdim_of), and a step's 64 per-token scales arrive in one 4-byte load
+// per lane and are handed to the lanes that need them by lane shuffles.
+// Measured on the int8 workloads, each of the two cut the split pass by
+// about a fifth; a third register set (two steps in flight) was slower.
+//
 // Work distribution: a persistent grid (as many single-wave workgroups as
 // the chip holds at once) walks a work list of (split, KV head) items built
 // in LDS from the lengths, full splits first.  A sequence that fits in one
@@ -49,17 +56,21 @@ template <int FMT, int D>
 struct Step {
   static constexpr int NC = D / 32;  // 32-wide k chunks of the Q.K product
   static constexpr int ND = D / 16;  // 16-row dim tiles of the P.V product
-  // K: bf16 8 values / int8 8 codes per (tile, chunk); V: 8 tokens per dim tile
-  using KT = typename std::conditional<FMT == PKV_FMT_BF16, uint4, uint2>::type;
-  using VT = KT;
+  // K: one 16-byte load per (tile, load) = 8 bf16 values (one k chunk) or
+  // 16 int8 codes (two k chunks); V: 8 tokens per dim tile
+  static constexpr int NK = FMT == PKV_FMT_BF16 ? NC : D / 64;
+  using KT = uint4;
+  using VT = typename std::conditional<FMT == PKV_FMT_BF16, uint4, uint2>::type;
   // the same bytes as raw 32-bit vectors, for non-temporal loads
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  using NKT = typename std::conditional<sizeof(KT) == 16, u32x4, u32x2>::type;
-  using NVT = NKT;
-  KT k[2][NC];
+  using NKT = u32x4;
+  using NVT = typename std::conditional<sizeof(VT) == 16, u32x4, u32x2>::type;
+  KT k[2][NK];
   VT v[ND];
-  f32x4 ks[2], vs[2];  // int8 only: scales of the lane's tokens 8j+4t .. 8j+4t+3
+  // int8 only: lane x < 32 holds the K scale of token x of the step, lane
+  // 32 + x its V scale; compute_step fetches the ones it needs from there
+  float sc;
   bool live_a, live_b;  // the step's first / second 16 tokens sit on a valid page
 };
 
@@ -81,6 +92,17 @@ __device__ __forceinline__ uint2 codes_to_bf16(uint32_t w) {
   r.x = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
   r.y = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
   return r;
+}
+
+// The head dims that k slots 8j .. 8j+7 of Q.K chunk c stand for (the
+// contraction may take the dims in any order, as long as K and Q agree).
+// bf16: dims 32c + 8j .. +7, one 16-byte load of a K row per chunk.  int8:
+// lane j's 16 consecutive codes 64 (c / 2) + 16j .. +15 come in one 16-byte
+// load and serve chunks c and c + 1 (codes 0-7, then 8-15), so a K load
+// instruction covers 64 contiguous bytes of each row it reads, as in bf16.
+template <int FMT>
+__device__ __forceinline__ int kdim_of(int c, int j) {
+  return FMT == PKV_FMT_BF16 ? 32 * c + 8 * j : 64 * (c >> 1) + 16 * j + 8 * (c & 1);
 }
 
 // Write 4 consecutive outputs (bf16 rounded to nearest even, or f32).
@@ -152,6 +174,8 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
   using VT = typename S::VT;
   constexpr int NC = S::NC, ND = S::ND;
   constexpr int ESZ = FMT == PKV_FMT_BF16 ? 2 : 1;
+  constexpr int KPL = NC / S::NK;  // k chunks per K load
+  auto kdim = [](int c, int jj) { return kdim_of<FMT>(c, jj); };
   const int lane = threadIdx.x;
   const int n = lane & 15;  // head column (B/C operands), row (A operands)
   const int j = lane >> 4;  // k group (A/B operands), row quad (C operand)
@@ -245,11 +269,11 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
   bf16x8 qf[NC];
   {
     const uint16_t* q = static_cast<const uint16_t*>(a.q) +
-                        ((int64_t)b * a.n_q_heads + (int64_t)g * G + n) * D + 8 * j;
+                        ((int64_t)b * a.n_q_heads + (int64_t)g * G + n) * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       uint4 x = {0, 0, 0, 0};
-      if (n < G) x = *reinterpret_cast<const uint4*>(q + 32 * c);
+      if (n < G) x = *reinterpret_cast<const uint4*>(q + kdim(c, j));
       qf[c] = as_bf16x8(x);
     }
   }
@@ -309,10 +333,9 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
         const bool on_b = BS == 16 && tok >= 16;
         const char* kb = kp + (on_b ? slab_b : slab_a) * slab_bytes;
         const int row = BS == 16 ? (tok & 15) : slot0 + tok;
-        const int koff = (row * D + 8 * j) * ESZ;
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-          r.k[tau][c] = stream_load<KT, typename S::NKT>(kb + koff + 32 * c * ESZ);
+        for (int c = 0; c < S::NK; ++c)
+          r.k[tau][c] = stream_load<KT, typename S::NKT>(kb + (row * D + kdim(KPL * c, j)) * ESZ);
       }
       // V operand: tokens 8j .. 8j+7 of dim 16 * dt + n
       const bool v_on_b = BS == 16 && j >= 2;
@@ -323,12 +346,11 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
       for (int dt = 0; dt < ND; ++dt)
         r.v[dt] = stream_load<VT, typename S::NVT>(vb + voff + 16 * dt * bs * ESZ);
       if (FMT == PKV_FMT_INT8) {
-        const int64_t ss = (v_on_b ? slab_b : slab_a) * bs + col;
-#pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-          r.ks[tau] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.k_scales + ss + 4 * tau));
-          r.vs[tau] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.v_scales + ss + 4 * tau));
-        }
+        const int x = lane & 31;
+        const bool s_on_b = BS == 16 && x >= 16;
+        const int slot = BS == 16 ? (x & 15) : slot0 + x;
+        const float* sb = lane < 32 ? a.k_scales : a.v_scales;
+        r.sc = __builtin_nontemporal_load(sb + (s_on_b ? slab_b : slab_a) * bs + slot);
       }
     };
 
@@ -344,13 +366,23 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
           if constexpr (FMT == PKV_FMT_BF16) {
             ka = as_bf16x8(r.k[tau][c]);
           } else {
-            const uint2 lo = codes_to_bf16(r.k[tau][c].x), hi = codes_to_bf16(r.k[tau][c].y);
+            // chunk c: codes 8 (c % 2) .. +7 of the lane's 16-code load c / 2
+            const uint4& w = r.k[tau][c >> 1];
+            const uint2 lo = codes_to_bf16(c & 1 ? w.z : w.x), hi = codes_to_bf16(c & 1 ? w.w : w.y);
             ka = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
           }
           sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[c], sacc[tau], 0, 0, 0);
         }
       }
       const bool lane_live = BS == 16 && j >= 2 ? r.live_b : r.live_a;
+      float ksc[8], vsc[8];  // int8: scales of tokens 8j .. 8j+7
+      if constexpr (FMT == PKV_FMT_INT8) {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          ksc[x] = __shfl(r.sc, 8 * j + x, 64);
+          vsc[x] = __shfl(r.sc, 32 + 8 * j + x, 64);
+        }
+      }
       float sv[8];
       bool ok[8];  // token 8j + x of the step is real
       float mx = -INFINITY;
@@ -358,7 +390,7 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
       for (int x = 0; x < 8; ++x) {
         ok[x] = lane_live && ts + 8 * j + x < w_end;
         float y = sacc[x >> 2][x & 3] * qs;
-        if (FMT == PKV_FMT_INT8) y *= r.ks[x >> 2][x & 3];
+        if (FMT == PKV_FMT_INT8) y *= ksc[x];
         sv[x] = ok[x] ? y : -INFINITY;
         mx = fmaxf(mx, sv[x]);
       }
@@ -374,7 +406,7 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
         const float p = ok[x] ? __builtin_amdgcn_exp2f(sv[x] - m_use) : 0.f;
         psum += p;
         float pw = p;
-        if (FMT == PKV_FMT_INT8) pw = ok[x] ? p * r.vs[x >> 2][x & 3] : 0.f;
+        if (FMT == PKV_FMT_INT8) pw = ok[x] ? p * vsc[x] : 0.f;
         pb[x] = (__bf16)pw;
       }
       l = l * alpha + psum;
@@ -422,10 +454,10 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
       uint4 kb4[NC];
       uint32_t vnew[ND];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kb4[c] = *reinterpret_cast<const uint4*>(kr + 32 * c + 8 * j);
+      for (int c = 0; c < NC; ++c) kb4[c] = *reinterpret_cast<const uint4*>(kr + kdim(c, j));
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) vnew[dt] = vr[16 * dt + n];
-      KT knew[NC];
+      KT knew[S::NK];
       float ks_new = 0.f, vs_new = 0.f;
       if constexpr (FMT == PKV_FMT_BF16) {
 #pragma unroll
@@ -455,16 +487,20 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
           return (uint32_t)(int32_t)q & 0xffu;
         };
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const uint32_t w4[4] = {kb4[c].x, kb4[c].y, kb4[c].z, kb4[c].w};
-          uint32_t cw[2] = {0u, 0u};
+        for (int p = 0; p < S::NK; ++p) {
+          uint32_t cw[4] = {0u, 0u, 0u, 0u};  // codes of chunks 2p (cw 0-1) and 2p + 1 (cw 2-3)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = code(bf16_bits_to_f32(w4[i] & 0xffffu), ks_new);
-            const uint32_t hi = code(bf16_bits_to_f32(w4[i] >> 16), ks_new);
-            cw[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
+          for (int h = 0; h < 2; ++h) {
+            const uint4 kb = kb4[2 * p + h];
+            const uint32_t w4[4] = {kb.x, kb.y, kb.z, kb.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t lo = code(bf16_bits_to_f32(w4[i] & 0xffffu), ks_new);
+              const uint32_t hi = code(bf16_bits_to_f32(w4[i] >> 16), ks_new);
+              cw[2 * h + (i >> 1)] |= (lo | (hi << 8)) << (16 * (i & 1));
+            }
           }
-          knew[c] = KT{cw[0], cw[1]};
+          knew[p] = KT{cw[0], cw[1], cw[2], cw[3]};
         }
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) vnew[dt] = code(bf16_bits_to_f32(vnew[dt]), vs_new);
@@ -481,8 +517,8 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
         char* vw = static_cast<char*>(const_cast<void*>(a.v_pages)) + slab * slab_bytes;
         if (n == 0) {  // lanes j = 0..3 of one row hold the whole K row
 #pragma unroll
-          for (int c = 0; c < NC; ++c)
-            *reinterpret_cast<KT*>(kw + ((int64_t)slot * D + 32 * c + 8 * j) * ESZ) = knew[c];
+          for (int c = 0; c < S::NK; ++c)
+            *reinterpret_cast<KT*>(kw + ((int64_t)slot * D + kdim(KPL * c, j)) * ESZ) = knew[c];
         }
         if (j == 0) {  // lanes n = 0..15 hold every dim of the V row
 #pragma unroll
@@ -501,7 +537,7 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
+        for (int c = 0; c < S::NK; ++c)
           if (tau == tau_new && n == n_new) r.k[tau][c] = knew[c];
       if (j == j_new) {
         const int e = x_new & 7;  // element of this lane's 8-token V operand
@@ -524,16 +560,10 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
             r.v[dt] = uint2{w[0], w[1]};
           }
         }
-        if (FMT == PKV_FMT_INT8) {
-#pragma unroll
-          for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (tau == tau_new && i == (x_new & 3)) {
-                r.ks[tau][i] = ks_new;
-                r.vs[tau][i] = vs_new;
-              }
-        }
+      }
+      if (FMT == PKV_FMT_INT8) {
+        if (lane == x_new) r.sc = ks_new;
+        if (lane == 32 + x_new) r.sc = vs_new;
       }
     };
 
@@ -542,24 +572,24 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
     // a load under a condition would make the compiler wait for every
     // outstanding load (the prefetch included) before each step.
     const int n_steps = (w_end - w0 + 31) / 32;
+    auto T = [&](int i) { return w0 + 32 * i; };
     S r0, r1;
-    load_step(w0, r0);
+    load_step(T(0), r0);
     int st = 0;
     for (; st + 2 < n_steps; st += 2) {
-      const int ts = w0 + 32 * st;
-      load_step(ts + 32, r1);
-      compute_step(ts, r0);
-      load_step(ts + 64, r0);
-      compute_step(ts + 32, r1);
+      load_step(T(st + 1), r1);
+      compute_step(T(st), r0);
+      load_step(T(st + 2), r0);
+      compute_step(T(st + 1), r1);
     }
     if (st + 1 < n_steps) {
-      load_step(w0 + 32 * (st + 1), r1);
-      compute_step(w0 + 32 * st, r0);
-      substitute_new(w0 + 32 * (st + 1), r1);
-      compute_step(w0 + 32 * (st + 1), r1);
+      load_step(T(st + 1), r1);
+      compute_step(T(st), r0);
+      substitute_new(T(st + 1), r1);
+      compute_step(T(st + 1), r1);
     } else {
-      substitute_new(w0 + 32 * st, r0);
-      compute_step(w0 + 32 * st, r0);
+      substitute_new(T(st), r0);
+      compute_step(T(st), r0);
     }
   }
 

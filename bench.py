@@ -481,6 +481,7 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "kv_bytes_per_step": kvb,
         "achievable_read_GBps": round(read_gbps, 1),
+        "split_pass_frac_of_achievable_read": round(achieved / read_gbps, 4),
         "wall_ms_per_step": round(wall_ms, 5),
         "cold_cache": {"split_pass_us": round(kt_cold["attend_split"] * 1e3, 2),
                        "combine_us": round(kt_cold["attend_combine"] * 1e3, 2),

@@ -54,8 +54,8 @@ int plan_split(const pkv_cache* c, int batch, int n_q_heads, int max_len) {
   return (int)split;
 }
 
+// splits per sequence; the combine kernel keeps one weight per split in LDS
 constexpr int kMaxSplits = 16384;
-constexpr int kFuseMaxSplits = 8;  // in-kernel combine up to this many splits per sequence  // per sequence; the combine keeps one weight per split in LDS
 
 int check_split(const pkv_cache* c, int32_t split) {
   if (split < 0) return fail(PKV_EINVAL, "split_tokens must be >= 0");

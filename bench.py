@@ -276,10 +276,11 @@ def run_shared_prefix(args, device):
     upd_dev = torch.empty((B + 8, 3), dtype=torch.int32, device=device)
     torch.cuda.synchronize()
 
+    ones = np.ones(B, np.int32)
+
     def job(seqs):
         for s in range(sp.n_steps):
-            for b in range(B):
-                seqs.append(b, 1)
+            seqs.append_all(ones)  # every sequence grows by its new token
             n = seqs.take_updates(upd_host[s]).shape[0]
             if n:
                 upd_dev[:n].copy_(upd_host[s][:n], non_blocking=True)

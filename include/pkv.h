@@ -276,6 +276,11 @@ void pkv_seqs_destroy(pkv_seqs* seqs); /* releases every page still held */
 /* Grow sequence b by n tokens (allocating pages as needed, all or nothing):
  * ENOMEM leaves the sequence unchanged, ERANGE if the row would overflow. */
 int pkv_seqs_append(pkv_seqs* seqs, int32_t b, int32_t n);
+/* Grow every sequence b by n[b] tokens (host int32 [batch], each >= 0) in
+ * one call, all or nothing over the batch: pages go out as if
+ * pkv_seqs_append(b, n[b]) ran for b = 0, 1, ... in order; ENOMEM or ERANGE
+ * (checked for every sequence first) leave every sequence unchanged. */
+int pkv_seqs_append_all(pkv_seqs* seqs, const int32_t* n);
 /* Sequence dst (which must be empty) shares the first n_pages pages of src:
  * each gets one more reference.  Its length becomes n_pages * page_size. */
 int pkv_seqs_share(pkv_seqs* seqs, int32_t dst, int32_t src, int32_t n_pages);

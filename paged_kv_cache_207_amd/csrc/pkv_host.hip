@@ -624,6 +624,32 @@ int pkv_seqs_append(pkv_seqs* s, int32_t b, int32_t n) {
   return PKV_OK;
 }
 
+int pkv_seqs_append_all(pkv_seqs* s, const int32_t* n) {
+  if (!s || !n) return fail(PKV_EINVAL, "null argument");
+  int64_t total = 0;
+  for (int32_t b = 0; b < s->batch; ++b) {
+    if (n[b] < 0) return fail(PKV_EINVAL, "n[%d] = %d is negative", b, n[b]);
+    const int64_t need = ((int64_t)s->lens[b] + n[b] + s->page_size - 1) / s->page_size;
+    if (need > s->stride)
+      return fail(PKV_ERANGE, "sequence %d would need %lld pages, the row holds %d", b,
+                  (long long)need, s->stride);
+    total += std::max<int64_t>(need - s->npages[b], 0);
+  }
+  if (total > INT32_MAX) return fail(PKV_ENOMEM, "too many pages asked for");
+  std::vector<int32_t> ids((size_t)total);
+  if (total > 0)
+    if (int e = pkv_pool_alloc_n(s->pool, (int32_t)total, ids.data())) return e;
+  size_t next = 0;  // sequence by sequence, lowest pages first: as append(b, n[b]) in order
+  for (int32_t b = 0; b < s->batch; ++b) {
+    const int64_t new_len = (int64_t)s->lens[b] + n[b];
+    const int32_t need = (int32_t)((new_len + s->page_size - 1) / s->page_size);
+    for (int32_t j = s->npages[b]; j < need; ++j) s->set(b, j, ids[next++]);
+    s->npages[b] = std::max(s->npages[b], need);
+    s->lens[b] = (int32_t)new_len;
+  }
+  return PKV_OK;
+}
+
 int pkv_seqs_share(pkv_seqs* s, int32_t dst, int32_t src, int32_t n_pages) {
   if (!s || dst < 0 || dst >= s->batch || src < 0 || src >= s->batch || dst == src || n_pages < 0)
     return fail(PKV_EINVAL, "bad arguments");

@@ -9,6 +9,7 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,6 +59,7 @@ SYMBOLS = [
     ("pkv_seqs_create", C.c_int, [_P, _I32, _I32, _I32, C.POINTER(_P)]),
     ("pkv_seqs_destroy", None, [_P]),
     ("pkv_seqs_append", C.c_int, [_P, _I32, _I32]),
+    ("pkv_seqs_append_all", C.c_int, [_P, _PI32]),
     ("pkv_seqs_share", C.c_int, [_P, _I32, _I32, _I32]),
     ("pkv_seqs_release", C.c_int, [_P, _I32]),
     ("pkv_seqs_table", _PI32, [_P]),
@@ -353,6 +355,23 @@ class SeqTables:
 
     def append(self, b: int, n: int):
         _check(lib().pkv_seqs_append(self._h, b, n))
+
+    def append_all(self, n) -> None:
+        """Grow every sequence b by n[b] tokens (an int grows each by n), all
+        or nothing over the batch."""
+        if isinstance(n, np.ndarray) and n.dtype == np.int32 and n.flags.c_contiguous:
+            if n.shape != (self.batch,):
+                raise ValueError(f"n has shape {n.shape} for {self.batch} sequences")
+            _check(lib().pkv_seqs_append_all(self._h, n.ctypes.data_as(_PI32)))
+            return
+        if isinstance(n, int):
+            arr = (C.c_int32 * self.batch)(*([n] * self.batch))
+        else:
+            vals = [int(x) for x in n]
+            if len(vals) != self.batch:
+                raise ValueError(f"n has {len(vals)} entries for {self.batch} sequences")
+            arr = (C.c_int32 * self.batch)(*vals)
+        _check(lib().pkv_seqs_append_all(self._h, C.cast(arr, _PI32)))
 
     def share(self, dst: int, src: int, n_pages: int):
         _check(lib().pkv_seqs_share(self._h, dst, src, n_pages))

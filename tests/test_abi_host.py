@@ -165,6 +165,43 @@ def test_seqs_failures_leave_state_unchanged():
     assert pool.num_free() == 5
 
 
+def test_seqs_append_all_matches_appends_in_order():
+    rng = random.Random(11)
+    B, stride, bs, P = 6, 12, 8, 60
+    pa, pb = pkv.PagePool(P), pkv.PagePool(P)
+    sa, sb = pkv.SeqTables(pa, B, stride, bs), pkv.SeqTables(pb, B, stride, bs)
+    for step in range(40):
+        n = [rng.randint(0, 9) for _ in range(B)]
+        try:
+            sa.append_all(n)
+            ok = True
+        except pkv.PkvError as e:
+            assert e.code in (pkv.ENOMEM, pkv.ERANGE)
+            ok = False
+        if ok:
+            for b in range(B):
+                sb.append(b, n[b])
+        else:
+            # all or nothing: the same request done one by one must fail somewhere
+            # and the batched call left everything as it was
+            assert sa.lens() == sb.lens() and sa.table() == sb.table()
+            before = pa.num_free()
+            assert before == pb.num_free()
+            for b in range(B):  # release one sequence to make room and go on
+                if sa.lens()[b]:
+                    sa.release(b)
+                    sb.release(b)
+                    break
+        assert sa.lens() == sb.lens() and sa.table() == sb.table()
+        assert pa.num_free() == pb.num_free()
+        assert sa.take_updates().tolist() == sb.take_updates().tolist()
+    with pytest.raises(pkv.PkvError) as e:
+        sa.append_all([0] * (B - 1) + [-1])
+    assert e.value.code == pkv.EINVAL
+    sa.close()
+    sb.close()
+
+
 # ------------------------------------------------------------- validation --
 
 FAKE = 1 << 20  # an aligned non-null address; no call below reaches a launch

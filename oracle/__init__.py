@@ -14,5 +14,5 @@ hand-derived pool fixtures).  The int8 rounding rule has no page to compare
 against: its parity is pinned by definition and by properties only.
 """
 from .paged_cache import OracleCache, quantize_int8_rows, bf16_bits_to_f32  # noqa: F401
-from .attention import attend, attend_one  # noqa: F401
+from .attention import attend, attend_one, attend_multi, query_positions  # noqa: F401
 from .pool import PoolModel, PoolError  # noqa: F401

@@ -328,6 +328,71 @@ def shared_prefix(batch=256, prefix_pages=64, lo=16, hi=2048, n_steps=32, n_q_he
     return SharedPrefix(base, prefix_pages, suffix, n_steps)
 
 
+@dataclass
+class ChunkedPrefill:
+    """Several new tokens per sequence at once (a prefill chunk).
+
+    ``base`` holds the sequences at their final length (context + chunk);
+    its write rounds are the context (from position 0), then the chunk (from
+    position context[b]).  The chunk's queries are rows cu_q[b] .. cu_q[b+1]
+    of ``queries()``, one per new token, in position order.
+    """
+
+    base: Workload
+    context: np.ndarray  # int32 [B]: tokens already stored before the chunk
+    chunk: np.ndarray  # int32 [B]: new tokens (and queries) per sequence
+
+    @property
+    def cu_q(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.chunk)]).astype(np.int32)
+
+    @property
+    def total_q(self) -> int:
+        return int(self.chunk.sum())
+
+    @property
+    def max_q(self) -> int:
+        return int(self.chunk.max()) if len(self.chunk) else 0
+
+    def context_round(self, kv: dict | None = None) -> WriteRound:
+        return self.base.rounds(kv=kv)[0]
+
+    def chunk_round(self, kv: dict | None = None) -> WriteRound:
+        r = self.base.rounds(kv=kv)
+        if len(r) > 1:
+            return r[1]
+        B = self.base.batch  # every chunk empty
+        empty = torch.empty((0, self.base.n_kv_heads, self.base.head_dim),
+                            dtype=self.base.in_dtype)
+        return WriteRound(self.base.lens.copy(), np.zeros(B + 1, np.int32), empty, empty)
+
+    def queries(self) -> torch.Tensor:
+        w = self.base
+        g = torch.Generator().manual_seed(w.seed * 7919 + 29)
+        q = torch.randn((self.total_q, w.n_q_heads, w.head_dim), generator=g)
+        return q.to(w.q_dtype)
+
+
+def chunked_prefill(batch=4, context=(4096, 4096), chunk=(512, 512), n_q_heads=32,
+                    n_kv_heads=8, head_dim=128, page_size=16, kv_format="bf16",
+                    seed: int = 6) -> ChunkedPrefill:
+    """Chunked prefill: per sequence a context length uniform in ``context``
+    and a chunk length uniform in ``chunk`` (inclusive ranges), pool 1.25x the
+    pages needed, shuffled page ids."""
+    rng = np.random.default_rng(1000 + seed)
+    ctx = rng.integers(context[0], context[1] + 1, size=batch).astype(np.int32)
+    ch = rng.integers(chunk[0], chunk[1] + 1, size=batch).astype(np.int32)
+    lens = (ctx + ch).astype(np.int32)
+    P, tables = _random_pool(rng, lens, page_size)
+    in_dtype = torch.float32 if kv_format == "f32" else torch.bfloat16
+    base = Workload("chunked_prefill", P, page_size, n_kv_heads, head_dim, n_q_heads, kv_format,
+                    in_dtype, in_dtype if kv_format == "f32" else torch.bfloat16,
+                    float(np.float32(1.0 / math.sqrt(head_dim))), tables, lens, 2000 + seed,
+                    head_chunk=ctx.copy(), chunk=max(int(ch.max()), 1))
+    return ChunkedPrefill(base, ctx, ch)
+
+
 def by_name(name: str, **kw):
     return {"tiny_f32": tiny_f32, "decode_bf16": decode_bf16, "long_bf16": long_bf16,
-            "int8_kv": int8_kv, "shared_prefix": shared_prefix}[name](**kw)
+            "int8_kv": int8_kv, "shared_prefix": shared_prefix,
+            "chunked_prefill": chunked_prefill}[name](**kw)

@@ -368,6 +368,91 @@ def test_int8_attention_is_attention_on_dequantized_rows():
         assert np.max(np.abs(out[b] - ref)) < 1e-12
 
 
+# ------------------------------------------------- several queries per seq --
+
+def _contiguous_causal_sdpa(K, V, Q, scale, G):
+    """torch SDPA (float64) of T query rows over n contiguous tokens, the
+    rows being the last T tokens: row i may see tokens 0 .. n - T + i."""
+    n, T = K.shape[0], Q.shape[0]
+    k = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+    v = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+    q = torch.from_numpy(Q).permute(1, 0, 2)[None]  # [1, Hq, T, D]
+    mask = torch.ones(T, n, dtype=torch.bool).tril(diagonal=n - T)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("G,D,ctx,T", [(1, 16, 40, 9), (2, 32, 0, 21), (4, 16, 17, 1),
+                                        (2, 64, 50, 50)])
+def test_multi_query_matches_masked_sdpa(G, D, ctx, T):
+    """An identity table is contiguous attention with the chunk's causal mask
+    (each chunk row sees the context and the chunk up to itself)."""
+    Hkv, bs = 2, 8
+    n = ctx + T
+    P = max(-(-n // bs), 1)
+    g = torch.Generator().manual_seed(G * 1000 + D + T)
+    k = torch.randn(n, Hkv, D, generator=g)
+    v = torch.randn(n, Hkv, D, generator=g)
+    q = torch.randn(T, Hkv * G, D, generator=g)
+    c = OracleCache(1, P, bs, Hkv, D, "f32")
+    table = np.arange(P, dtype=np.int32)[None]
+    c.write(0, table, np.zeros(1, np.int32), np.array([0, n], np.int32), k.numpy(), v.numpy(), "f32")
+    scale = float(np.float32(1 / math.sqrt(D)))
+    out = oracle.attend_multi(c, 0, q.numpy(), "f32", table, np.array([n]), np.array([0, T]),
+                              scale)
+    ref = _contiguous_causal_sdpa(k.double().numpy(), v.double().numpy(), q.double().numpy(),
+                                  scale, G)
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_multi_query_brute_force():
+    """Scalar loops with the positions written out by hand: two sequences,
+    chunks of 3 and 2 rows after contexts of 4 and 0 tokens."""
+    Hkv, G, D, bs = 1, 2, 4, 4
+    lens = np.array([7, 2])
+    cu = np.array([0, 3, 5])
+    positions = [4, 5, 6, 0, 1]  # context + i
+    g = torch.Generator().manual_seed(77)
+    rows = [torch.randn(int(L), Hkv, D, generator=g) for L in lens]
+    vrows = [torch.randn(int(L), Hkv, D, generator=g) for L in lens]
+    q = torch.randn(5, G, D, generator=g)
+    tables = np.array([[2, 0], [1, -1]], np.int32)
+    c = OracleCache(1, 3, bs, Hkv, D, "f32")
+    c.write(0, tables, np.zeros(2, np.int32), np.array([0, 7, 9], np.int32),
+            torch.cat(rows).numpy(), torch.cat(vrows).numpy(), "f32")
+    out = oracle.attend_multi(c, 0, q.numpy(), "f32", tables, lens, cu, 0.5)
+    assert list(oracle.query_positions(lens, cu)) == positions
+    for r, pos in enumerate(positions):
+        b = 0 if r < 3 else 1
+        for h in range(G):
+            sc = [0.5 * sum(float(q[r, h, d]) * float(rows[b][t, 0, d]) for d in range(D))
+                  for t in range(pos + 1)]
+            mx = max(sc)
+            e = [math.exp(x - mx) for x in sc]
+            for d in range(D):
+                ref = sum(e[t] * float(vrows[b][t, 0, d]) for t in range(pos + 1)) / sum(e)
+                assert abs(out[r, h, d] - ref) < 1e-12
+
+
+def test_multi_query_single_rows_are_decode():
+    """A chunk of one row is a decode query over the whole sequence, and every
+    chunk's last row sees the whole sequence as well."""
+    w = small_decode("bf16")
+    c = filled(w)
+    q = w.query()
+    dec = attend(c, 0, np_bits(q), "bf16", w.tables, w.lens, w.scale)
+    one = oracle.attend_multi(c, 0, np_bits(q), "bf16", w.tables, w.lens,
+                              np.arange(w.batch + 1), w.scale)
+    assert np.array_equal(dec, one)
+    # chunks of 3 rows whose last row carries the decode query
+    qq = np.repeat(np_bits(q), 3, axis=0)
+    multi = oracle.attend_multi(c, 0, qq, "bf16", w.tables, w.lens,
+                                np.arange(0, 3 * w.batch + 1, 3), w.scale)
+    assert np.array_equal(multi[2::3], dec)
+    # ... and its earlier rows see fewer tokens, so they differ
+    assert not np.allclose(multi[0::3], dec)
+
+
 # ------------------------------------------------------ planted mistakes ----
 
 def test_planted_mistakes_are_caught(monkeypatch):
@@ -404,3 +489,21 @@ def test_planted_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(me, "quantize_int8_rows", wrong_quant)
     with pytest.raises(AssertionError):
         test_int8_matches_scalar_reference()
+    monkeypatch.undo()
+    # strictly causal (a query not seeing its own token) -> SDPA and brute force fail
+    monkeypatch.setattr(oracle_attention, "_visible", lambda pos: max(pos, 0))
+    with pytest.raises(AssertionError):
+        test_multi_query_matches_masked_sdpa(2, 32, 0, 21)
+    with pytest.raises(AssertionError):
+        test_multi_query_brute_force()
+    monkeypatch.undo()
+    # chunk rows placed from position 0 instead of after the context -> SDPA fails
+    def from_zero(lens, cu_q):
+        cu = np.asarray(cu_q, np.int64)
+        pos = np.zeros(int(cu[-1]), np.int64)
+        for b in range(len(cu) - 1):
+            pos[cu[b]:cu[b + 1]] = np.arange(cu[b + 1] - cu[b])
+        return pos
+    monkeypatch.setattr(oracle_attention, "query_positions", from_zero)
+    with pytest.raises(AssertionError):
+        test_multi_query_matches_masked_sdpa(1, 16, 40, 9)

@@ -347,6 +347,89 @@ def run_shared_prefix(args, device):
     return line
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def run_chunked_prefill(args, device):
+    """Several queries per sequence: each step writes every sequence's chunk
+    of new rows (paged_write at position context[b]) and runs causal
+    multi-query attention of the chunk over context + chunk tokens.  The
+    context is written once before timing; each step rewrites the same chunk."""
+    cp = W.chunked_prefill()
+    w = cp.base
+    B = w.batch
+    log(f"workload chunked_prefill: B={B} context={cp.context.tolist()} "
+        f"chunk={cp.chunk.tolist()} Hq={w.n_q_heads} Hkv={w.n_kv_heads} D={w.head_dim} "
+        f"bs={w.page_size}")
+    cache = pkv.PagedKVCache(w.n_pages, w.page_size, w.n_kv_heads, w.head_dim, w.kv_format,
+                             device=device)
+    table = torch.as_tensor(w.tables).to(device)
+    kv = {b: w.seq_kv(b) for b in range(B)}
+    r0, r1 = cp.context_round(kv), cp.chunk_round(kv)
+    cache.write(table, torch.as_tensor(r0.start_pos).to(device),
+                torch.as_tensor(r0.cu_new).to(device), r0.k.to(device), r0.v.to(device))
+    start = torch.as_tensor(r1.start_pos).to(device)
+    cu_new = torch.as_tensor(r1.cu_new).to(device)
+    kc, vc = r1.k.to(device), r1.v.to(device)
+    lens = torch.as_tensor(w.lens).to(device)
+    cu_q = torch.as_tensor(cp.cu_q).to(device)
+    q = cp.queries().to(device)
+    out = torch.empty_like(q)
+
+    def step():
+        cache.write(table, start, cu_new, kc, vc)
+        cache.attend_multi(q, table, lens, cu_q, cp.max_q, w.max_len, w.scale, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert cache.status() == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    cache.timing_read()
+    cache.timing(True)
+    for _ in range(args.steps):
+        step()
+    cache.timing(False)
+    t = cache.timing_read()
+    attn_ms = t["attend_multi"][0] / max(t["attend_multi"][1], 1)
+    wr_ms = t["write"][0] / max(t["write"][1], 1)
+    # algorithmic work: every query row scores and weights its visible tokens
+    pos = (w.lens.astype(np.int64) - cp.chunk)[:, None]
+    visible = sum(int((pos[b, 0] + np.arange(1, int(cp.chunk[b]) + 1)).sum()) for b in range(B))
+    flops = 4 * w.n_q_heads * w.head_dim * visible
+    kvb = kv_bytes(w)
+    tflops = flops / (attn_ms / 1e3) / 1e12
+    log(f"chunked prefill step {ms_per_step * 1e3:.1f} us: write {wr_ms * 1e3:.1f} us, "
+        f"multi-query attention {attn_ms * 1e3:.1f} us = {tflops:.1f} TFLOP/s")
+    return {
+        "metric": METRIC, "value": round(kvb / (ms_per_step / 1e3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.kv_format, "data": "synthetic",
+        "config": {"workload": "chunked_prefill", "batch": B,
+                   "context": cp.context.tolist(), "chunk": cp.chunk.tolist(),
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "page_size": w.page_size,
+                   "step": "paged_write of each chunk + causal multi-query paged attention"},
+        "tokens_per_s": round(cp.total_q / (ms_per_step / 1e3), 1),
+        "attention_TFLOPs": round(tflops, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "attend_multi (causal, several queries per sequence)",
+                     "avg_launch_us": round(attn_ms * 1e3, 2),
+                     "flops_per_launch": flops,
+                     "timing": "library kernel events over a second run of the K steps"},
+        "cpu_baseline": None,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -371,6 +454,9 @@ def main():
     device = torch.device("cuda:0")
     if args.workload == "shared_prefix":
         print(json.dumps(run_shared_prefix(args, device)), flush=True)
+        return
+    if args.workload == "chunked_prefill":
+        print(json.dumps(run_chunked_prefill(args, device)), flush=True)
         return
     w = W.by_name(args.workload)
     log(f"workload {w.name}: B={w.batch} lens={int(w.lens.min())}..{int(w.lens.max())} "

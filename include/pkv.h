@@ -68,6 +68,11 @@ extern "C" {
 #define PKV_DEV_WRITE_TABLE 2u  /* a written row's position is negative or past the table row */
 #define PKV_DEV_READ_PAGE 4u    /* attend/gather met a table entry outside [0, n_pages) */
 #define PKV_DEV_LEN 8u          /* attend met lens[b] < 0 or > max_len (clamped) */
+#define PKV_DEV_QROWS 16u       /* multi-query attend met cu_q outside [0, total_q] or
+                                   decreasing (that sequence skipped), a chunk longer than
+                                   its sequence (rows before position 0 give zeros) or
+                                   longer than max_q (rows past max_q may be left
+                                   unwritten) */
 
 typedef enum { PKV_FMT_F32 = 0, PKV_FMT_BF16 = 1, PKV_FMT_INT8 = 2 } pkv_format;
 typedef enum { PKV_DT_F32 = 0, PKV_DT_BF16 = 1 } pkv_dtype;
@@ -198,6 +203,33 @@ int pkv_decode_step(pkv_cache* cache, int32_t layer, const int32_t* table, int32
                     uint64_t workspace_bytes, int32_t split_tokens, uint32_t flags,
                     void* stream);
 
+/* Several queries per sequence (a chunk of new tokens, as in chunked
+ * prefill).  Sequence b's T_b = cu_q[b+1] - cu_q[b] query rows stand for its
+ * last T_b tokens, which a page write has already stored (AstrAI cache.py
+ * PagedCache.write with seq_len > 1): row cu_q[b] + i sits at position
+ * lens[b] - T_b + i and attends to the tokens t <= that position (the
+ * valid-slot rule of metrale_storage high_speed_swap/impl_more.rs: a query
+ * at q_pos sees the first q_pos % page_size + 1 slots of its own block; with
+ * T_b = 1 this is pkv_paged_attend).  Query head h uses KV head
+ * h / (n_q_heads / n_kv_heads).  A row whose position is below 0 gives zeros.
+ *   q          device [total_q][n_q_heads][head_dim] bf16 (q_dtype must be
+ *              PKV_DT_BF16); out the same shape, bf16 rounded to nearest even.
+ *   table      device int32 [batch][table_stride].
+ *   lens       device int32 [batch], stored tokens (chunk included); max_len a
+ *              host upper bound on them, at most table_stride * page_size.
+ *   cu_q       device int32 [batch + 1], non-decreasing, cu_q[0] = 0,
+ *              cu_q[batch] = total_q; max_q a host upper bound on T_b.
+ * Matrix-core kernel only: BF16 or INT8 pages, head_dim 64 or 128, page_size
+ * 16 or a multiple of 32, n_q_heads / n_kv_heads at most 16; other shapes
+ * return EFORMAT.  No workspace: every row is computed whole by one wave.
+ * Device-side, malformed cu_q / chunk lengths set PKV_DEV_QROWS (see there);
+ * lens are clamped as in pkv_paged_attend.  Nothing is synchronised. */
+int pkv_paged_attend_multi(pkv_cache* cache, int32_t layer, const void* q, int32_t q_dtype,
+                           int32_t n_q_heads, const int32_t* table, int32_t table_stride,
+                           const int32_t* lens, const int32_t* cu_q, int32_t batch,
+                           int32_t total_q, int32_t max_q, int32_t max_len, float scale,
+                           void* out, void* stream);
+
 /* gather(table, len): rows 0 .. len-1 of one sequence copied out in token
  * order (AstrAI cache.py PagedCache.gather truncated by CacheView;
  * libmir-metal PagedStore::context).  k_out, v_out: device
@@ -231,7 +263,8 @@ const char* pkv_last_error(void);
 #define PKV_T_ATTEND_SPLIT 1  /* the split-K partial pass */
 #define PKV_T_ATTEND_COMBINE 2
 #define PKV_T_GATHER 3
-#define PKV_T_COUNT 4
+#define PKV_T_ATTEND_MULTI 4
+#define PKV_T_COUNT 5
 int pkv_timing_enable(pkv_cache* cache, int32_t on);
 int pkv_timing_read(pkv_cache* cache, double* ms, int32_t* counts);
 

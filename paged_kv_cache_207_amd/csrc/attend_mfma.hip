@@ -10,111 +10,26 @@
 // table[t / page_size], slot t % page_size; query heads outnumber KV heads
 // as in metrale_storage high_speed_swap/impl_more.rs attend_layer).
 //
-// How, on gfx950.  One wave owns one (b, g, s).  The query group is the N
-// dimension of v_mfma_f32_16x16x32_bf16 (16 columns; columns >= G hold zeros),
-// so every K/V element is loaded from HBM once, straight into registers, and
-// used for all the group's heads without an LDS round trip.  The scores are
-// computed transposed, S^T = K Q^T, whose accumulator layout (lane = head +
-// 16 * token quad) is exactly the B-operand layout the P.V product needs, so
-// the softmax weights never move between lanes.  P.V is computed as
-// O^T = V^T P^T, with V read from the dim-major page slab.  Row r of score
-// tile t (t = 0, 1) holds token 8 * (r / 4) + 4 * t + r % 4 of the 32-token
-// step, so the accumulator lanes of k group j hold tokens 8j .. 8j+7 of the
-// step in order: the P.V k-slots are the tokens in their natural order and
-// each lane's V operand is 8 consecutive slots of one dim, one 16-byte load
-// (8 bytes for int8).  The loads of step i+1 are issued before step i is
-// computed.  int8 pages are converted to bf16 exactly (|code| <= 127); the
-// per-token K scale multiplies the score and the V scale the weight.
-//
-// Memory instructions, not only bytes, set the pace: every K load covers 64
-// contiguous bytes of each row it touches (int8 lanes load 16 codes at once,
-// see kdim_of), and a step's 64 per-token scales arrive in one 4-byte load
-// per lane and are handed to the lanes that need them by lane shuffles.
-// Measured on the int8 workloads, each of the two cut the split pass by
-// about a fifth; a third register set (two steps in flight) was slower.
+// How, on gfx950 (the step machinery is in mfma_step.h).  One wave owns one
+// (b, g, s); the query group is the N dimension of the matrix-core tiles
+// (16 columns; columns >= G hold zeros).  The loads of step i+1 are issued
+// before step i is computed.  int8 pages are converted to bf16 exactly
+// (|code| <= 127); the per-token K scale multiplies the score and the V
+// scale the weight.
 //
 // Work distribution: a persistent grid (as many single-wave workgroups as
 // the chip holds at once) walks a work list of (split, KV head) items built
 // in LDS from the lengths, full splits first.  A sequence that fits in one
 // split gets its output written directly.  For longer sequences either the
-// combine kernel merges the partials afterwards, or (fuse_combine, chosen
-// when sequences have few splits) the workgroup that finishes a (sequence,
-// KV head)'s last split merges them, so one launch does the whole attention.
+// combine kernel merges the partials afterwards (the default), or, when the
+// caller asks for it (fuse_combine), the workgroup that finishes a
+// (sequence, KV head)'s last split merges them in the same launch.
 #include <algorithm>
-#include <type_traits>
 
-#include "pkv_device.h"
-#include "pkv_internal.h"
+#include "mfma_step.h"
 
 namespace pkv {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-template <int FMT, int D>
-struct Step {
-  static constexpr int NC = D / 32;  // 32-wide k chunks of the Q.K product
-  static constexpr int ND = D / 16;  // 16-row dim tiles of the P.V product
-  // K: one 16-byte load per (tile, load) = 8 bf16 values (one k chunk) or
-  // 16 int8 codes (two k chunks); V: 8 tokens per dim tile
-  static constexpr int NK = FMT == PKV_FMT_BF16 ? NC : D / 64;
-  using KT = uint4;
-  using VT = typename std::conditional<FMT == PKV_FMT_BF16, uint4, uint2>::type;
-  // the same bytes as raw 32-bit vectors, for non-temporal loads
-  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  using NKT = u32x4;
-  using NVT = typename std::conditional<sizeof(VT) == 16, u32x4, u32x2>::type;
-  KT k[2][NK];
-  VT v[ND];
-  // int8 only: lane x < 32 holds the K scale of token x of the step, lane
-  // 32 + x its V scale; compute_step fetches the ones it needs from there
-  float sc;
-  bool live_a, live_b;  // the step's first / second 16 tokens sit on a valid page
-};
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
-
-// Page reads are streamed once per call: non-temporal loads keep them from
-// displacing other data in the caches (measured: +45% bandwidth on the
-// 32k-token bf16 workload over plain loads).
-template <typename T, typename R>
-__device__ __forceinline__ T stream_load(const char* p) {
-  return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const R*>(p)));
-}
-
-// 4 int8 codes -> 4 bf16 (exact: an integer of at most 7 bits plus sign)
-__device__ __forceinline__ uint2 codes_to_bf16(uint32_t w) {
-  float f0 = (float)(int8_t)(w & 0xffu), f1 = (float)(int8_t)((w >> 8) & 0xffu);
-  float f2 = (float)(int8_t)((w >> 16) & 0xffu), f3 = (float)(int8_t)(w >> 24);
-  uint2 r;
-  r.x = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
-  r.y = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
-  return r;
-}
-
-// The head dims that k slots 8j .. 8j+7 of Q.K chunk c stand for (the
-// contraction may take the dims in any order, as long as K and Q agree).
-// bf16: dims 32c + 8j .. +7, one 16-byte load of a K row per chunk.  int8:
-// lane j's 16 consecutive codes 64 (c / 2) + 16j .. +15 come in one 16-byte
-// load and serve chunks c and c + 1 (codes 0-7, then 8-15), so a K load
-// instruction covers 64 contiguous bytes of each row it reads, as in bf16.
-template <int FMT>
-__device__ __forceinline__ int kdim_of(int c, int j) {
-  return FMT == PKV_FMT_BF16 ? 32 * c + 8 * j : 64 * (c >> 1) + 16 * j + 8 * (c & 1);
-}
-
-// Write 4 consecutive outputs (bf16 rounded to nearest even, or f32).
-__device__ __forceinline__ void store_out4(const AttendArgs& a, int64_t oi, f32x4 r) {
-  if (a.q_bf16) {
-    const uint2 w = {f32_to_bf16_bits(r[0]) | (f32_to_bf16_bits(r[1]) << 16),
-                     f32_to_bf16_bits(r[2]) | (f32_to_bf16_bits(r[3]) << 16)};
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oi) = w;
-  } else {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + oi) = r;
-  }
-}
 
 // Partials are exchanged between workgroups, which may sit on different XCDs
 // with separate L2 caches.  Writers store them as agent-scope relaxed atomics
@@ -163,7 +78,7 @@ __device__ __forceinline__ void combine_group(const AttendArgs& a, int b, int g,
         }
       }
     }
-    store_out4(a, hrow * D + 4 * d4, acc * (1.f / L));
+    store_out4(a.out, a.q_bf16, hrow * D + 4 * d4, acc * (1.f / L));
   }
 }
 
@@ -171,10 +86,9 @@ template <int FMT, int D, int BS>
 __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
   using S = Step<FMT, D>;
   using KT = typename S::KT;
-  using VT = typename S::VT;
   constexpr int NC = S::NC, ND = S::ND;
   constexpr int ESZ = FMT == PKV_FMT_BF16 ? 2 : 1;
-  constexpr int KPL = NC / S::NK;  // k chunks per K load
+  constexpr int KPL = S::KPL;
   auto kdim = [](int c, int jj) { return kdim_of<FMT>(c, jj); };
   const int lane = threadIdx.x;
   const int n = lane & 15;  // head column (B/C operands), row (A operands)
@@ -240,7 +154,7 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
   for (int b = blockIdx.x; b < B; b += gridDim.x) {
     if (lens[b] != 0) continue;
     for (int i = lane; i < a.n_q_heads * D / 4; i += 64)
-      store_out4(a, (int64_t)b * a.n_q_heads * D + 4 * i, f32x4{0.f, 0.f, 0.f, 0.f});
+      store_out4(a.out, a.q_bf16, (int64_t)b * a.n_q_heads * D + 4 * i, f32x4{0.f, 0.f, 0.f, 0.f});
   }
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -267,20 +181,13 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
 
   // ---- query group as the B operand of S^T = K Q^T (zeros past the group) ----
   bf16x8 qf[NC];
-  {
-    const uint16_t* q = static_cast<const uint16_t*>(a.q) +
-                        ((int64_t)b * a.n_q_heads + (int64_t)g * G + n) * D;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      uint4 x = {0, 0, 0, 0};
-      if (n < G) x = *reinterpret_cast<const uint4*>(q + kdim(c, j));
-      qf[c] = as_bf16x8(x);
-    }
-  }
+  load_q<FMT, D>(qf, static_cast<const uint16_t*>(a.q) +
+                         ((int64_t)b * a.n_q_heads + (int64_t)g * G + n) * D,
+                 n < G, j);
 
   const int64_t slab_bytes = (int64_t)bs * D * ESZ;
-  const char* kp = static_cast<const char*>(a.k_pages);
-  const char* vp = static_cast<const char*>(a.v_pages);
+  const PageSrc src{static_cast<const char*>(a.k_pages), static_cast<const char*>(a.v_pages),
+                    a.k_scales, a.v_scales, a.layer_page0, slab_bytes, a.n_kv_heads, bs};
   const int32_t* trow = a.table + (int64_t)b * a.table_stride;
   const int pg_last = (t_end - 1) / bs;
 
@@ -311,78 +218,22 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
       }
     }
 
-    // Loads are unconditional: a 16-token half with no page (past the length
-    // or a bad entry) reads page 0 of the array instead and is masked
-    // afterwards, so the compiler can keep the next step's loads in flight.
     // With 16-token pages a step spans pages A (tokens 0-15) and B (16-31);
     // with larger pages both halves sit on page A.
-    auto load_step = [&](int ts, S& r) {
+    auto load_step_at = [&](int ts, S& r) {
       const int lp = ts / bs;
       const int page_a = ts < w_end ? __builtin_amdgcn_readlane(vpage, lp - pg0) : -1;
       int page_b = page_a;
       if (BS == 16) page_b = ts + 16 < w_end ? __builtin_amdgcn_readlane(vpage, lp + 1 - pg0) : -1;
-      r.live_a = page_a >= 0;
-      r.live_b = page_b >= 0;
-      const int slot0 = ts - lp * bs;  // 0 for 16-token pages
-      const int64_t slab_a = (a.layer_page0 + (page_a >= 0 ? page_a : 0)) * a.n_kv_heads + g;
-      const int64_t slab_b = (a.layer_page0 + (page_b >= 0 ? page_b : 0)) * a.n_kv_heads + g;
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        // this lane's K row: token 8 * (n / 4) + 4 * tau + n % 4 of the step
-        const int tok = 8 * (n >> 2) + 4 * tau + (n & 3);
-        const bool on_b = BS == 16 && tok >= 16;
-        const char* kb = kp + (on_b ? slab_b : slab_a) * slab_bytes;
-        const int row = BS == 16 ? (tok & 15) : slot0 + tok;
-#pragma unroll
-        for (int c = 0; c < S::NK; ++c)
-          r.k[tau][c] = stream_load<KT, typename S::NKT>(kb + (row * D + kdim(KPL * c, j)) * ESZ);
-      }
-      // V operand: tokens 8j .. 8j+7 of dim 16 * dt + n
-      const bool v_on_b = BS == 16 && j >= 2;
-      const char* vb = vp + (v_on_b ? slab_b : slab_a) * slab_bytes;
-      const int col = BS == 16 ? 8 * (j & 1) : slot0 + 8 * j;
-      const int voff = (n * bs + col) * ESZ;
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt)
-        r.v[dt] = stream_load<VT, typename S::NVT>(vb + voff + 16 * dt * bs * ESZ);
-      if (FMT == PKV_FMT_INT8) {
-        const int x = lane & 31;
-        const bool s_on_b = BS == 16 && x >= 16;
-        const int slot = BS == 16 ? (x & 15) : slot0 + x;
-        const float* sb = lane < 32 ? a.k_scales : a.v_scales;
-        r.sc = __builtin_nontemporal_load(sb + (s_on_b ? slab_b : slab_a) * bs + slot);
-      }
+      load_step<FMT, D, BS>(r, src, page_a, page_b, ts - lp * bs, g, lane);
     };
 
     auto compute_step = [&](int ts, S& r) {
-      // S^T tiles: accumulator row 4j + i of tile tau = token 8j + 4 * tau + i
       f32x4 sacc[2];
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        sacc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          bf16x8 ka;
-          if constexpr (FMT == PKV_FMT_BF16) {
-            ka = as_bf16x8(r.k[tau][c]);
-          } else {
-            // chunk c: codes 8 (c % 2) .. +7 of the lane's 16-code load c / 2
-            const uint4& w = r.k[tau][c >> 1];
-            const uint2 lo = codes_to_bf16(c & 1 ? w.z : w.x), hi = codes_to_bf16(c & 1 ? w.w : w.y);
-            ka = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
-          }
-          sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[c], sacc[tau], 0, 0, 0);
-        }
-      }
+      step_scores<FMT, D>(r, qf, sacc);
       const bool lane_live = BS == 16 && j >= 2 ? r.live_b : r.live_a;
       float ksc[8], vsc[8];  // int8: scales of tokens 8j .. 8j+7
-      if constexpr (FMT == PKV_FMT_INT8) {
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          ksc[x] = __shfl(r.sc, 8 * j + x, 64);
-          vsc[x] = __shfl(r.sc, 32 + 8 * j + x, 64);
-        }
-      }
+      if constexpr (FMT == PKV_FMT_INT8) step_scales<FMT, D>(r, j, ksc, vsc);
       float sv[8];
       bool ok[8];  // token 8j + x of the step is real
       float mx = -INFINITY;
@@ -411,29 +262,9 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
       }
       l = l * alpha + psum;
       m = m_new;
-      // V^T A operands.  Where a slot of the step is dead (past the length or
-      // on a missing page) zero its bf16 value: it may hold NaN, and 0 * NaN
-      // would reach the sum.  int8 codes are finite and carry weight 0 there.
-      const bool mask_v = FMT == PKV_FMT_BF16 && (ts + 32 > w_end || !r.live_a || !r.live_b);
       uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
-      if (mask_v) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          keep[w] = (ok[2 * w] ? 0x0000ffffu : 0u) | (ok[2 * w + 1] ? 0xffff0000u : 0u);
-      }
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt) {
-        o[dt] *= alpha;
-        uint4 va;
-        if constexpr (FMT == PKV_FMT_BF16) {
-          va = uint4{r.v[dt].x & keep[0], r.v[dt].y & keep[1], r.v[dt].z & keep[2],
-                     r.v[dt].w & keep[3]};
-        } else {
-          const uint2 lo = codes_to_bf16(r.v[dt].x), hi = codes_to_bf16(r.v[dt].y);
-          va = uint4{lo.x, lo.y, hi.x, hi.y};
-        }
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pb, o[dt], 0, 0, 0);
-      }
+      if (FMT == PKV_FMT_BF16 && (ts + 32 > w_end || !r.live_a || !r.live_b)) v_keep_masks(ok, keep);
+      step_pv<FMT, D>(r, pb, keep, alpha, o);
     };
 
     // A fused decode step: the item that owns the sequence's last split loads
@@ -574,16 +405,16 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
     const int n_steps = (w_end - w0 + 31) / 32;
     auto T = [&](int i) { return w0 + 32 * i; };
     S r0, r1;
-    load_step(T(0), r0);
+    load_step_at(T(0), r0);
     int st = 0;
     for (; st + 2 < n_steps; st += 2) {
-      load_step(T(st + 1), r1);
+      load_step_at(T(st + 1), r1);
       compute_step(T(st), r0);
-      load_step(T(st + 2), r0);
+      load_step_at(T(st + 2), r0);
       compute_step(T(st + 1), r1);
     }
     if (st + 1 < n_steps) {
-      load_step(T(st + 1), r1);
+      load_step_at(T(st + 1), r1);
       compute_step(T(st), r0);
       substitute_new(T(st + 1), r1);
       compute_step(T(st + 1), r1);
@@ -603,7 +434,7 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
       const float inv = 1.f / l;
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt)
-        store_out4(a, hrow * D + 16 * dt + 4 * j, o[dt] * inv);
+        store_out4(a.out, a.q_bf16, hrow * D + 16 * dt + 4 * j, o[dt] * inv);
     }
   } else if (!a.fuse_combine) {
     // one of several splits: leave the partial for the combine kernel

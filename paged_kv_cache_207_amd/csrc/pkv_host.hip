@@ -417,6 +417,70 @@ int pkv_paged_attend(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype
                      nullptr, 0);
 }
 
+int pkv_paged_attend_multi(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype,
+                           int32_t n_q_heads, const int32_t* table, int32_t table_stride,
+                           const int32_t* lens, const int32_t* cu_q, int32_t batch,
+                           int32_t total_q, int32_t max_q, int32_t max_len, float scale,
+                           void* out, void* stream) {
+  if (!c) return fail(PKV_EINVAL, "cache is null");
+  if (layer < 0 || layer >= c->L.n_layers)
+    return fail(PKV_ERANGE, "layer %d outside [0, %d)", layer, c->L.n_layers);
+  if (q_dtype != PKV_DT_BF16) return fail(PKV_EINVAL, "queries must be bf16 (dtype %d)", q_dtype);
+  if (n_q_heads < 1 || n_q_heads % c->L.n_kv_heads)
+    return fail(PKV_EINVAL, "n_q_heads %d is not a positive multiple of n_kv_heads %d",
+                n_q_heads, c->L.n_kv_heads);
+  if (batch < 0 || total_q < 0 || max_q < 0 || max_len < 0 || table_stride < 1)
+    return fail(PKV_EINVAL, "negative sizes or table_stride < 1");
+  if ((int64_t)max_len > (int64_t)table_stride * c->L.page_size)
+    return fail(PKV_ERANGE, "max_len %d exceeds the table row (%d pages of %d)", max_len,
+                table_stride, c->L.page_size);
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "scale is not finite");
+  const int group = n_q_heads / c->L.n_kv_heads;
+  if (!pkv::mfma_supported(c->L.format, 1, c->L.head_dim, c->L.page_size, group, 1,
+                           c->L.n_kv_heads))
+    return fail(PKV_EFORMAT,
+                "no multi-query kernel for this cache (needs bf16/int8 pages, head_dim 64 or "
+                "128, page_size 16 or a multiple of 32, at most 16 query heads per KV head)");
+  if (batch == 0 || total_q == 0 || max_q == 0) return PKV_OK;
+  if (!q || !out || !table || !lens || !cu_q) return fail(PKV_EINVAL, "null device pointer");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(PKV_EINVAL, "q and out must be 16-byte aligned");
+  pkv::MultiArgs a;
+  a.q = q;
+  a.out = out;
+  a.k_pages = c->k_pages;
+  a.v_pages = c->v_pages;
+  a.k_scales = c->k_scales;
+  a.v_scales = c->v_scales;
+  a.status = c->status;
+  a.table = table;
+  a.lens = lens;
+  a.cu_q = cu_q;
+  a.layer_page0 = (int64_t)layer * c->L.n_pages;
+  a.qk_scale_log2 = scale * pkv::kLog2eHost;
+  a.n_pages = c->L.n_pages;
+  a.page_size = c->L.page_size;
+  a.n_kv_heads = c->L.n_kv_heads;
+  a.head_dim = c->L.head_dim;
+  a.n_q_heads = n_q_heads;
+  a.group = group;
+  a.table_stride = table_stride;
+  a.batch = batch;
+  a.max_len = max_len;
+  a.total_q = total_q;
+  a.max_q = max_q;
+  a.n_pos = 16 / group;
+  a.n_qgroups = (max_q + a.n_pos - 1) / a.n_pos;
+  if (pkv::multi_grid(batch, c->L.n_kv_heads, a.n_qgroups) > INT32_MAX)
+    return fail(PKV_EINVAL, "too many work items (batch %d, max_q %d)", batch, max_q);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  Timer tm(c, PKV_T_ATTEND_MULTI, s);
+  const hipError_t e = pkv::launch_attend_multi(a, c->L.format, tm.l);
+  tm.stop(e);
+  if (e != hipSuccess) return fail(PKV_EHIP, "multi-query launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
 int pkv_decode_step(pkv_cache* c, int32_t layer, const int32_t* table, int32_t table_stride,
                     const int32_t* lens, int32_t batch, int32_t max_len, const void* k_new,
                     const void* v_new, int32_t in_dtype, const void* q, int32_t q_dtype,

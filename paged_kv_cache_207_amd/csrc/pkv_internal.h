@@ -68,6 +68,27 @@ struct AttendArgs {
   int32_t single_done;   // combine kernel: single-split sequences are already written
 };
 
+// Arguments of the several-queries-per-sequence kernel (one launch = one
+// pkv_paged_attend_multi call).
+struct MultiArgs {
+  const void* q;  // [total_q][n_q_heads][head_dim] bf16
+  void* out;      // same shape, bf16
+  const void* k_pages;
+  const void* v_pages;
+  const float* k_scales;
+  const float* v_scales;
+  int32_t* status;
+  const int32_t* table;
+  const int32_t* lens;
+  const int32_t* cu_q;  // [batch + 1] query rows of each sequence
+  int64_t layer_page0;
+  float qk_scale_log2;  // softmax scale * log2(e)
+  int32_t n_pages, page_size, n_kv_heads, head_dim, n_q_heads, group;
+  int32_t table_stride, batch, max_len, total_q, max_q;
+  int32_t n_pos;      // query positions per work item (16 / group)
+  int32_t n_qgroups;  // work items per (sequence, KV head): ceil(max_q / n_pos)
+};
+
 struct GatherArgs {
   const void* k_pages;
   const void* v_pages;
@@ -116,6 +137,9 @@ constexpr int kMaxMfmaKvHeads = 64;  // split counters: a fixed region of the wo
 bool mfma_supported(int fmt, int q_bf16, int head_dim, int page_size, int group, int batch,
                     int n_kv_heads);
 hipError_t launch_reduce(const AttendArgs& a, const Launch& l);
+// Returns hipErrorNotSupported when the shape has no matrix-core variant.
+hipError_t launch_attend_multi(const MultiArgs& a, int fmt, const Launch& l);
+int64_t multi_grid(int batch, int n_kv_heads, int n_qgroups);
 hipError_t launch_probe(const void* src, void* dst, float* sink, uint64_t bytes, int mode,
                         hipStream_t s);
 int probe_blocks(uint64_t bytes);

@@ -18,9 +18,9 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 OK, EINVAL, ERANGE, EFORMAT, ENOMEM, EHIP, EDOUBLEFREE = 0, -1, -2, -3, -4, -5, -6
 FMT_F32, FMT_BF16, FMT_INT8 = 0, 1, 2
 DT_F32, DT_BF16 = 0, 1
-DEV_WRITE_PAGE, DEV_WRITE_TABLE, DEV_READ_PAGE, DEV_LEN = 1, 2, 4, 8
+DEV_WRITE_PAGE, DEV_WRITE_TABLE, DEV_READ_PAGE, DEV_LEN, DEV_QROWS = 1, 2, 4, 8, 16
 ATTEND_VALU, ATTEND_COMBINE_KERNEL, ATTEND_COMBINE_FUSED = 1, 2, 4
-T_WRITE, T_ATTEND_SPLIT, T_ATTEND_COMBINE, T_GATHER, T_COUNT = 0, 1, 2, 3, 4
+T_WRITE, T_ATTEND_SPLIT, T_ATTEND_COMBINE, T_GATHER, T_ATTEND_MULTI, T_COUNT = 0, 1, 2, 3, 4, 5
 
 FORMAT_CODE = {"f32": FMT_F32, "bf16": FMT_BF16, "int8": FMT_INT8}
 DTYPE_CODE = {torch.float32: DT_F32, torch.bfloat16: DT_BF16}
@@ -41,6 +41,8 @@ SYMBOLS = [
     ("pkv_decode_step", C.c_int,
      [_P, _I32, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _I32, _I32, _F, _P, _P, _U64, _I32,
       _U32, _P]),
+    ("pkv_paged_attend_multi", C.c_int,
+     [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _F, _P, _P]),
     ("pkv_gather", C.c_int, [_P, _I32, _P, _I32, _P, _P, _P, _P, _P]),
     ("pkv_table_apply", C.c_int, [_P, _I32, _I32, _P, _I32, _P]),
     ("pkv_last_error", C.c_char_p, []),
@@ -173,6 +175,10 @@ class PagedKVCache:
         """The device status word (synchronises: for tests and checks)."""
         return int(self.status_word.item())
 
+    def clear_status(self) -> None:
+        """Zero the device status word (on the current stream)."""
+        self.status_word.zero_()
+
     # -- paged_write -----------------------------------------------------------
     def write(self, table, start_pos, cu_new, k, v, layer: int = 0):
         total = int(k.shape[0])
@@ -243,6 +249,26 @@ class PagedKVCache:
             split_tokens, flags, _stream(self.device)))
         return out
 
+    # -- several queries per sequence (a chunk of new tokens) -------------------
+    def attend_multi(self, q, table, lens, cu_q, max_q: int, max_len: int, scale: float,
+                     out=None, layer: int = 0) -> torch.Tensor:
+        """q [total_q, Hq, D] bf16; rows cu_q[b] .. cu_q[b+1] are sequence b's
+        last tokens, each attending causally to its sequence."""
+        total_q, Hq, D = q.shape
+        if q.dtype != torch.bfloat16:
+            raise ValueError("q must be bfloat16")
+        if out is None:
+            out = torch.empty_like(q)
+        B = lens.shape[0]
+        if cu_q.shape[0] != B + 1:
+            raise ValueError("cu_q must hold batch + 1 offsets")
+        _check(lib().pkv_paged_attend_multi(
+            self._h, layer, _dev(q, name="q"), DTYPE_CODE[q.dtype], Hq,
+            _dev(table, torch.int32, "table"), table.shape[1], _dev(lens, torch.int32, "lens"),
+            _dev(cu_q, torch.int32, "cu_q"), B, total_q, max_q, max_len, float(scale),
+            _dev(out, q.dtype, "out"), _stream(self.device)))
+        return out
+
     # -- kernel timing -----------------------------------------------------------
     def timing(self, on: bool = True):
         _check(lib().pkv_timing_enable(self._h, int(on)))
@@ -253,7 +279,7 @@ class PagedKVCache:
         ms = (C.c_double * T_COUNT)()
         n = (C.c_int32 * T_COUNT)()
         _check(lib().pkv_timing_read(self._h, ms, n))
-        names = ["write", "attend_split", "attend_combine", "gather"]
+        names = ["write", "attend_split", "attend_combine", "gather", "attend_multi"]
         return {k: (ms[i], n[i]) for i, k in enumerate(names)}
 
     # -- gather ------------------------------------------------------------------

@@ -287,6 +287,31 @@ def test_attend_validation():
     L.pkv_cache_destroy(h)
 
 
+def test_attend_multi_validation():
+    L, h = _cache()  # bf16 pages, Hkv 2, D 64, bs 16, 16 pages
+    P = C.c_void_p(FAKE)
+
+    def m(q_dt=pkv.DT_BF16, hq=4, stride=4, batch=2, total_q=9, max_q=5, max_len=50,
+          scale=0.125, q=P, layer=0):
+        return L.pkv_paged_attend_multi(h, layer, q, q_dt, hq, P, stride, P, P, batch, total_q,
+                                        max_q, max_len, scale, P, None)
+
+    assert m(q_dt=pkv.DT_F32) == pkv.EINVAL  # queries must be bf16
+    assert m(hq=3) == pkv.EINVAL
+    assert m(hq=34) == pkv.EFORMAT  # 17 query heads per KV head
+    assert m(layer=1) == pkv.ERANGE
+    assert m(max_len=65) == pkv.ERANGE
+    assert m(scale=float("inf")) == pkv.EINVAL
+    assert m(total_q=-1) == pkv.EINVAL
+    assert m(q=None) == pkv.EINVAL
+    assert m(q=C.c_void_p(FAKE + 2)) == pkv.EINVAL
+    assert m(batch=0) == pkv.OK and m(total_q=0) == pkv.OK and m(max_q=0) == pkv.OK
+    L.pkv_cache_destroy(h)
+    L, h = _cache(fmt=pkv.FMT_F32)
+    assert m() == pkv.EFORMAT  # no multi-query kernel for f32 pages
+    L.pkv_cache_destroy(h)
+
+
 def test_gather_and_table_validation():
     L, h = _cache(fmt=pkv.FMT_INT8)
     P = C.c_void_p(FAKE)

@@ -240,6 +240,15 @@ int pkv_paged_attend_multi(pkv_cache* cache, int32_t layer, const void* q, int32
 int pkv_gather(pkv_cache* cache, int32_t layer, const int32_t* table_row, int32_t len,
                void* k_out, void* v_out, float* k_scale_out, float* v_scale_out, void* stream);
 
+/* Copy n pages: for every (src, dst) pair of the device int32 [n][2] list
+ * and every layer, page src's K and V (all KV heads) and, for int8 pages,
+ * its scales are copied to page dst.  This is the device half of
+ * copy-on-write (pkv_seqs_take_copies hands out the pairs); run it before any
+ * write into the dst pages.  The copies of one call run concurrently: no dst
+ * may also be a src of the same call.  Pairs with an id outside the pool are
+ * skipped and set PKV_DEV_WRITE_PAGE. */
+int pkv_copy_pages(pkv_cache* cache, const int32_t* pairs, int32_t n, void* stream);
+
 /* Apply n block-table updates: table[upd[3i] * table_stride + upd[3i+1]] =
  * upd[3i+2], with upd a device int32 [n][3] list (sequence, logical block,
  * physical page), as tiny-llm paged_kv.py's begin_step mirrors newly
@@ -264,7 +273,8 @@ const char* pkv_last_error(void);
 #define PKV_T_ATTEND_COMBINE 2
 #define PKV_T_GATHER 3
 #define PKV_T_ATTEND_MULTI 4
-#define PKV_T_COUNT 5
+#define PKV_T_COPY_PAGES 5
+#define PKV_T_COUNT 6
 int pkv_timing_enable(pkv_cache* cache, int32_t on);
 int pkv_timing_read(pkv_cache* cache, double* ms, int32_t* counts);
 
@@ -317,6 +327,28 @@ int pkv_seqs_append_all(pkv_seqs* seqs, const int32_t* n);
 /* Sequence dst (which must be empty) shares the first n_pages pages of src:
  * each gets one more reference.  Its length becomes n_pages * page_size. */
 int pkv_seqs_share(pkv_seqs* seqs, int32_t dst, int32_t src, int32_t n_pages);
+/* Sequence dst (which must be empty) becomes a copy of src that shares all
+ * of its pages, a partly filled last page included, with one more reference
+ * each, and takes its length (libmir-metal PagedStore::snapshot).
+ * Copy-on-write: whenever an append (pkv_seqs_append, pkv_seqs_append_all)
+ * would write into a sequence's last page while that page is partly filled
+ * and held by another sequence as well, the sequence gets a fresh page in its
+ * place, drops its reference to the shared one and queues a (shared, fresh)
+ * page copy for pkv_copy_pages. */
+int pkv_seqs_fork(pkv_seqs* seqs, int32_t dst, int32_t src);
+/* Make room for appending n[b] tokens to every sequence (host int32
+ * [batch]): while the pages those appends need (copies included) exceed the
+ * free pages, the sequence admitted last (by its first append, share or fork)
+ * among those holding tokens is preempted: its pages are released and its
+ * length becomes 0, for the caller to requeue (tiny-llm paged_kv.py
+ * reserve_step, which frees the newest sequences first).  Writes the
+ * preempted sequences, newest first, to host victims[cap] (cap >= batch) and
+ * returns their number, or a negative status (ERANGE if an append would
+ * overflow its row). */
+int32_t pkv_seqs_reserve(pkv_seqs* seqs, const int32_t* n, int32_t* victims, int32_t cap);
+/* Move up to cap queued (src, dst) page copies into host pairs[cap][2];
+ * returns the number moved (the rest stay queued), or a negative status. */
+int32_t pkv_seqs_take_copies(pkv_seqs* seqs, int32_t* pairs, int32_t cap);
 int pkv_seqs_release(pkv_seqs* seqs, int32_t b);
 const int32_t* pkv_seqs_table(const pkv_seqs* seqs); /* host [batch][table_stride] */
 const int32_t* pkv_seqs_lens(const pkv_seqs* seqs);  /* host [batch] */

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <map>
 #include <new>
 #include <set>
 #include <vector>
@@ -548,6 +549,31 @@ int pkv_table_apply(int32_t* table, int32_t table_stride, int32_t batch, const i
   return PKV_OK;
 }
 
+int pkv_copy_pages(pkv_cache* c, const int32_t* pairs, int32_t n, void* stream) {
+  if (!c || n < 0) return fail(PKV_EINVAL, "bad arguments");
+  if (n == 0) return PKV_OK;
+  if (!pairs) return fail(PKV_EINVAL, "null device pointer");
+  pkv::CopyArgs a;
+  a.k_pages = c->k_pages;
+  a.v_pages = c->v_pages;
+  a.k_scales = c->k_scales;
+  a.v_scales = c->v_scales;
+  a.status = c->status;
+  a.pairs = pairs;
+  a.page_bytes = (int64_t)c->L.n_kv_heads * c->L.page_size * c->L.head_dim *
+                 pkv::format_bytes(c->L.format);
+  a.scale_bytes = (int64_t)c->L.n_kv_heads * c->L.page_size * (int64_t)sizeof(float);
+  a.n_pairs = n;
+  a.n_layers = c->L.n_layers;
+  a.n_pages = c->L.n_pages;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  Timer tm(c, PKV_T_COPY_PAGES, s);
+  const hipError_t e = pkv::launch_copy_pages(a, tm.l);
+  tm.stop(e);
+  if (e != hipSuccess) return fail(PKV_EHIP, "page copy launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------- pool ----
@@ -623,15 +649,78 @@ struct pkv_seqs {
   pkv_pool* pool;
   int32_t batch, stride, page_size;
   std::vector<int32_t> table, lens, npages;
+  std::vector<int64_t> admit_no;  // admission order of each sequence (0 = empty)
+  int64_t admits = 0;
   std::vector<int32_t> updates;  // queued (b, j, page) triples, oldest first
   size_t upd_head = 0;
+  std::vector<int32_t> copies;  // queued (src, dst) page copies, oldest first
+  size_t copy_head = 0;
   void set(int32_t b, int32_t j, int32_t page) {
     table[(size_t)b * stride + j] = page;
     updates.push_back(b);
     updates.push_back(j);
     updates.push_back(page);
   }
+  int32_t last_page(int32_t b) const { return table[(size_t)b * stride + npages[b] - 1]; }
+  // Whether growing b by n tokens writes into its last page while another
+  // sequence still holds it (copy-on-write), given that page's reference count.
+  bool needs_copy(int32_t b, int32_t n, int32_t refs) const {
+    return n > 0 && lens[b] % page_size != 0 && refs > 1;
+  }
+  int32_t new_pages(int32_t b, int32_t n) const {
+    const int64_t need = ((int64_t)lens[b] + n + page_size - 1) / page_size;
+    return (int32_t)std::max<int64_t>(need - npages[b], 0);
+  }
+  // Grow b by n tokens from ids (copy first if `copy`): the shared last page
+  // is replaced by a fresh one whose contents the device copies over.
+  void grow(int32_t b, int32_t n, bool copy, const int32_t* ids) {
+    size_t k = 0;
+    if (copy) {
+      const int32_t old = last_page(b), fresh = ids[k++];
+      copies.push_back(old);
+      copies.push_back(fresh);
+      set(b, npages[b] - 1, fresh);
+      pkv_pool_release(pool, old);  // still held by the sharers
+    }
+    const int32_t extra = new_pages(b, n);
+    for (int32_t e = 0; e < extra; ++e) set(b, npages[b] + e, ids[k++]);
+    npages[b] += extra;
+    lens[b] += n;
+    if (lens[b] > 0 && admit_no[b] == 0) admit_no[b] = ++admits;
+  }
 };
+
+namespace {
+
+// Pages the appends n[b] need, in sequence order, with the copy-on-write
+// decisions they imply (a copy lowers the shared page's count for the
+// sequences after it).  ERANGE if a row would overflow.
+int plan_growth(const pkv_seqs* s, const int32_t* n, std::vector<char>& copy, int64_t& total) {
+  std::map<int32_t, int32_t> refs;  // simulated counts of shared last pages
+  copy.assign(s->batch, 0);
+  total = 0;
+  for (int32_t b = 0; b < s->batch; ++b) {
+    if (n[b] < 0) return fail(PKV_EINVAL, "n[%d] = %d is negative", b, n[b]);
+    const int64_t need = ((int64_t)s->lens[b] + n[b] + s->page_size - 1) / s->page_size;
+    if (need > s->stride)
+      return fail(PKV_ERANGE, "sequence %d would need %lld pages, the row holds %d", b,
+                  (long long)need, s->stride);
+    if (s->npages[b] > 0 && n[b] > 0 && s->lens[b] % s->page_size) {
+      const int32_t last = s->last_page(b);
+      auto it = refs.find(last);
+      if (it == refs.end()) it = refs.emplace(last, pkv_pool_refcount(s->pool, last)).first;
+      if (s->needs_copy(b, n[b], it->second)) {
+        copy[b] = 1;
+        --it->second;
+        ++total;
+      }
+    }
+    total += s->new_pages(b, n[b]);
+  }
+  return PKV_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -648,6 +737,7 @@ int pkv_seqs_create(pkv_pool* pool, int32_t batch, int32_t table_stride, int32_t
   s->table.assign((size_t)batch * table_stride, -1);
   s->lens.assign(batch, 0);
   s->npages.assign(batch, 0);
+  s->admit_no.assign(batch, 0);
   *out = s;
   return PKV_OK;
 }
@@ -661,6 +751,7 @@ int pkv_seqs_release(pkv_seqs* s, int32_t b) {
   }
   s->npages[b] = 0;
   s->lens[b] = 0;
+  s->admit_no[b] = 0;
   return PKV_OK;
 }
 
@@ -672,46 +763,75 @@ void pkv_seqs_destroy(pkv_seqs* s) {
 
 int pkv_seqs_append(pkv_seqs* s, int32_t b, int32_t n) {
   if (!s || b < 0 || b >= s->batch || n < 0) return fail(PKV_EINVAL, "bad arguments");
-  const int64_t new_len = (int64_t)s->lens[b] + n;
-  const int64_t need = (new_len + s->page_size - 1) / s->page_size;
-  if (need > s->stride)
-    return fail(PKV_ERANGE, "sequence %d would need %lld pages, the row holds %d", b,
-                (long long)need, s->stride);
-  const int32_t extra = (int32_t)(need - s->npages[b]);
-  if (extra > 0) {
-    std::vector<int32_t> ids(extra);
-    if (int e = pkv_pool_alloc_n(s->pool, extra, ids.data())) return e;
-    for (int32_t k = 0; k < extra; ++k) s->set(b, s->npages[b] + k, ids[k]);
-    s->npages[b] += extra;
-  }
-  s->lens[b] = (int32_t)new_len;
-  return PKV_OK;
+  std::vector<int32_t> one(s->batch, 0);
+  one[b] = n;
+  return pkv_seqs_append_all(s, one.data());
 }
 
 int pkv_seqs_append_all(pkv_seqs* s, const int32_t* n) {
   if (!s || !n) return fail(PKV_EINVAL, "null argument");
+  std::vector<char> copy;
   int64_t total = 0;
-  for (int32_t b = 0; b < s->batch; ++b) {
-    if (n[b] < 0) return fail(PKV_EINVAL, "n[%d] = %d is negative", b, n[b]);
-    const int64_t need = ((int64_t)s->lens[b] + n[b] + s->page_size - 1) / s->page_size;
-    if (need > s->stride)
-      return fail(PKV_ERANGE, "sequence %d would need %lld pages, the row holds %d", b,
-                  (long long)need, s->stride);
-    total += std::max<int64_t>(need - s->npages[b], 0);
-  }
+  if (int e = plan_growth(s, n, copy, total)) return e;
   if (total > INT32_MAX) return fail(PKV_ENOMEM, "too many pages asked for");
   std::vector<int32_t> ids((size_t)total);
   if (total > 0)
     if (int e = pkv_pool_alloc_n(s->pool, (int32_t)total, ids.data())) return e;
-  size_t next = 0;  // sequence by sequence, lowest pages first: as append(b, n[b]) in order
+  size_t next = 0;  // sequence by sequence, lowest pages first: as appends in sequence order
   for (int32_t b = 0; b < s->batch; ++b) {
-    const int64_t new_len = (int64_t)s->lens[b] + n[b];
-    const int32_t need = (int32_t)((new_len + s->page_size - 1) / s->page_size);
-    for (int32_t j = s->npages[b]; j < need; ++j) s->set(b, j, ids[next++]);
-    s->npages[b] = std::max(s->npages[b], need);
-    s->lens[b] = (int32_t)new_len;
+    const size_t used = (size_t)copy[b] + (size_t)s->new_pages(b, n[b]);
+    s->grow(b, n[b], copy[b] != 0, ids.data() + next);
+    next += used;
   }
   return PKV_OK;
+}
+
+int pkv_seqs_fork(pkv_seqs* s, int32_t dst, int32_t src) {
+  if (!s || dst < 0 || dst >= s->batch || src < 0 || src >= s->batch || dst == src)
+    return fail(PKV_EINVAL, "bad arguments");
+  if (s->npages[dst] != 0 || s->lens[dst] != 0)
+    return fail(PKV_EINVAL, "sequence %d is not empty", dst);
+  for (int32_t j = 0; j < s->npages[src]; ++j) {
+    const int32_t page = s->table[(size_t)src * s->stride + j];
+    if (int e = pkv_pool_retain(s->pool, page)) return e;
+    s->set(dst, j, page);
+  }
+  s->npages[dst] = s->npages[src];
+  s->lens[dst] = s->lens[src];
+  if (s->lens[dst] > 0) s->admit_no[dst] = ++s->admits;
+  return PKV_OK;
+}
+
+int32_t pkv_seqs_reserve(pkv_seqs* s, const int32_t* n, int32_t* victims, int32_t cap) {
+  if (!s || !n || !victims || cap < s->batch) return fail(PKV_EINVAL, "bad arguments");
+  int32_t count = 0;
+  std::vector<int32_t> m(n, n + s->batch);
+  for (;;) {
+    std::vector<char> copy;
+    int64_t total = 0;
+    if (int e = plan_growth(s, m.data(), copy, total)) return e;
+    if (total <= pkv_pool_num_free(s->pool)) return count;
+    int32_t v = -1;
+    for (int32_t b = 0; b < s->batch; ++b)
+      if (s->lens[b] > 0 && (v < 0 || s->admit_no[b] > s->admit_no[v])) v = b;
+    if (v < 0) return count;  // nothing left to preempt
+    if (int e = pkv_seqs_release(s, v)) return e;
+    m[v] = 0;  // requeued by the caller
+    victims[count++] = v;
+  }
+}
+
+int32_t pkv_seqs_take_copies(pkv_seqs* s, int32_t* pairs, int32_t cap) {
+  if (!s || cap < 0 || (cap > 0 && !pairs)) return fail(PKV_EINVAL, "bad arguments");
+  const size_t avail = (s->copies.size() - s->copy_head) / 2;
+  const size_t n = std::min<size_t>(avail, (size_t)cap);
+  std::copy(s->copies.begin() + s->copy_head, s->copies.begin() + s->copy_head + 2 * n, pairs);
+  s->copy_head += 2 * n;
+  if (s->copy_head == s->copies.size()) {
+    s->copies.clear();
+    s->copy_head = 0;
+  }
+  return (int32_t)n;
 }
 
 int pkv_seqs_share(pkv_seqs* s, int32_t dst, int32_t src, int32_t n_pages) {
@@ -727,6 +847,7 @@ int pkv_seqs_share(pkv_seqs* s, int32_t dst, int32_t src, int32_t n_pages) {
   }
   s->npages[dst] = n_pages;
   s->lens[dst] = n_pages * s->page_size;
+  if (s->lens[dst] > 0) s->admit_no[dst] = ++s->admits;
   return PKV_OK;
 }
 

@@ -89,6 +89,19 @@ struct MultiArgs {
   int32_t n_qgroups;  // work items per (sequence, KV head): ceil(max_q / n_pos)
 };
 
+// Arguments of the page-copy kernel (copy-on-write).
+struct CopyArgs {
+  void* k_pages;
+  void* v_pages;
+  float* k_scales;  // null unless int8
+  float* v_scales;
+  int32_t* status;
+  const int32_t* pairs;  // [n_pairs][2] (src, dst) page ids
+  int64_t page_bytes;    // one layer's page of K (or V): n_kv_heads * page_size * head_dim * elem
+  int64_t scale_bytes;   // one layer's page of scales: n_kv_heads * page_size * 4
+  int32_t n_pairs, n_layers, n_pages;
+};
+
 struct GatherArgs {
   const void* k_pages;
   const void* v_pages;
@@ -140,6 +153,7 @@ hipError_t launch_reduce(const AttendArgs& a, const Launch& l);
 // Returns hipErrorNotSupported when the shape has no matrix-core variant.
 hipError_t launch_attend_multi(const MultiArgs& a, int fmt, const Launch& l);
 int64_t multi_grid(int batch, int n_kv_heads, int n_qgroups);
+hipError_t launch_copy_pages(const CopyArgs& a, const Launch& l);
 hipError_t launch_probe(const void* src, void* dst, float* sink, uint64_t bytes, int mode,
                         hipStream_t s);
 int probe_blocks(uint64_t bytes);

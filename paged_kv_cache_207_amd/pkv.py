@@ -20,7 +20,8 @@ FMT_F32, FMT_BF16, FMT_INT8 = 0, 1, 2
 DT_F32, DT_BF16 = 0, 1
 DEV_WRITE_PAGE, DEV_WRITE_TABLE, DEV_READ_PAGE, DEV_LEN, DEV_QROWS = 1, 2, 4, 8, 16
 ATTEND_VALU, ATTEND_COMBINE_KERNEL, ATTEND_COMBINE_FUSED = 1, 2, 4
-T_WRITE, T_ATTEND_SPLIT, T_ATTEND_COMBINE, T_GATHER, T_ATTEND_MULTI, T_COUNT = 0, 1, 2, 3, 4, 5
+T_WRITE, T_ATTEND_SPLIT, T_ATTEND_COMBINE, T_GATHER, T_ATTEND_MULTI, T_COPY_PAGES = 0, 1, 2, 3, 4, 5
+T_COUNT = 6
 
 FORMAT_CODE = {"f32": FMT_F32, "bf16": FMT_BF16, "int8": FMT_INT8}
 DTYPE_CODE = {torch.float32: DT_F32, torch.bfloat16: DT_BF16}
@@ -45,6 +46,7 @@ SYMBOLS = [
      [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _F, _P, _P]),
     ("pkv_gather", C.c_int, [_P, _I32, _P, _I32, _P, _P, _P, _P, _P]),
     ("pkv_table_apply", C.c_int, [_P, _I32, _I32, _P, _I32, _P]),
+    ("pkv_copy_pages", C.c_int, [_P, _P, _I32, _P]),
     ("pkv_last_error", C.c_char_p, []),
     ("pkv_timing_enable", C.c_int, [_P, _I32]),
     ("pkv_timing_read", C.c_int, [_P, C.POINTER(C.c_double), _PI32]),
@@ -62,6 +64,9 @@ SYMBOLS = [
     ("pkv_seqs_destroy", None, [_P]),
     ("pkv_seqs_append", C.c_int, [_P, _I32, _I32]),
     ("pkv_seqs_append_all", C.c_int, [_P, _PI32]),
+    ("pkv_seqs_fork", C.c_int, [_P, _I32, _I32]),
+    ("pkv_seqs_reserve", C.c_int32, [_P, _PI32, _PI32, _I32]),
+    ("pkv_seqs_take_copies", C.c_int32, [_P, _PI32, _I32]),
     ("pkv_seqs_share", C.c_int, [_P, _I32, _I32, _I32]),
     ("pkv_seqs_release", C.c_int, [_P, _I32]),
     ("pkv_seqs_table", _PI32, [_P]),
@@ -269,6 +274,14 @@ class PagedKVCache:
             _dev(out, q.dtype, "out"), _stream(self.device)))
         return out
 
+    # -- copy-on-write page copies ------------------------------------------------
+    def copy_pages(self, pairs: torch.Tensor) -> None:
+        """Copy pages pairs[i, 0] -> pairs[i, 1] (device int32 [n, 2]), every layer."""
+        if pairs.dim() != 2 or pairs.shape[1] != 2:
+            raise ValueError("pairs must be [n, 2]")
+        _check(lib().pkv_copy_pages(self._h, _dev(pairs, torch.int32, "pairs"), pairs.shape[0],
+                                    _stream(self.device)))
+
     # -- kernel timing -----------------------------------------------------------
     def timing(self, on: bool = True):
         _check(lib().pkv_timing_enable(self._h, int(on)))
@@ -279,7 +292,8 @@ class PagedKVCache:
         ms = (C.c_double * T_COUNT)()
         n = (C.c_int32 * T_COUNT)()
         _check(lib().pkv_timing_read(self._h, ms, n))
-        names = ["write", "attend_split", "attend_combine", "gather", "attend_multi"]
+        names = ["write", "attend_split", "attend_combine", "gather", "attend_multi",
+                 "copy_pages"]
         return {k: (ms[i], n[i]) for i, k in enumerate(names)}
 
     # -- gather ------------------------------------------------------------------
@@ -401,6 +415,31 @@ class SeqTables:
 
     def share(self, dst: int, src: int, n_pages: int):
         _check(lib().pkv_seqs_share(self._h, dst, src, n_pages))
+
+    def fork(self, dst: int, src: int):
+        """dst (empty) shares all of src's pages and takes its length; later
+        appends into a shared partly filled page copy it first."""
+        _check(lib().pkv_seqs_fork(self._h, dst, src))
+
+    def reserve(self, n) -> list[int]:
+        """Preempt the newest sequences until appending n[b] tokens to each fits
+        the free pages; returns the preempted sequences, newest first."""
+        vals = [int(x) for x in ([n] * self.batch if isinstance(n, int) else n)]
+        arr = (C.c_int32 * self.batch)(*vals)
+        vic = (C.c_int32 * self.batch)()
+        k = lib().pkv_seqs_reserve(self._h, C.cast(arr, _PI32), C.cast(vic, _PI32), self.batch)
+        if k < 0:
+            _check(k)
+        return [vic[i] for i in range(k)]
+
+    def take_copies(self, out: torch.Tensor | None = None, cap: int = 1 << 16):
+        """Move queued (src, dst) page copies into a host int32 tensor [n, 2]."""
+        if out is None:
+            out = torch.empty((cap, 2), dtype=torch.int32)
+        n = lib().pkv_seqs_take_copies(self._h, C.cast(out.data_ptr(), _PI32), out.shape[0])
+        if n < 0:
+            _check(n)
+        return out[:n]
 
     def release(self, b: int):
         _check(lib().pkv_seqs_release(self._h, b))

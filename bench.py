@@ -350,6 +350,42 @@ def run_shared_prefix(args, device):
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
+def multi_layer_write(cp, device, kc, vc, start, cu_new, n_layers=32, reps=5):
+    """The chunk's rows stored in every layer of a 32-layer store: one
+    pkv_paged_write_layers launch against one pkv_paged_write per layer."""
+    w = cp.base
+    cache = pkv.PagedKVCache(w.n_pages, w.page_size, w.n_kv_heads, w.head_dim, w.kv_format,
+                             n_layers, device=device)
+    table = torch.as_tensor(w.tables).to(device)
+    k = kc.unsqueeze(0).expand(n_layers, *kc.shape).contiguous()
+    v = vc.unsqueeze(0).expand(n_layers, *vc.shape).contiguous()
+
+    def one_launch():
+        cache.write_layers(table, start, cu_new, k, v)
+
+    def per_layer():
+        for layer in range(n_layers):
+            cache.write(table, start, cu_new, k[layer], v[layer], layer=layer)
+
+    out = {"layers": n_layers, "rows_per_layer": int(kc.shape[0])}
+    moved = 2 * k.numel() * k.element_size() * 2  # K and V rows read, pages written
+    for name, fn in (("one_launch", one_launch), ("launch_per_layer", per_layer)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name + "_us"] = round(ms * 1e3, 1)
+        out[name + "_GBps_in_plus_out"] = round(moved / (ms / 1e3) / 1e9, 1)
+    assert cache.status() == 0
+    del cache
+    return out
+
+
 def run_chunked_prefill(args, device):
     """Several queries per sequence: each step writes every sequence's chunk
     of new rows (paged_write at position context[b]) and runs causal
@@ -407,11 +443,14 @@ def run_chunked_prefill(args, device):
     tflops = flops / (attn_ms / 1e3) / 1e12
     log(f"chunked prefill step {ms_per_step * 1e3:.1f} us: write {wr_ms * 1e3:.1f} us, "
         f"multi-query attention {attn_ms * 1e3:.1f} us = {tflops:.1f} TFLOP/s")
+    layers_info = multi_layer_write(cp, device, kc, vc, start, cu_new)
+    log(f"multi-layer write: {layers_info}")
     return {
         "metric": METRIC, "value": round(kvb / (ms_per_step / 1e3) / 1e9, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.kv_format, "data": "synthetic",
+        "multi_layer_write": layers_info,
         "config": {"workload": "chunked_prefill", "batch": B,
                    "context": cp.context.tolist(), "chunk": cp.chunk.tolist(),
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,

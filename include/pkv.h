@@ -131,6 +131,18 @@ int pkv_paged_write(pkv_cache* cache, int32_t layer, const int32_t* table, int32
                     int32_t total_new, const void* k, const void* v, int32_t in_dtype,
                     int32_t format, void* stream);
 
+/* pkv_paged_write for layers layer0 .. layer0 + n_layers - 1 in one launch,
+ * through the one block table all layers share (tiny-llm paged_kv.py: a
+ * block holds the same token positions in every layer's pool).  k and v are
+ * device [n_layers][total_new][n_kv_heads][head_dim]: layer l's rows follow
+ * layer l-1's, and every layer's rows go to the same positions.  ERANGE if
+ * the layers leave the store. */
+int pkv_paged_write_layers(pkv_cache* cache, int32_t layer0, int32_t n_layers,
+                           const int32_t* table, int32_t table_stride, int32_t batch,
+                           const int32_t* start_pos, const int32_t* cu_new, int32_t total_new,
+                           const void* k, const void* v, int32_t in_dtype, int32_t format,
+                           void* stream);
+
 /* Split size (tokens per split-K partition) that pkv_paged_attend uses when
  * called with split_tokens = 0: 1024 tokens (2048 when max_len > 16384),
  * halved down to 256 while batch * n_kv_heads * splits < 512; rounded up to

@@ -209,9 +209,19 @@ int pkv_paged_write(pkv_cache* c, int32_t layer, const int32_t* table, int32_t t
                     int32_t batch, const int32_t* start_pos, const int32_t* cu_new,
                     int32_t total_new, const void* k, const void* v, int32_t in_dtype,
                     int32_t format, void* stream) {
+  return pkv_paged_write_layers(c, layer, 1, table, table_stride, batch, start_pos, cu_new,
+                                total_new, k, v, in_dtype, format, stream);
+}
+
+int pkv_paged_write_layers(pkv_cache* c, int32_t layer0, int32_t n_layers,
+                           const int32_t* table, int32_t table_stride, int32_t batch,
+                           const int32_t* start_pos, const int32_t* cu_new, int32_t total_new,
+                           const void* k, const void* v, int32_t in_dtype, int32_t format,
+                           void* stream) {
   if (!c) return fail(PKV_EINVAL, "cache is null");
-  if (layer < 0 || layer >= c->L.n_layers)
-    return fail(PKV_ERANGE, "layer %d outside [0, %d)", layer, c->L.n_layers);
+  if (n_layers < 1 || layer0 < 0 || (int64_t)layer0 + n_layers > c->L.n_layers)
+    return fail(PKV_ERANGE, "layers [%d, %d) outside [0, %d)", layer0, layer0 + n_layers,
+                c->L.n_layers);
   if (format != c->L.format)
     return fail(PKV_EFORMAT, "write format %d differs from the store's %d", format, c->L.format);
   if (in_dtype != PKV_DT_F32 && in_dtype != PKV_DT_BF16)
@@ -237,7 +247,7 @@ int pkv_paged_write(pkv_cache* c, int32_t layer, const int32_t* table, int32_t t
   a.cu_new = cu_new;
   a.k_in = k;
   a.v_in = v;
-  a.layer_page0 = (int64_t)layer * c->L.n_pages;
+  a.layer_page0 = (int64_t)layer0 * c->L.n_pages;
   a.n_pages = c->L.n_pages;
   a.page_size = c->L.page_size;
   a.n_kv_heads = c->L.n_kv_heads;
@@ -245,6 +255,7 @@ int pkv_paged_write(pkv_cache* c, int32_t layer, const int32_t* table, int32_t t
   a.table_stride = table_stride;
   a.batch = batch;
   a.total_new = total_new;
+  a.n_layers_w = n_layers;
   a.decode_lens = nullptr;
   Timer tm(c, PKV_T_WRITE, static_cast<hipStream_t>(stream));
   hipError_t e = pkv::launch_write(a, c->L.format, in_dtype, tm.l);

@@ -37,9 +37,10 @@ struct WriteArgs {
   const int32_t* cu_new;
   const void* k_in;
   const void* v_in;
-  int64_t layer_page0;  // layer * n_pages
+  int64_t layer_page0;  // first layer * n_pages
   int32_t n_pages, page_size, n_kv_heads, head_dim;
   int32_t table_stride, batch, total_new;
+  int32_t n_layers_w = 1;  // layers written (k_in/v_in: [n_layers_w][total_new][Hkv][D])
   const int32_t* decode_lens;  // non-null: row b goes to position decode_lens[b] - 1 of sequence b
 };
 

@@ -9,7 +9,9 @@
 // libmir-metal src/engine/kv/paged/mod.rs, with scale = max|x| / 127 and
 // codes rint(x / scale) clamped to +-127.
 //
-// One workgroup (one wave) handles 16 consecutive input rows of one KV head.
+// One workgroup (one wave) handles 16 consecutive input rows of one KV head
+// of one layer (grid z: several layers in one launch, each layer's rows
+// following the previous layer's in k_in / v_in).
 // The rows are staged in LDS as 32-bit words (bf16 bits widened to the
 // float32 value's bits), then K is stored as slot rows of head_dim (16-byte
 // vector stores) and V as the dim-major slab (for each dim, consecutive
@@ -41,6 +43,8 @@ __global__ __launch_bounds__(64) void write_kernel(WriteArgs a) {
   const int lane = threadIdx.x;
   const int h = blockIdx.y;
   const int row0 = blockIdx.x * kRows;
+  const int64_t layer_page0 = a.layer_page0 + (int64_t)blockIdx.z * a.n_pages;
+  const int64_t in_row0 = (int64_t)blockIdx.z * a.total_new;  // this layer's rows in k_in/v_in
 
   // ---- row metadata: sequence, position, page, slot ----
   if (lane < kRows) {
@@ -72,7 +76,7 @@ __global__ __launch_bounds__(64) void write_kernel(WriteArgs a) {
           report(a.status, PKV_DEV_WRITE_PAGE);
         } else {
           const int slot = t - j * a.page_size;
-          const int64_t slab = (a.layer_page0 + page) * a.n_kv_heads + h;
+          const int64_t slab = (layer_page0 + page) * a.n_kv_heads + h;
           m.k_off = (slab * a.page_size + slot) * D;
           m.v_off = slab * a.page_size * D + slot;
           m.s_off = slab * a.page_size + slot;
@@ -91,7 +95,7 @@ __global__ __launch_bounds__(64) void write_kernel(WriteArgs a) {
       const int r = row0 + rr;
       uint4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
       if (r < a.total_new) {
-        const int64_t e = ((int64_t)r * a.n_kv_heads + h) * D + d0;
+        const int64_t e = ((in_row0 + r) * a.n_kv_heads + h) * D + d0;
         const int esz = IN_BF16 ? 2 : 4;
         kx = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_in) + e * esz);
         vx = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_in) + e * esz);
@@ -213,7 +217,7 @@ __global__ __launch_bounds__(64) void write_kernel(WriteArgs a) {
 
 hipError_t launch_write(const WriteArgs& a, int fmt, int in_dtype, const Launch& l) {
   if (a.total_new <= 0) return hipSuccess;
-  dim3 grid((a.total_new + kRows - 1) / kRows, a.n_kv_heads);
+  dim3 grid((a.total_new + kRows - 1) / kRows, a.n_kv_heads, a.n_layers_w);
   const size_t shm = 2 * kRows * (a.head_dim + 1) * sizeof(uint32_t);
   const bool bf = in_dtype == PKV_DT_BF16;
   if (fmt == PKV_FMT_F32)

@@ -35,6 +35,8 @@ SYMBOLS = [
     ("pkv_cache_create", C.c_int, [_P, _P, _P, _P, _P, _P, C.POINTER(_P)]),
     ("pkv_cache_destroy", None, [_P]),
     ("pkv_paged_write", C.c_int, [_P, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _P, _I32, _I32, _P]),
+    ("pkv_paged_write_layers", C.c_int,
+     [_P, _I32, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _P, _I32, _I32, _P]),
     ("pkv_attend_split", C.c_int, [_P, _I32, _I32, _I32, _PI32]),
     ("pkv_attend_workspace_size", C.c_int, [_P, _I32, _I32, _I32, _I32, C.POINTER(C.c_uint64)]),
     ("pkv_paged_attend", C.c_int,
@@ -196,6 +198,19 @@ class PagedKVCache:
             _dev(start_pos, torch.int32, "start_pos"), _dev(cu_new, torch.int32, "cu_new"), total,
             _dev(k, name="k"), _dev(v, name="v"), DTYPE_CODE[k.dtype], FORMAT_CODE[self.fmt],
             _stream(self.device)))
+
+    def write_layers(self, table, start_pos, cu_new, k, v, layer0: int = 0):
+        """One launch for several layers: k, v [n_layers, total_new, Hkv, D]."""
+        nl, total = int(k.shape[0]), int(k.shape[1])
+        if tuple(k.shape) != (nl, total, self.n_kv_heads, self.head_dim) or v.shape != k.shape:
+            raise ValueError("k and v must be [n_layers, total_new, n_kv_heads, head_dim]")
+        if k.dtype not in DTYPE_CODE or v.dtype != k.dtype:
+            raise ValueError("k and v must both be float32 or bfloat16")
+        _check(lib().pkv_paged_write_layers(
+            self._h, layer0, nl, _dev(table, torch.int32, "table"), table.shape[1],
+            table.shape[0], _dev(start_pos, torch.int32, "start_pos"),
+            _dev(cu_new, torch.int32, "cu_new"), total, _dev(k, name="k"), _dev(v, name="v"),
+            DTYPE_CODE[k.dtype], FORMAT_CODE[self.fmt], _stream(self.device)))
 
     # -- paged_attend ----------------------------------------------------------
     def split_for(self, batch: int, n_q_heads: int, max_len: int) -> int:

@@ -249,6 +249,13 @@ def test_write_validation():
     assert w(k=None) == pkv.EINVAL
     assert w(k=C.c_void_p(FAKE + 2)) == pkv.EINVAL
     assert w(total=0) == pkv.OK  # nothing to do, nothing launched
+
+    def wl(layer0=0, n=1):
+        return L.pkv_paged_write_layers(h, layer0, n, P, 4, 2, P, P, 5, P, P, pkv.DT_BF16,
+                                        pkv.FMT_BF16, None)
+    assert wl(n=2) == pkv.ERANGE  # the store has one layer
+    assert wl(n=0) == pkv.ERANGE
+    assert wl(layer0=-1) == pkv.ERANGE
     assert b"16-byte" in L.pkv_last_error() or True
     L.pkv_cache_destroy(h)
 

@@ -11,18 +11,29 @@
 // decode rule of tiny-llm paged_kv.py when T_b = 1.  A position below 0 sees
 // nothing and gives zeros.
 //
-// How, on gfx950.  The 16 columns of the matrix-core tiles (mfma_step.h)
-// are (query position, head) pairs of one KV head's group: n_pos = 16 / G
-// consecutive positions times the G heads, so every K/V byte a wave loads
-// serves all of them; each column keeps its own causal bound, its own
-// running maximum and sum.  One wave owns one (sequence, KV head, group of
-// n_pos positions) and walks the tokens up to its last position in 32-token
-// steps, loads one step ahead (two register sets, peeled tail, as the decode
-// kernel), and writes normalised outputs; there is no split of the token
-// range, the parallelism comes from the queries.
+// How, on gfx950.  A workgroup of 4 waves owns one (sequence, KV head) and
+// 8 * n_pos consecutive positions of its chunk; each wave holds two tiles of
+// 16 matrix-core columns, each tile n_pos = 16 / G positions times the G
+// heads (mfma_step.h gives the tile layouts), every column with its own
+// causal bound, running maximum and sum.  Both tiles use the same K/V
+// operand registers, so each LDS read feeds two matrix-core operations.  The workgroup walks the tokens up to its last position in
+// 32-token steps: all 256 threads load the next step's K/V (and int8 scales)
+// from the pages into registers while the waves compute the current step
+// from LDS, then store it into the other LDS buffer (one barrier per step).
+// int8 codes are converted to bf16 once, on the way into LDS, and slots past
+// the range or on a missing page are stored as zeros, so every wave reads
+// plain bf16 operands.  Each byte read from the pages thus serves 128 query
+// columns; there is no split of the token range, the parallelism comes from
+// the queries.  Steps that every column of a wave sees whole skip the
+// per-token masks, and the output is rescaled only when some column's
+// running maximum grew.
+//
+// LDS holds K as [32 tokens][head_dim] (tokens in score-tile order, see
+// k_row) and V as [head_dim][32 tokens], bf16, rows padded by 16 bytes so the
+// rows one read instruction touches fall on different banks.
 //
 // Launch order is XCD-aware: workgroups are handed to the 8 XCDs in turn, so
-// block x runs on XCD x % 8; the items of one (sequence, KV head) are given
+// block x runs on XCD x % 8; the blocks of one (sequence, KV head) are given
 // consecutive blocks of one XCD, where they run together and share that
 // XCD's L2 copy of the sequence's pages.
 #include <algorithm>
@@ -33,168 +44,413 @@ namespace pkv {
 namespace {
 
 constexpr int kXcds = 8;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTiles = 2;  // 16-column tiles per wave: both use the same K/V operands
+constexpr int kPageWin = 1024;  // page ids staged in LDS at a time
+
+template <int D>
+struct MultiLds {
+  static constexpr int KP = 2 * D + 16;       // K row pitch in bytes (one token)
+  static constexpr int VP = 2 * 32 + 16;      // V row pitch in bytes (one dim)
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = 32 * KP;
+  static constexpr int S_OFF = V_OFF + D * VP;  // int8: 32 K scales, then 32 V scales
+  static constexpr int BUF = S_OFF + 64 * 4;
+};
+
+// LDS row of token r of a step: the 16 tokens of score tile t (token
+// 8 (n / 4) + 4t + n % 4 for row n) are stored in rows 16t .. 16t+15, so the
+// lanes of one read instruction touch consecutive rows, whose 16-byte-padded
+// pitch spreads them over distinct banks.
+__device__ __forceinline__ int k_row(int r) {
+  return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+}
+
+// 16 int8 codes -> 16 bf16 (two 16-byte words)
+__device__ __forceinline__ void codes16_to_bf16(uint4 w, uint4& lo, uint4& hi) {
+  const uint2 a = codes_to_bf16(w.x), b = codes_to_bf16(w.y);
+  const uint2 c = codes_to_bf16(w.z), d = codes_to_bf16(w.w);
+  lo = uint4{a.x, a.y, b.x, b.y};
+  hi = uint4{c.x, c.y, d.x, d.y};
+}
+
+// zero the bf16 elements e (0..7) of a 16-byte word with dead[e]
+__device__ __forceinline__ uint4 zero_dead(uint4 v, uint32_t dead_bits) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t m = ((dead_bits >> (2 * i)) & 1u ? 0x0000ffffu : 0u) |
+                       ((dead_bits >> (2 * i + 1)) & 1u ? 0xffff0000u : 0u);
+    w[i] &= ~m;
+  }
+  return uint4{w[0], w[1], w[2], w[3]};
+}
 
 template <int FMT, int D, int BS>
-__global__ __launch_bounds__(64, 2) void attend_multi_kernel(MultiArgs a) {
-  using S = Step<FMT, D>;
-  constexpr int NC = S::NC, ND = S::ND;
-  constexpr int ESZ = FMT == PKV_FMT_BF16 ? 2 : 1;
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(kThreads, 2) void attend_multi_kernel(MultiArgs a) {
+  using L = MultiLds<D>;
+  constexpr int NC = D / 32, ND = D / 16;
+  constexpr int ESZ = FMT == PKV_FMT_BF16 ? 2 : 1;  // page element bytes
+  constexpr int E = 16 / ESZ;                        // elements per 16-byte chunk
+  constexpr int CK = D / E;                          // K chunks per token row
+  constexpr int NKC = 32 * CK;                       // K chunks per step
+  constexpr int CV = 32 / E;                         // V chunks per dim row
+  constexpr int NVC = D * CV;                        // V chunks per step
+  constexpr int KL = (NKC + kThreads - 1) / kThreads;
+  constexpr int VL = (NVC + kThreads - 1) / kThreads;
+  __shared__ __align__(16) char lds[2 * L::BUF];
+
+  const int tid = threadIdx.x;
+  // wave-uniform values are made scalar so that branches on them are
+  // scalar branches, not per-lane masks
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int n = lane & 15;  // column (B/C operands)
   const int j = lane >> 4;  // k group (A/B operands), row quad (C operand)
   const int G = a.group;
   const int P = a.n_pos;
   const int bs = BS ? BS : a.page_size;
 
-  // ---- the item: (sequence, KV head) pair and group of positions
+  // ---- the item: (sequence, KV head) pair and block of 4 * P positions
   const int xcd = blockIdx.x % kXcds;
   const int k = blockIdx.x / kXcds;
   const int pair = (k / a.n_qgroups) * kXcds + xcd;
-  const int qg = k % a.n_qgroups;
-  if (pair >= a.batch * a.n_kv_heads) return;
+  const int qb = k % a.n_qgroups;
+  if (pair >= a.batch * a.n_kv_heads) return;  // whole workgroup: uniform
   const int b = pair / a.n_kv_heads;
   const int g = pair - b * a.n_kv_heads;
-  const bool reporter = qg == 0 && g == 0 && lane == 0;
-  int q0 = a.cu_q[b];
-  int T = a.cu_q[b + 1] - q0;
+  const bool reporter = qb == 0 && g == 0 && tid == 0;
+  const int q0 = __builtin_amdgcn_readfirstlane(a.cu_q[b]);
+  const int T = __builtin_amdgcn_readfirstlane(a.cu_q[b + 1]) - q0;
   if (q0 < 0 || T < 0 || q0 + T > a.total_q) {
     if (reporter) report(a.status, PKV_DEV_QROWS);
     return;  // malformed rows: none is read or written
   }
-  const int len = clamp_len(a.lens[b], a.max_len, reporter ? a.status : nullptr, PKV_DEV_LEN);
+  const int len = clamp_len(__builtin_amdgcn_readfirstlane(a.lens[b]), a.max_len,
+                            reporter ? a.status : nullptr, PKV_DEV_LEN);
   if (reporter && (T > len || T > a.max_q)) report(a.status, PKV_DEV_QROWS);
-  const int p0 = qg * P;
-  if (p0 >= T) return;
+  const int pb0 = qb * kWaves * kTiles * P;  // the block's first position
+  if (pb0 >= T) return;
+  const int last_blk = min(pb0 + kWaves * kTiles * P, T) - 1;
+  const int t_end = min(max(len - T + last_blk + 1, 0), len);  // tokens the block reads
 
-  // ---- this lane's column: position p0 + p of the chunk, head g * G + h
+  // ---- this wave's positions (kTiles tiles of P) and this lane's columns
+  const int p0 = pb0 + wave * kTiles * P;
   const int p = n / G;
   const int h = n - p * G;
-  const bool col = n < P * G && p0 + p < T;
-  const int pos = len - T + p0 + p;  // below 0: sees nothing
-  const int last = min(p0 + P, T) - 1;
-  const int t_end = min(max(len - T + last + 1, 0), len);  // tokens the item reads
-
-  bf16x8 qf[NC];
-  const int64_t qrow = col ? (int64_t)(q0 + p0 + p) * a.n_q_heads + (int64_t)g * G + h : 0;
-  load_q<FMT, D>(qf, static_cast<const uint16_t*>(a.q) + qrow * D, col && pos >= 0, j);
-
-  const int64_t slab_bytes = (int64_t)bs * D * ESZ;
-  const PageSrc src{static_cast<const char*>(a.k_pages), static_cast<const char*>(a.v_pages),
-                    a.k_scales, a.v_scales, a.layer_page0, slab_bytes, a.n_kv_heads, bs};
-  const int32_t* trow = a.table + (int64_t)b * a.table_stride;
-  const int pg_last = (t_end - 1) / bs;
-
-  f32x4 o[ND];
+  bool col[kTiles];
+  int pos[kTiles];  // below 0: sees nothing
+  int64_t qrow[kTiles];
+  bf16x8 qf[kTiles][NC];
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
-  const float qs = a.qk_scale_log2;
+  for (int u = 0; u < kTiles; ++u) {
+    const int pu = p0 + u * P + p;
+    col[u] = n < P * G && pu < T;
+    pos[u] = len - T + pu;
+    qrow[u] = col[u] ? (int64_t)(q0 + pu) * a.n_q_heads + (int64_t)g * G + h : 0;
+    load_q<PKV_FMT_BF16, D>(qf[u], static_cast<const uint16_t*>(a.q) + qrow[u] * D,
+                            col[u] && pos[u] >= 0, j);
+  }
+  const int w_last = p0 < T ? len - T + min(p0 + kTiles * P, T) - 1 : -1;  // wave's last
 
-  // windows of at most 64 logical pages: one table entry per lane
-  const int tokens_per_window = 64 * bs;
-  for (int w0 = 0; w0 < t_end; w0 += tokens_per_window) {
-    const int w_end = min(w0 + tokens_per_window, t_end);
-    const int pg0 = w0 / bs;
-    int vpage = -1;
-    {
-      const int lp = pg0 + lane;
+  const char* kp = static_cast<const char*>(a.k_pages);
+  const char* vp = static_cast<const char*>(a.v_pages);
+  const int64_t slab_bytes = (int64_t)bs * D * ESZ;
+  const int32_t* trow = a.table + (int64_t)b * a.table_stride;
+  const int pg_last = t_end > 0 ? (t_end - 1) / bs : -1;
+
+  // Page ids of a window of kPageWin logical pages, staged in LDS by the
+  // whole workgroup (bad entries stored as -1 and reported), so a step's page
+  // lookups are LDS reads and the step loads never wait on a table load.
+  __shared__ int32_t pids[kPageWin];
+  int win0 = 0;  // first logical page held in pids
+  auto stage_pages = [&](int lp0) {  // all threads; ends with a barrier
+    win0 = lp0;
+    for (int e = tid; e < kPageWin; e += kThreads) {
+      const int lp = lp0 + e;
+      int v = -1;
       if (lp <= pg_last) {
         const int pg = trow[lp];
         if (pg < 0 || pg >= a.n_pages) report(a.status, PKV_DEV_READ_PAGE);
-        else vpage = pg;
+        else v = pg;
+      }
+      pids[e] = v;
+    }
+    __syncthreads();
+  };
+  auto page_of = [&](int lp) {  // uniform; -1 past the range or on a bad entry
+    return lp > pg_last ? -1 : __builtin_amdgcn_readfirstlane(pids[lp - win0]);
+  };
+  // whether the window must move before the pages of logical page lp (and
+  // lp + 1) can be looked up
+  auto window_misses = [&](int lp) { return lp < win0 || lp + 1 >= win0 + kPageWin; };
+
+  // ---- cooperative step load: registers, then LDS
+  struct Stage {
+    uint4 kc[KL], vc[VL];
+    float sc;
+    int page_a, page_b, slot0;
+  };
+  auto load_stage = [&](int ts, Stage& st) {
+    const int lp = ts / bs;
+    st.page_a = page_of(lp);
+    st.page_b = BS == 16 ? (ts + 16 < t_end ? page_of(lp + 1) : -1) : st.page_a;
+    st.slot0 = ts - lp * bs;
+    const int64_t sa = (a.layer_page0 + max(st.page_a, 0)) * a.n_kv_heads + g;
+    const int64_t sb = (a.layer_page0 + max(st.page_b, 0)) * a.n_kv_heads + g;
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      const int q = tid + i * kThreads;
+      st.kc[i] = uint4{0, 0, 0, 0};
+      if (NKC % kThreads == 0 || q < NKC) {
+        const int r = q / CK, c = q - r * CK;  // token row, chunk
+        const bool on_b = BS == 16 && r >= 16;
+        const int slot = BS == 16 ? (r & 15) : st.slot0 + r;
+        st.kc[i] = stream_load<uint4, typename Step<FMT, D>::u32x4>(
+            kp + (on_b ? sb : sa) * slab_bytes + ((int64_t)slot * D + c * E) * ESZ);
       }
     }
-
-    auto load_step_at = [&](int ts, S& r) {
-      const int lp = ts / bs;
-      const int page_a = ts < w_end ? __builtin_amdgcn_readlane(vpage, lp - pg0) : -1;
-      int page_b = page_a;
-      if (BS == 16) page_b = ts + 16 < w_end ? __builtin_amdgcn_readlane(vpage, lp + 1 - pg0) : -1;
-      load_step<FMT, D, BS>(r, src, page_a, page_b, ts - lp * bs, g, lane);
+#pragma unroll
+    for (int i = 0; i < VL; ++i) {
+      const int q = tid + i * kThreads;
+      st.vc[i] = uint4{0, 0, 0, 0};
+      if (NVC % kThreads == 0 || q < NVC) {
+        const int d = q / CV, kk = q - d * CV;  // dim row, token group
+        const int t0 = kk * E;
+        const bool on_b = BS == 16 && t0 >= 16;
+        const int slot = BS == 16 ? (t0 & 15) : st.slot0 + t0;
+        st.vc[i] = stream_load<uint4, typename Step<FMT, D>::u32x4>(
+            vp + (on_b ? sb : sa) * slab_bytes + ((int64_t)d * bs + slot) * ESZ);
+      }
+    }
+    st.sc = 0.f;
+    if (FMT == PKV_FMT_INT8 && tid < 64) {
+      const int x = tid & 31;
+      const bool on_b = BS == 16 && x >= 16;
+      const int slot = BS == 16 ? (x & 15) : st.slot0 + x;
+      const float* sp = tid < 32 ? a.k_scales : a.v_scales;
+      st.sc = __builtin_nontemporal_load(sp + (on_b ? sb : sa) * bs + slot);
+    }
+  };
+  auto store_stage = [&](int ts, const Stage& st, char* buf) {
+    // token r of the step is dead past the block's range or on a missing page
+    const bool whole = ts + 32 <= t_end && st.page_a >= 0 && st.page_b >= 0;  // uniform
+    auto dead = [&](int r) {
+      return !whole && (ts + r >= t_end || (BS == 16 && r >= 16 ? st.page_b : st.page_a) < 0);
     };
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      const int q = tid + i * kThreads;
+      if (NKC % kThreads == 0 || q < NKC) {
+        const int r = q / CK, c = q - r * CK;
+        char* dst = buf + L::K_OFF + k_row(r) * L::KP + c * E * 2;
+        const bool z = dead(r);
+        if constexpr (FMT == PKV_FMT_BF16) {
+          *reinterpret_cast<uint4*>(dst) = z ? uint4{0, 0, 0, 0} : st.kc[i];
+        } else {
+          uint4 lo, hi;
+          codes16_to_bf16(st.kc[i], lo, hi);
+          if (z) lo = hi = uint4{0, 0, 0, 0};
+          *reinterpret_cast<uint4*>(dst) = lo;
+          *reinterpret_cast<uint4*>(dst + 16) = hi;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VL; ++i) {
+      const int q = tid + i * kThreads;
+      if (NVC % kThreads == 0 || q < NVC) {
+        const int d = q / CV, kk = q - d * CV;
+        const int t0 = kk * E;
+        char* dst = buf + L::V_OFF + d * L::VP + t0 * 2;
+        uint32_t dbits = 0;  // one bit per token of the chunk
+#pragma unroll
+        for (int e = 0; e < E; ++e) dbits |= (dead(t0 + e) ? 1u : 0u) << e;
+        if constexpr (FMT == PKV_FMT_BF16) {
+          *reinterpret_cast<uint4*>(dst) = zero_dead(st.vc[i], dbits);
+        } else {
+          uint4 lo, hi;
+          codes16_to_bf16(st.vc[i], lo, hi);
+          *reinterpret_cast<uint4*>(dst) = zero_dead(lo, dbits & 0xffu);
+          *reinterpret_cast<uint4*>(dst + 16) = zero_dead(hi, dbits >> 8);
+        }
+      }
+    }
+    if (FMT == PKV_FMT_INT8 && tid < 64)
+      reinterpret_cast<float*>(buf + L::S_OFF)[tid] = dead(tid & 31) ? 0.f : st.sc;
+  };
 
-    auto compute_step = [&](int ts, S& r) {
-      f32x4 sacc[2];
-      step_scores<FMT, D>(r, qf, sacc);
-      const bool lane_live = BS == 16 && j >= 2 ? r.live_b : r.live_a;
-      float ksc[8], vsc[8];
-      if constexpr (FMT == PKV_FMT_INT8) step_scales<FMT, D>(r, j, ksc, vsc);
-      float sv[8];
-      bool readable[8], ok[8];  // token 8j + x: stored on a valid page / seen by the column
-      float mx = -INFINITY;
+  f32x4 o[kTiles][ND];
+  float m[kTiles], l[kTiles];
+#pragma unroll
+  for (int u = 0; u < kTiles; ++u) {
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[u] = -INFINITY;
+    l[u] = 0.f;
+  }
+  const float qs = a.qk_scale_log2;
+  const bool raw_max = qs > 0.f;  // the maximum of raw sums scales to the maximum of scores
+
+  // The wave's smallest position: every column of the wave sees a step whole
+  // when the step lies below it (and inside the block's range, on live pages).
+  const int pos_min = len - T + p0;
+
+  auto compute_step = [&](int ts, const char* buf, bool live_a, bool live_b) {
+    f32x4 sacc[kTiles][2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+#pragma unroll
+      for (int u = 0; u < kTiles; ++u) sacc[u][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int row = 16 * tau + n;  // LDS row of token 8 (n / 4) + 4 tau + n % 4
+      // all of the tile's K chunks in one batch of reads, then the products
+      uint4 kw[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        kw[c] = *reinterpret_cast<const uint4*>(buf + L::K_OFF + row * L::KP +
+                                                kdim_of<PKV_FMT_BF16>(c, j) * 2);
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int u = 0; u < kTiles; ++u)
+          sacc[u][tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw[c]), qf[u][c],
+                                                                 sacc[u][tau], 0, 0, 0);
+    }
+    float ksc[8], vsc[8];
+    if constexpr (FMT == PKV_FMT_INT8) {
+      const float4* sp = reinterpret_cast<const float4*>(buf + L::S_OFF);
+      const float4 k0 = sp[2 * j], k1 = sp[2 * j + 1], v0 = sp[8 + 2 * j], v1 = sp[8 + 2 * j + 1];
+      const float kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+      const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        const int t = ts + 8 * j + x;
-        readable[x] = lane_live && t < w_end;
-        ok[x] = readable[x] && t <= pos;
-        float y = sacc[x >> 2][x & 3] * qs;
-        if (FMT == PKV_FMT_INT8) y *= ksc[x];
-        sv[x] = ok[x] ? y : -INFINITY;
-        mx = fmaxf(mx, sv[x]);
+        ksc[x] = kk[x];
+        vsc[x] = vv[x];
+      }
+    }
+    // wave-uniform: every token of the step is seen by every column
+    const bool open = live_a && live_b && ts + 31 <= pos_min && ts + 32 <= t_end;
+    const bool lane_live = BS == 16 && j >= 2 ? live_b : live_a;
+    bf16x8 pb[kTiles];
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) {
+      // scores in log2 units: sacc * qs (int8: times the token's K scale).
+      // With bf16 pages and qs > 0 the maximum is taken over the raw sums and
+      // the scale goes into one fma inside the exponential.
+      float mx = -INFINITY;
+      float sv[8];
+      bool ok[8];  // token 8j + x of the step: on a valid page and seen by the column
+      if (open) {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          sv[x] = sacc[u][x >> 2][x & 3];
+          if (FMT == PKV_FMT_INT8 || !raw_max) sv[x] *= qs * (FMT == PKV_FMT_INT8 ? ksc[x] : 1.f);
+          mx = fmaxf(mx, sv[x]);
+          ok[x] = true;
+        }
+        if (FMT == PKV_FMT_BF16 && raw_max) mx *= qs;
+      } else {
+        const int lim = min(pos[u], t_end - 1) - ts - 8 * j;  // token 8j + x seen iff x <= lim
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          ok[x] = lane_live && x <= lim;
+          float y = sacc[u][x >> 2][x & 3] * qs;
+          if (FMT == PKV_FMT_INT8) y *= ksc[x];
+          sv[x] = ok[x] ? y : -INFINITY;
+          mx = fmaxf(mx, sv[x]);
+        }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m, mx);
+      const float m_new = fmaxf(m[u], mx);
+      // lazy rescale: the output only moves when some column's maximum grew
+      const bool grow = __any(m_new > m[u]);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m[u] - m_use) : 1.f;
       float psum = 0.f;
-      bf16x8 pb;
+      if (open) {
 #pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const float pr = ok[x] ? __builtin_amdgcn_exp2f(sv[x] - m_use) : 0.f;
-        psum += pr;
-        float pw = pr;
-        if (FMT == PKV_FMT_INT8) pw = ok[x] ? pr * vsc[x] : 0.f;
-        pb[x] = (__bf16)pw;
+        for (int x = 0; x < 8; ++x) {
+          const float pr = FMT == PKV_FMT_BF16 && raw_max
+                               ? __builtin_amdgcn_exp2f(fmaf(sv[x], qs, -m_use))
+                               : __builtin_amdgcn_exp2f(sv[x] - m_use);
+          psum += pr;
+          pb[u][x] = (__bf16)(FMT == PKV_FMT_INT8 ? pr * vsc[x] : pr);
+        }
+      } else {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const float pr = ok[x] ? __builtin_amdgcn_exp2f(sv[x] - m_use) : 0.f;
+          psum += pr;
+          pb[u][x] = (__bf16)(FMT == PKV_FMT_INT8 ? pr * vsc[x] : pr);
+        }
       }
-      l = l * alpha + psum;
-      m = m_new;
-      // every stored slot is finite; only slots past the item's range (or
-      // on a missing page) may hold NaN and are zeroed
-      uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
-      if (FMT == PKV_FMT_BF16 && (ts + 32 > w_end || !r.live_a || !r.live_b))
-        v_keep_masks(readable, keep);
-      step_pv<FMT, D>(r, pb, keep, alpha, o);
-    };
-
-    // ---- two register sets, loads one step ahead, prefetches unconditional
-    // in the loop body and the last one or two steps peeled
-    const int n_steps = (w_end - w0 + 31) / 32;
-    auto T32 = [&](int i) { return w0 + 32 * i; };
-    S r0, r1;
-    load_step_at(T32(0), r0);
-    int st = 0;
-    for (; st + 2 < n_steps; st += 2) {
-      load_step_at(T32(st + 1), r1);
-      compute_step(T32(st), r0);
-      load_step_at(T32(st + 2), r0);
-      compute_step(T32(st + 1), r1);
+      l[u] = l[u] * alpha + psum;
+      m[u] = m_new;
+      if (grow) {
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) o[u][dt] *= alpha;
+      }
     }
-    if (st + 1 < n_steps) {
-      load_step_at(T32(st + 1), r1);
-      compute_step(T32(st), r0);
-      compute_step(T32(st + 1), r1);
-    } else {
-      compute_step(T32(st), r0);
+    uint4 vw[ND];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+      vw[dt] = *reinterpret_cast<const uint4*>(buf + L::V_OFF + (16 * dt + n) * L::VP + 16 * j);
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int u = 0; u < kTiles; ++u)
+        o[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vw[dt]), pb[u], o[u][dt], 0, 0, 0);
+  };
+
+  // ---- the step loop: the loads of step i+1 are in flight while step i is
+  // computed from LDS; then step i+1 goes into the other LDS buffer (one
+  // barrier per step).  The prefetch is issued every iteration (past the
+  // last step it reloads the last step, unused): a load under a condition
+  // would make every step wait for all outstanding loads.
+  const int n_steps = (t_end + 31) / 32;
+  if (n_steps > 0) {
+    const int ts_last = 32 * (n_steps - 1);
+    stage_pages(0);
+    Stage st;
+    load_stage(0, st);
+    store_stage(0, st, lds);
+    bool la = st.page_a >= 0, lb = st.page_b >= 0;
+    __syncthreads();
+    for (int i = 0; i < n_steps; ++i) {
+      const int ts = 32 * i;
+      const int ts1 = min(ts + 32, ts_last);
+      if (window_misses(ts1 / bs)) stage_pages(ts1 / bs);  // uniform, rare
+      load_stage(ts1, st);
+      if (ts <= w_last) compute_step(ts, lds + (i & 1) * L::BUF, la, lb);
+      if (i + 1 < n_steps) {
+        store_stage(ts + 32, st, lds + ((i + 1) & 1) * L::BUF);
+        la = st.page_a >= 0;
+        lb = st.page_b >= 0;
+      }
+      __syncthreads();
     }
   }
 
   // ---- results: O^T lane layout = dims 16 dt + 4j + i of column n
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  if (col) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-      store_out4(a.out, 1, qrow * D + 16 * dt + 4 * j, o[dt] * inv);
+  for (int u = 0; u < kTiles; ++u) {
+    float lu = l[u];
+    lu += __shfl_xor(lu, 16, 64);
+    lu += __shfl_xor(lu, 32, 64);
+    if (col[u]) {
+      const float inv = lu > 0.f ? 1.f / lu : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+        store_out4(a.out, 1, qrow[u] * D + 16 * dt + 4 * j, o[u][dt] * inv);
+    }
   }
 }
 
 template <int FMT, int D, int BS>
 hipError_t launch_bs(const MultiArgs& a, const Launch& l) {
-  const int64_t pairs = (int64_t)a.batch * a.n_kv_heads;
-  const int64_t grid = (pairs + kXcds - 1) / kXcds * kXcds * a.n_qgroups;
-  return launch1(attend_multi_kernel<FMT, D, BS>, dim3((unsigned)grid), dim3(64), 0, l, a);
+  const int64_t grid = multi_grid(a.batch, a.n_kv_heads, a.n_qgroups);
+  return launch1(attend_multi_kernel<FMT, D, BS>, dim3((unsigned)grid), dim3(kThreads), 0, l, a);
 }
 
 template <int FMT, int D>
@@ -210,6 +466,8 @@ hipError_t launch_fmt(const MultiArgs& a, const Launch& l) {
 }
 
 }  // namespace
+
+int multi_positions_per_block(int group) { return kWaves * kTiles * (16 / group); }
 
 int64_t multi_grid(int batch, int n_kv_heads, int n_qgroups) {
   const int64_t pairs = (int64_t)batch * n_kv_heads;

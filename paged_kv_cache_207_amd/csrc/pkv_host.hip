@@ -482,7 +482,8 @@ int pkv_paged_attend_multi(pkv_cache* c, int32_t layer, const void* q, int32_t q
   a.total_q = total_q;
   a.max_q = max_q;
   a.n_pos = 16 / group;
-  a.n_qgroups = (max_q + a.n_pos - 1) / a.n_pos;
+  const int per_block = pkv::multi_positions_per_block(group);
+  a.n_qgroups = (max_q + per_block - 1) / per_block;
   if (pkv::multi_grid(batch, c->L.n_kv_heads, a.n_qgroups) > INT32_MAX)
     return fail(PKV_EINVAL, "too many work items (batch %d, max_q %d)", batch, max_q);
   const hipStream_t s = static_cast<hipStream_t>(stream);

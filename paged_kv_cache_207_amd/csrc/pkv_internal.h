@@ -86,8 +86,8 @@ struct MultiArgs {
   float qk_scale_log2;  // softmax scale * log2(e)
   int32_t n_pages, page_size, n_kv_heads, head_dim, n_q_heads, group;
   int32_t table_stride, batch, max_len, total_q, max_q;
-  int32_t n_pos;      // query positions per work item (16 / group)
-  int32_t n_qgroups;  // work items per (sequence, KV head): ceil(max_q / n_pos)
+  int32_t n_pos;      // query positions per wave (16 / group)
+  int32_t n_qgroups;  // workgroups per (sequence, KV head): ceil(max_q / positions per block)
 };
 
 // Arguments of the page-copy kernel (copy-on-write).
@@ -154,6 +154,7 @@ hipError_t launch_reduce(const AttendArgs& a, const Launch& l);
 // Returns hipErrorNotSupported when the shape has no matrix-core variant.
 hipError_t launch_attend_multi(const MultiArgs& a, int fmt, const Launch& l);
 int64_t multi_grid(int batch, int n_kv_heads, int n_qgroups);
+int multi_positions_per_block(int group);
 hipError_t launch_copy_pages(const CopyArgs& a, const Launch& l);
 hipError_t launch_probe(const void* src, void* dst, float* sink, uint64_t bytes, int mode,
                         hipStream_t s);

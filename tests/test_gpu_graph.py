@@ -1,0 +1,97 @@
+"""The decode step under HIP-graph capture: each step's device work -- the
+table updates (a fixed-size padded list; padding rows name no sequence and
+are skipped) and pkv_decode_step -- captured once per step and replayed, with
+eager work and synchronisations between replays, bit-identical to the eager
+steps every time."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_207_amd import pkv
+from paged_kv_cache_207_amd import workloads as W
+from tests.gpu_helpers import dev, gpu_write, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_decode_steps_replayed_from_graphs():
+    require_gpu()
+    sp = W.shared_prefix(batch=12, prefix_pages=4, lo=5, hi=60, n_steps=6, n_q_heads=8,
+                         n_kv_heads=2, head_dim=64)
+    w = sp.base
+    B, bs, cap = w.batch, w.page_size, w.batch + 8
+    ks, vs = sp.step_rows_all()
+    qs = torch.stack([w.query(step=s) for s in range(sp.n_steps)]).cuda()
+    ks, vs = ks.cuda(), vs.cuda()
+    lens_all = torch.stack([torch.as_tensor(sp.step_lens(s)) for s in range(sp.n_steps)]).cuda()
+    max_len = int(sp.step_lens(sp.n_steps - 1).max())
+
+    def setup():
+        pool = pkv.PagePool(w.n_pages)
+        seqs = pkv.SeqTables(pool, B, w.table_stride, bs)
+        seqs.append(0, sp.prefix_tokens)
+        for b in range(1, B):
+            seqs.share(b, 0, sp.prefix_pages)
+        for b in range(B):
+            seqs.append(b, int(sp.suffix[b]))
+        table = torch.full((B, w.table_stride), -1, dtype=torch.int32, device="cuda")
+        pkv.table_apply(table, seqs.take_updates().cuda())
+        cache = pkv.PagedKVCache(w.n_pages, bs, w.n_kv_heads, w.head_dim, w.kv_format)
+        gpu_write(cache, table, sp.fill_rounds())
+        return pool, seqs, table, cache
+
+    # eager reference: per step, host growth, device table updates, decode step
+    pool, seqs, table, cache = setup()
+    ref = []
+    for s in range(sp.n_steps):
+        seqs.append_all(1)
+        upd = seqs.take_updates()
+        if upd.shape[0]:
+            pkv.table_apply(table, upd.cuda())
+        ref.append(cache.decode_step(table, lens_all[s], max_len, ks[s], vs[s], qs[s], w.scale))
+    torch.cuda.synchronize()
+    ref = [r.clone() for r in ref]
+    ref_table = table.clone()
+
+    # graphs: one per step, over static buffers
+    pool2, seqs2, table2, cache2 = setup()
+    split = cache2.split_for(B, w.n_q_heads, max_len)
+    ws = cache2.workspace(B, w.n_q_heads, max_len, split)
+    upd_host = [torch.full((cap, 3), -1, dtype=torch.int32).pin_memory() for _ in range(sp.n_steps)]
+    upd_dev = torch.full((cap, 3), -1, dtype=torch.int32, device="cuda")
+    outs = [torch.empty_like(qs[0]) for _ in range(sp.n_steps)]
+    stream = torch.cuda.Stream()
+    graphs = []
+    with torch.cuda.stream(stream):
+        for s in range(sp.n_steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                upd_dev.copy_(upd_host[s], non_blocking=True)
+                pkv.table_apply(table2, upd_dev)
+                cache2.decode_step(table2, lens_all[s], max_len, ks[s], vs[s], qs[s], w.scale,
+                                   out=outs[s], workspace=ws, split_tokens=split)
+            graphs.append(g)
+    torch.cuda.synchronize()
+    say(f"captured {len(graphs)} step graphs")
+
+    for s in range(sp.n_steps):
+        seqs2.append_all(1)
+        u = seqs2.take_updates()
+        assert u.shape[0] <= cap
+        upd_host[s].fill_(-1)
+        upd_host[s][:u.shape[0]] = u
+        graphs[s].replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs[s], ref[s]), s
+    assert torch.equal(table2, ref_table)
+    # replays again, with eager work between them: the same outputs every time
+    for rep in range(3):
+        for s in range(sp.n_steps):
+            scratch = torch.randn(1 << 16, device="cuda").sum()  # eager work
+            graphs[s].replay()
+            torch.cuda.synchronize()
+            assert torch.equal(outs[s], ref[s]), (rep, s)
+            del scratch
+    assert cache2.status() == 0

@@ -73,6 +73,9 @@ extern "C" {
                                    its sequence (rows before position 0 give zeros) or
                                    longer than max_q (rows past max_q may be left
                                    unwritten) */
+#define PKV_DEV_WRITE_ROWS 32u  /* paged_write met a sequence whose rows cu_new[b] ..
+                                   cu_new[b+1] are decreasing or outside [0, total_new]
+                                   (that sequence skipped) */
 
 typedef enum { PKV_FMT_F32 = 0, PKV_FMT_BF16 = 1, PKV_FMT_INT8 = 2 } pkv_format;
 typedef enum { PKV_DT_F32 = 0, PKV_DT_BF16 = 1 } pkv_dtype;
@@ -118,6 +121,9 @@ void pkv_cache_destroy(pkv_cache* cache);
  *              write reaches are never read.
  *   start_pos  device int32 [batch]; cu_new device int32 [batch + 1],
  *              non-decreasing, cu_new[0] = 0, cu_new[batch] = total_new.
+ *              Device-side, a sequence whose row range is decreasing or
+ *              outside [0, total_new] is skipped and sets PKV_DEV_WRITE_ROWS;
+ *              positions without a page set PKV_DEV_WRITE_TABLE/_PAGE.
  *   k, v       device [total_new][n_kv_heads][head_dim] of in_dtype.
  *   format     must equal the store's format (EFORMAT otherwise).
  * F32 pages take f32 rows and BF16 pages bf16 rows, copied bit for bit.

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 OK, EINVAL, ERANGE, EFORMAT, ENOMEM, EHIP, EDOUBLEFREE = 0, -1, -2, -3, -4, -5, -6
 FMT_F32, FMT_BF16, FMT_INT8 = 0, 1, 2
 DT_F32, DT_BF16 = 0, 1
-DEV_WRITE_PAGE, DEV_WRITE_TABLE, DEV_READ_PAGE, DEV_LEN, DEV_QROWS = 1, 2, 4, 8, 16
+DEV_WRITE_PAGE, DEV_WRITE_TABLE, DEV_READ_PAGE, DEV_LEN, DEV_QROWS, DEV_WRITE_ROWS = 1, 2, 4, 8, 16, 32
 ATTEND_VALU, ATTEND_COMBINE_KERNEL, ATTEND_COMBINE_FUSED = 1, 2, 4
 T_WRITE, T_ATTEND_SPLIT, T_ATTEND_COMBINE, T_GATHER, T_ATTEND_MULTI, T_COPY_PAGES = 0, 1, 2, 3, 4, 5
 T_COUNT = 6

@@ -95,6 +95,119 @@ def test_int8_and_f32_rows_with_ties_and_zero_rows(fmt):
             assert np.array_equal(VS.view(np.uint32), o.v_scale.view(np.uint32))
 
 
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "int8"])
+@pytest.mark.parametrize("bs", [4, 8, 16, 32])
+def test_write_aligned_runs_and_stragglers(fmt, bs):
+    """Blocks of rows that fill whole aligned runs of a page's slots (stored
+    as vectors along each V dim row) next to blocks that straddle sequences,
+    pages or an unaligned start (stored slot by slot), over two rounds."""
+    require_gpu()
+    Hkv, D = 2, 64
+    lens = np.array([80, 37, 64, 21], np.int32)
+    npg = [-(-int(n) // bs) for n in lens]
+    P = sum(npg) + 3
+    perm = np.random.default_rng(bs).permutation(P).astype(np.int32)
+    table = np.full((len(lens), max(npg)), -1, np.int32)
+    o_ = 0
+    for b, n in enumerate(npg):
+        table[b, :n] = perm[o_:o_ + n]
+        o_ += n
+    in_dt = torch.bfloat16 if fmt == "bf16" else torch.float32
+    w = W.Workload("runs", P, bs, Hkv, D, 2 * Hkv, fmt, in_dt, in_dt, 0.125, table, lens, 0)
+    g = torch.Generator().manual_seed(bs)
+    # round 1 writes 48 / 16 / 32 / 5 rows from position 0, round 2 the rest
+    first = np.array([48, 16, 32, 5], np.int32)
+    rounds = []
+    for start, n in ((np.zeros(4, np.int32), first), (first, lens - first)):
+        cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        k = (torch.randn(int(cu[-1]), Hkv, D, generator=g) * 3).to(in_dt)
+        v = (torch.randn(int(cu[-1]), Hkv, D, generator=g) * 3).to(in_dt)
+        rounds.append(W.WriteRound(start.astype(np.int32), cu, k, v))
+    c, _ = _run_fill(w, rounds)
+    o = sentinel_oracle(w)
+    oracle_write_rounds(o, w, rounds)
+    K, V, KS, VS = pages_in_oracle_order(c)
+    assert np.array_equal(K, o.k), "K pages differ"
+    assert np.array_equal(V, o.v), "V pages differ"
+    if fmt == "int8":
+        assert np.array_equal(KS.view(np.uint32), o.k_scale.view(np.uint32))
+        assert np.array_equal(VS.view(np.uint32), o.v_scale.view(np.uint32))
+    assert c.status() == 0
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "int8"])
+@pytest.mark.parametrize("bs", [5, 16, 32])
+def test_write_ragged_starts_and_empty_sequences(fmt, bs):
+    """Forty sequences with seeded start positions and row counts (zero, one,
+    a few, a hundred) in one call: every position-aligned window of the
+    write, full or partly used, against the oracle bit for bit."""
+    require_gpu()
+    rng = np.random.default_rng(77 + bs)
+    Hkv, D, B = 2, 64, 40
+    start = rng.integers(0, 300, size=B).astype(np.int32)
+    n = rng.choice([0, 1, 2, 7, 15, 16, 17, 33, 100], size=B).astype(np.int32)
+    lens = start + n
+    npg = [-(-int(x) // bs) for x in lens]
+    P = sum(npg) + 2
+    perm = rng.permutation(P).astype(np.int32)
+    table = np.full((B, max(npg)), -1, np.int32)
+    o_ = 0
+    for b_, k_ in enumerate(npg):
+        table[b_, :k_] = perm[o_:o_ + k_]
+        o_ += k_
+    in_dt = torch.bfloat16 if fmt == "bf16" else torch.float32
+    w = W.Workload("ragged", P, bs, Hkv, D, 2 * Hkv, fmt, in_dt, in_dt, 0.125, table, lens, 0)
+    g = torch.Generator().manual_seed(bs)
+    cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    k = (torch.randn(int(cu[-1]), Hkv, D, generator=g) * 2).to(in_dt)
+    v = (torch.randn(int(cu[-1]), Hkv, D, generator=g) * 2).to(in_dt)
+    r = W.WriteRound(start, cu, k, v)
+    c, _ = _run_fill(w, [r])
+    o = sentinel_oracle(w)
+    oracle_write_rounds(o, w, [r])
+    K, V, KS, VS = pages_in_oracle_order(c)
+    assert np.array_equal(K, o.k), "K pages differ"
+    assert np.array_equal(V, o.v), "V pages differ"
+    if fmt == "int8":
+        assert np.array_equal(KS.view(np.uint32), o.k_scale.view(np.uint32))
+        assert np.array_equal(VS.view(np.uint32), o.v_scale.view(np.uint32))
+    assert c.status() == 0
+
+
+def test_int8_quotients_next_to_half_integers():
+    """Rows whose quotients x / scale sit a few float32 ulps either side of
+    k + 0.5 (and on it), for scales that are not powers of two: the codes
+    must follow the correctly rounded division exactly."""
+    require_gpu()
+    Hkv, D, bs = 1, 64, 16
+    rows = []
+    for mx in (100.0, 3.7, 0.011, 2.0e-30):
+        s = np.float32(np.float32(mx) / np.float32(127.0))
+        for j in range(4):
+            row = np.zeros(D, np.float32)
+            row[0] = np.float32(mx)
+            for i in range(1, D):
+                kk = (i * 7 + j * 13) % 126 - 63
+                x = np.float32(np.float32(kk + 0.5) * s)
+                row[i] = np.nextafter(x, np.float32(np.inf if (i + j) % 2 else -np.inf),
+                                      dtype=np.float32) if (i % 5) else x
+                for _ in range((i // 5) % 3):
+                    row[i] = np.nextafter(row[i], np.float32(np.inf), dtype=np.float32)
+            rows.append(row)
+    x = torch.from_numpy(np.stack(rows)).reshape(-1, Hkv, D)
+    n = x.shape[0]
+    table = np.arange(-(-n // bs), dtype=np.int32)[None]
+    w = W.Workload("ties", table.shape[1], bs, Hkv, D, Hkv, "int8", torch.float32, torch.float32,
+                   0.125, table, np.array([n], np.int32), 0)
+    r = W.WriteRound(np.array([0], np.int32), np.array([0, n], np.int32), x, -x)
+    c, _ = _run_fill(w, [r])
+    o = sentinel_oracle(w)
+    oracle_write_rounds(o, w, [r])
+    K, V, KS, VS = pages_in_oracle_order(c)
+    assert np.array_equal(K, o.k) and np.array_equal(V, o.v)
+    assert np.array_equal(KS.view(np.uint32), o.k_scale.view(np.uint32))
+
+
 # ------------------------------------------------------------------ gather --
 
 @pytest.mark.parametrize("name", NAMES)
@@ -299,6 +412,12 @@ def test_device_status_flags_without_fault():
     short = np.ascontiguousarray(w.tables[:, :2])
     c2.write(dev(short), dev(np.array([0, 0], np.int32)), dev(r.cu_new), r.k.cuda(), r.v.cuda())
     assert c2.status() & pkv.DEV_WRITE_TABLE
+    # decreasing row offsets: the malformed sequence is skipped and reported
+    c5 = make_cache(w)
+    badcu = np.array([0, 40, 30], np.int32)
+    c5.write(tdev, dev(r.start_pos), dev(badcu), r.k[:30].cuda(), r.v[:30].cuda())
+    torch.cuda.synchronize()
+    assert c5.status() & pkv.DEV_WRITE_ROWS
     # attention over a bad entry and a length past the bound
     c3, t3 = _run_fill(w)
     q = w.query().cuda()

@@ -42,7 +42,8 @@ from paged_kv_cache_207_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "paged decode attention KV GB/s (% of HBM peak) and decode tokens/s"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_split_long_bf16_traffic.json")
+# calibrated rocprofv3 traffic of the split pass, one file per workload
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_split_{}_traffic.json")
 # the split kernel and what decides its launch: its sources, its argument
 # struct and the split planner (the traffic counters are kept only while
 # these are unchanged)
@@ -154,9 +155,9 @@ def calibration_copy(device, nbytes=256 << 20) -> float:
     return 2 * nbytes / (e0.elapsed_time(e1) / 1e3) / 1e9
 
 
-def load_traffic():
+def load_traffic(workload: str):
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILE.format(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -652,7 +653,7 @@ def main():
     kvb = kv_bytes(w)
     value = kvb / (ms_per_step / 1e3) / 1e9
     achieved = split_kernel_bytes(w, not args.separate_write) / (split_avg / 1e3) / 1e9
-    traffic = load_traffic()
+    traffic = load_traffic(w.name)
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),

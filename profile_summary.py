@@ -1,15 +1,19 @@
 #!/usr/bin/env python3
 """Turn rocprofv3 CSV output into the short summaries kept in profiles/.
 
-    python profile_summary.py TAG TRACE_DIR [FETCH_DIR WRITE_DIR] --cmd "..." [--cmd "..."]
+    python profile_summary.py TAG TRACE_DIR [--fetch DIR --write DIR] [--util DIR]
+                              --cmd "..." [--cmd "..." ...]
 
 TRACE_DIR holds a `rocprofv3 --kernel-trace --stats --output-format csv -o trace`
-run (trace_kernel_stats.csv); FETCH_DIR and WRITE_DIR, when given, hold
-`--pmc FETCH_SIZE` (-o fetch) and `--pmc WRITE_SIZE` (-o write) runs of the
-same bench.py command.  Writes profiles/kernel_trace_TAG.md and, with the
-counter runs, profiles/hbm_traffic_TAG.md and the per-launch traffic of the
-split-K pass that bench.py reports (profiles/attend_split_TAG_traffic.json,
-tagged with the hash of the sources it was measured on).
+run (trace_kernel_stats.csv); --fetch and --write name `--pmc FETCH_SIZE`
+(-o fetch) and `--pmc WRITE_SIZE` (-o write) runs of the same bench.py
+command, --util a `--pmc VALUBusy MfmaUtil MemUnitStalled` run (-o util).  The
+--cmd lines are the commands, in that order.  Writes
+profiles/kernel_trace_TAG.md; with the counter runs also
+profiles/hbm_traffic_TAG.md and the per-launch traffic of the split-K pass
+that bench.py reports (profiles/attend_split_TAG_traffic.json, tagged with the
+hash of the sources it was measured on); with the utilisation run
+profiles/unit_busy_TAG.md.
 
 Counter calibration: the bench's plain copy of 256 MiB (probe_copy) reads and
 writes known byte counts; FETCH_SIZE and WRITE_SIZE are scaled by what they
@@ -54,12 +58,43 @@ def mean(xs):
     return sum(xs) / len(xs)
 
 
+def unit_busy(tag: str, util_dir: str, cmd: str) -> None:
+    """Per-kernel averages of rocprofv3's derived VALUBusy (VALU instruction
+    cycles over compute-unit cycles), MfmaUtil (matrix-core busy cycles over
+    SIMD cycles) and MemUnitStalled (texture-unit data-stall cycles over GPU
+    cycles and shader engines), in percent, for the dispatches of one run."""
+    path = os.path.join(util_dir, "util_counter_collection.csv")
+    agg: dict = {}
+    for r in csv.DictReader(open(path)):
+        agg.setdefault(short(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(
+            float(r["Counter_Value"]))
+    lines = [f"# Unit utilisation per kernel: {tag} (bench.py)", "",
+             "Command (from the repository root, on one MI355X):", "", "```", cmd, "```", "",
+             "rocprofv3 derived counters, averaged over the kernel's dispatches: VALUBusy = VALU "
+             "instruction cycles / (compute units x GPU cycles), MfmaUtil = matrix-core busy "
+             "cycles / (SIMDs x GPU cycles), MemUnitStalled = texture-unit data-stall cycles / (GPU "
+             "cycles x shader engines).", "",
+             "| kernel | dispatches | VALUBusy % | MfmaUtil % | MemUnitStalled % |",
+             "|---|---|---|---|---|"]
+    for k, c in agg.items():
+        if not k.startswith(("attend", "reduce", "write", "gather", "copy_pages", "probe")):
+            continue
+        n = max(len(v) for v in c.values())
+        vals = [f"{mean(c[x]):.1f}" if x in c else "-" for x in
+                ("VALUBusy", "MfmaUtil", "MemUnitStalled")]
+        lines.append(f"| {k} | {n} | " + " | ".join(vals) + " |")
+    out = os.path.join(ROOT, "profiles", f"unit_busy_{tag}.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(open(out).read())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("tag")
     ap.add_argument("trace_dir")
-    ap.add_argument("fetch_dir", nargs="?")
-    ap.add_argument("write_dir", nargs="?")
+    ap.add_argument("--fetch", dest="fetch_dir")
+    ap.add_argument("--write", dest="write_dir")
+    ap.add_argument("--util", dest="util_dir")
     ap.add_argument("--cmd", action="append", default=[], help="the command(s) that made the data")
     a = ap.parse_args()
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
@@ -75,6 +110,9 @@ def main():
     out = os.path.join(ROOT, "profiles", f"kernel_trace_{a.tag}.md")
     open(out, "w").write("\n".join(lines) + "\n")
     print(open(out).read())
+    cmds = a.cmd[1:]
+    if a.util_dir:
+        unit_busy(a.tag, a.util_dir, cmds[-1])
     if not a.fetch_dir:
         return
 
@@ -88,7 +126,7 @@ def main():
     w = bench.W.by_name(a.tag)
     alg = bench.split_kernel_bytes(w)
     lines = [f"# HBM traffic of the split-K attention pass: {a.tag}", "",
-             "Commands (from the repository root, on one MI355X):", "", "```", *a.cmd[1:3], "```",
+             "Commands (from the repository root, on one MI355X):", "", "```", *cmds[:2], "```",
              "",
              f"Calibration: a plain copy of {COPY_BYTES >> 20} MiB (probe_copy, reads and writes "
              f"{COPY_BYTES} bytes) reads FETCH_SIZE = {ff * COPY_BYTES / 1024:.0f} KiB and "

@@ -642,6 +642,18 @@ def main():
     torch.cuda.synchronize()
     cache.timing(False)
     kt_cold = kernel_times()
+
+    # (4) the same cold steps timed one by one with events on the stream (no
+    # library timing): median and minimum step time with flushed caches
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for ea, eb in evs:
+        pkv.probe_stream(sweep_buf, sink=sweep_sink)
+        ea.record()
+        step()
+        eb.record()
+    torch.cuda.synchronize()
+    cold_steps = sorted(ea.elapsed_time(eb) * 1e3 for ea, eb in evs)
     assert cache.status() == 0
     comb_avg, wr_avg = kt["attend_combine"], kt["write"]
     log(f"step: {ms_per_step * 1e3:.1f} us back to back (wall {wall_ms * 1e3:.1f} us); "
@@ -674,8 +686,11 @@ def main():
         "wall_ms_per_step": round(wall_ms, 5),
         "cold_cache": {"split_pass_us": round(kt_cold["attend_split"] * 1e3, 2),
                        "combine_us": round(kt_cold["attend_combine"] * 1e3, 2),
-                       "note": "kernel durations when each step follows a 512 MiB read-only "
-                               "sweep of the caches"},
+                       "step_us_median": round(float(np.median(cold_steps)), 2),
+                       "step_us_min": round(cold_steps[0], 2),
+                       "note": "each step follows a 512 MiB read-only sweep of the caches: "
+                               "kernel durations from the library's events, step median and "
+                               "minimum from events on the stream around each step"},
         "fill_write": fill_info,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -233,7 +233,7 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
       step_scores<FMT, D>(r, qf, sacc);
       const bool lane_live = BS == 16 && j >= 2 ? r.live_b : r.live_a;
       float ksc[8], vsc[8];  // int8: scales of tokens 8j .. 8j+7
-      if constexpr (FMT == PKV_FMT_INT8) step_scales<FMT, D>(r, j, ksc, vsc);
+      if constexpr (FMT == PKV_FMT_INT8) step_scales<FMT, D>(r, ksc, vsc);
       float sv[8];
       bool ok[8];  // token 8j + x of the step is real
       float mx = -INFINITY;
@@ -245,21 +245,21 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
         sv[x] = ok[x] ? y : -INFINITY;
         mx = fmaxf(mx, sv[x]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = rows_max(mx);
       const float m_new = fmaxf(m, mx);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m - m_use);
       float psum = 0.f;
-      bf16x8 pb;
+      float pw[8];
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const float p = ok[x] ? __builtin_amdgcn_exp2f(sv[x] - m_use) : 0.f;
         psum += p;
-        float pw = p;
-        if (FMT == PKV_FMT_INT8) pw = ok[x] ? p * vsc[x] : 0.f;
-        pb[x] = (__bf16)pw;
+        pw[x] = p;
+        if (FMT == PKV_FMT_INT8) pw[x] = ok[x] ? p * vsc[x] : 0.f;
       }
+      const bf16x8 pb = as_bf16x8(uint4{pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3]),
+                                        pack_bf16x2(pw[4], pw[5]), pack_bf16x2(pw[6], pw[7])});
       l = l * alpha + psum;
       m = m_new;
       uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
@@ -392,16 +392,18 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
           }
         }
       }
-      if (FMT == PKV_FMT_INT8) {
-        if (lane == x_new) r.sc = ks_new;
-        if (lane == 32 + x_new) r.sc = vs_new;
+      if (FMT == PKV_FMT_INT8) {  // scale lanes: see Step::sc
+        if (lane == 16 * j_new + (x_new & 7)) r.sc = ks_new;
+        if (lane == 16 * j_new + 8 + (x_new & 7)) r.sc = vs_new;
       }
     };
 
     // ---- two register sets, loads one step ahead.  The loop body issues its
     // prefetches unconditionally and the last one or two steps are peeled:
     // a load under a condition would make the compiler wait for every
-    // outstanding load (the prefetch included) before each step.
+    // outstanding load (the prefetch included) before each step.  (Three
+    // sets, two steps ahead, would keep more int8 bytes in flight, but do
+    // not fit the 256 registers a wave has at two waves per SIMD.)
     const int n_steps = (w_end - w0 + 31) / 32;
     auto T = [&](int i) { return w0 + 32 * i; };
     S r0, r1;
@@ -425,8 +427,7 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
   }
 
   // ---- results: O^T lane layout = dims 16*dt + 4j + i of head n ----
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  l = rows_sum(l);
   const int64_t hrow = (int64_t)b * a.n_q_heads + (int64_t)g * G + n;  // (b, h) row
   if (n_splits_b == 1) {
     // the only split of the sequence: normalise and write the output here

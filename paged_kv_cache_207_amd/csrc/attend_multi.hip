@@ -360,14 +360,14 @@ __global__ __launch_bounds__(kThreads, 2) void attend_multi_kernel(MultiArgs a) 
           mx = fmaxf(mx, sv[x]);
         }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = rows_max(mx);
       const float m_new = fmaxf(m[u], mx);
       // lazy rescale: the output only moves when some column's maximum grew
       const bool grow = __any(m_new > m[u]);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = grow ? __builtin_amdgcn_exp2f(m[u] - m_use) : 1.f;
       float psum = 0.f;
+      float pw[8];
       if (open) {
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
@@ -375,16 +375,18 @@ __global__ __launch_bounds__(kThreads, 2) void attend_multi_kernel(MultiArgs a) 
                                ? __builtin_amdgcn_exp2f(fmaf(sv[x], qs, -m_use))
                                : __builtin_amdgcn_exp2f(sv[x] - m_use);
           psum += pr;
-          pb[u][x] = (__bf16)(FMT == PKV_FMT_INT8 ? pr * vsc[x] : pr);
+          pw[x] = FMT == PKV_FMT_INT8 ? pr * vsc[x] : pr;
         }
       } else {
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           const float pr = ok[x] ? __builtin_amdgcn_exp2f(sv[x] - m_use) : 0.f;
           psum += pr;
-          pb[u][x] = (__bf16)(FMT == PKV_FMT_INT8 ? pr * vsc[x] : pr);
+          pw[x] = FMT == PKV_FMT_INT8 ? pr * vsc[x] : pr;
         }
       }
+      pb[u] = as_bf16x8(uint4{pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3]),
+                              pack_bf16x2(pw[4], pw[5]), pack_bf16x2(pw[6], pw[7])});
       l[u] = l[u] * alpha + psum;
       m[u] = m_new;
       if (grow) {

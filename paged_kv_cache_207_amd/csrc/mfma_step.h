@@ -22,7 +22,7 @@
 // bytes, set the pace: every K load covers 64 contiguous bytes of each row it
 // touches (int8 lanes load 16 codes at once, see kdim_of), and a step's 64
 // per-token int8 scales arrive in one 4-byte load per lane and are handed to
-// the lanes that need them by lane shuffles.
+// the lanes that need them by DPP row broadcasts.
 #pragma once
 
 #include <type_traits>
@@ -52,8 +52,9 @@ struct Step {
   using NVT = typename std::conditional<sizeof(VT) == 16, u32x4, u32x2>::type;
   KT k[2][NK];
   VT v[ND];
-  // int8 only: lane x < 32 holds the K scale of token x of the step, lane
-  // 32 + x its V scale; step_scales fetches the ones a lane needs
+  // int8 only: lane 16j + x holds the K scale (x < 8) or V scale (x >= 8) of
+  // token 8j + x % 8 of the step, so the 16-lane row j holds the scales of
+  // the tokens its k group uses; step_scales broadcasts them along the row
   float sc;
   bool live_a, live_b;  // the step's first / second 16 tokens sit on a valid page
 };
@@ -159,10 +160,10 @@ __device__ __forceinline__ void load_step(Step<FMT, D>& r, const PageSrc& s, int
   for (int dt = 0; dt < S::ND; ++dt)
     r.v[dt] = stream_load<typename S::VT, typename S::NVT>(vb + voff + 16 * dt * bs * ESZ);
   if (FMT == PKV_FMT_INT8) {
-    const int x = lane & 31;
+    const int x = 8 * j + (n & 7);  // token of this lane's scale
     const bool s_on_b = BS == 16 && x >= 16;
     const int slot = BS == 16 ? (x & 15) : slot0 + x;
-    const float* sb = lane < 32 ? s.ks : s.vs;
+    const float* sb = n < 8 ? s.ks : s.vs;
     r.sc = __builtin_nontemporal_load(sb + (s_on_b ? slab_b : slab_a) * bs + slot);
   }
 }
@@ -190,15 +191,26 @@ __device__ __forceinline__ void step_scores(const Step<FMT, D>& r, const bf16x8*
   }
 }
 
-// int8: the K and V scales of this lane's tokens 8j .. 8j+7.
+// int8: the K and V scales of this lane's tokens 8j .. 8j+7, broadcast
+// along the lane's 16-lane row (no LDS round trip).
 template <int FMT, int D>
-__device__ __forceinline__ void step_scales(const Step<FMT, D>& r, int j, float ksc[8],
-                                            float vsc[8]) {
-#pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    ksc[x] = __shfl(r.sc, 8 * j + x, 64);
-    vsc[x] = __shfl(r.sc, 32 + 8 * j + x, 64);
-  }
+__device__ __forceinline__ void step_scales(const Step<FMT, D>& r, float ksc[8], float vsc[8]) {
+  ksc[0] = row_bcast<0>(r.sc);
+  ksc[1] = row_bcast<1>(r.sc);
+  ksc[2] = row_bcast<2>(r.sc);
+  ksc[3] = row_bcast<3>(r.sc);
+  ksc[4] = row_bcast<4>(r.sc);
+  ksc[5] = row_bcast<5>(r.sc);
+  ksc[6] = row_bcast<6>(r.sc);
+  ksc[7] = row_bcast<7>(r.sc);
+  vsc[0] = row_bcast<8>(r.sc);
+  vsc[1] = row_bcast<9>(r.sc);
+  vsc[2] = row_bcast<10>(r.sc);
+  vsc[3] = row_bcast<11>(r.sc);
+  vsc[4] = row_bcast<12>(r.sc);
+  vsc[5] = row_bcast<13>(r.sc);
+  vsc[6] = row_bcast<14>(r.sc);
+  vsc[7] = row_bcast<15>(r.sc);
 }
 
 // O^T = alpha O^T + V^T P^T over the step.  pb holds the weights of this

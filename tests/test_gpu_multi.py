@@ -4,6 +4,8 @@ matrix-core kernel takes, bf16 and int8 pages, NaN-filled pools, page
 permutation, malformed chunk offsets, and the full-size workload."""
 from __future__ import annotations
 
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -62,7 +64,8 @@ def test_multi_query_parity(case):
     require_gpu()
     fmt, Hq, Hkv, D, bs, ctx, ch = case
     cp = W.chunked_prefill(batch=5, context=ctx, chunk=ch, n_q_heads=Hq, n_kv_heads=Hkv,
-                           head_dim=D, page_size=bs, kv_format=fmt, seed=hash(case) % 1000)
+                           head_dim=D, page_size=bs, kv_format=fmt,
+                           seed=zlib.crc32(repr(case).encode()) % 1000)
     say(f"multi {fmt} G={Hq // Hkv} D={D} bs={bs} ctx={cp.context} chunk={cp.chunk}")
     c, q, out = run(cp)
     ref = oracle_out(cp, q)

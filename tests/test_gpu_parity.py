@@ -9,6 +9,8 @@ ragged last page; the full-size workloads are checked on sampled sequences.
 """
 from __future__ import annotations
 
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -252,6 +254,57 @@ def test_attend_parity(name, split, flags):
     err = max_err(out, ref)
     say(f"  max err {err:.3e} (tol {TOL[w.kv_format]})")
     assert err <= TOL[w.kv_format]
+    assert c.status() == 0
+
+
+DECODE_SHAPES = [
+    # fmt, Hq, Hkv, D, bs: every group size class and page-size path of the
+    # matrix-core kernel (16- and 32-token pages and the general multiple of 32)
+    ("bf16", 8, 8, 128, 16),    # G = 1
+    ("bf16", 12, 4, 64, 32),    # G = 3
+    ("bf16", 32, 2, 128, 64),   # G = 16, 64-token pages
+    ("bf16", 16, 8, 64, 128),   # G = 2, 128-token pages
+    ("int8", 8, 8, 64, 16),     # G = 1
+    ("int8", 20, 4, 128, 64),   # G = 5
+    ("int8", 32, 2, 64, 32),    # G = 16
+]
+
+
+@pytest.mark.parametrize("case", DECODE_SHAPES,
+                         ids=lambda c: f"{c[0]}-G{c[1] // c[2]}-D{c[3]}-bs{c[4]}")
+def test_attend_group_and_page_shapes(case):
+    """Decode attention over seeded ragged lengths for group sizes 1 to 16,
+    head dims 64 and 128 and pages of 16, 32, 64 and 128 tokens, with the
+    planned split and with one-unit splits (many partials to combine)."""
+    require_gpu()
+    fmt, Hq, Hkv, D, bs = case
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    lens = rng.integers(1, 900, size=5).astype(np.int32)
+    lens[0] = 1
+    npg = [-(-int(n) // bs) for n in lens]
+    P = sum(npg) + 3
+    perm = rng.permutation(P).astype(np.int32)
+    tables = np.full((len(lens), max(npg)), -1, np.int32)
+    o_ = 0
+    for b, n in enumerate(npg):
+        tables[b, :n] = perm[o_:o_ + n]
+        o_ += n
+    w = W.Workload("shapes", P, bs, Hkv, D, Hq, fmt, torch.bfloat16, torch.bfloat16,
+                   float(np.float32(D ** -0.5)), tables, lens, 91)
+    say(f"decode {fmt} G={Hq // Hkv} D={D} bs={bs} lens={lens.tolist()}")
+    c = make_cache(w, sentinel=0xFF)
+    tdev = dev(w.tables)
+    gpu_write(c, tdev, w.rounds())
+    o = sentinel_oracle(w, 0xFF)
+    oracle_write_rounds(o, w, w.rounds())
+    q = w.query()
+    ref = attend(o, 0, np_bits(q), dtype_name(q), tables, lens, w.scale)
+    unit = int(64 // np.gcd(64, bs) * bs)
+    for split in (0, unit):
+        out = c.attend(q.cuda(), tdev, dev(lens), int(lens.max()), w.scale, split_tokens=split)
+        e = max_err(out, ref)
+        say(f"  split {split}: max err {e:.3e}")
+        assert e <= TOL[fmt], split
     assert c.status() == 0
 
 

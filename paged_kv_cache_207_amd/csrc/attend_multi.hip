@@ -233,18 +233,18 @@ __global__ __launch_bounds__(kThreads, 2) void attend_multi_kernel(MultiArgs a) 
     }
   };
   auto store_stage = [&](int ts, const Stage& st, char* buf) {
-    // token r of the step is dead past the block's range or on a missing page
+    // token r of the step is dead past the block's range or on a missing
+    // page; a whole step (the common case) is stored as it came
     const bool whole = ts + 32 <= t_end && st.page_a >= 0 && st.page_b >= 0;  // uniform
-    auto dead = [&](int r) {
-      return !whole && (ts + r >= t_end || (BS == 16 && r >= 16 ? st.page_b : st.page_a) < 0);
-    };
+    const int live_n = t_end - ts;  // tokens r < live_n are inside the range
+    auto page_dead = [&](int r) { return (BS == 16 && r >= 16 ? st.page_b : st.page_a) < 0; };
 #pragma unroll
     for (int i = 0; i < KL; ++i) {
       const int q = tid + i * kThreads;
       if (NKC % kThreads == 0 || q < NKC) {
         const int r = q / CK, c = q - r * CK;
         char* dst = buf + L::K_OFF + k_row(r) * L::KP + c * E * 2;
-        const bool z = dead(r);
+        const bool z = !whole && (r >= live_n || page_dead(r));
         if constexpr (FMT == PKV_FMT_BF16) {
           *reinterpret_cast<uint4*>(dst) = z ? uint4{0, 0, 0, 0} : st.kc[i];
         } else {
@@ -263,21 +263,28 @@ __global__ __launch_bounds__(kThreads, 2) void attend_multi_kernel(MultiArgs a) 
         const int d = q / CV, kk = q - d * CV;
         const int t0 = kk * E;
         char* dst = buf + L::V_OFF + d * L::VP + t0 * 2;
-        uint32_t dbits = 0;  // one bit per token of the chunk
-#pragma unroll
-        for (int e = 0; e < E; ++e) dbits |= (dead(t0 + e) ? 1u : 0u) << e;
+        // one bit per token of the chunk (its E tokens share one page half):
+        // all on a missing page, else those at or past the range's end
+        uint32_t dbits = 0;
+        if (!whole) {
+          const int keep = min(max(live_n - t0, 0), E);
+          dbits = page_dead(t0) ? (1u << E) - 1u : ((1u << E) - 1u) & ~((1u << keep) - 1u);
+        }
         if constexpr (FMT == PKV_FMT_BF16) {
-          *reinterpret_cast<uint4*>(dst) = zero_dead(st.vc[i], dbits);
+          *reinterpret_cast<uint4*>(dst) = whole ? st.vc[i] : zero_dead(st.vc[i], dbits);
         } else {
           uint4 lo, hi;
           codes16_to_bf16(st.vc[i], lo, hi);
-          *reinterpret_cast<uint4*>(dst) = zero_dead(lo, dbits & 0xffu);
-          *reinterpret_cast<uint4*>(dst + 16) = zero_dead(hi, dbits >> 8);
+          *reinterpret_cast<uint4*>(dst) = whole ? lo : zero_dead(lo, dbits & 0xffu);
+          *reinterpret_cast<uint4*>(dst + 16) = whole ? hi : zero_dead(hi, dbits >> 8);
         }
       }
     }
-    if (FMT == PKV_FMT_INT8 && tid < 64)
-      reinterpret_cast<float*>(buf + L::S_OFF)[tid] = dead(tid & 31) ? 0.f : st.sc;
+    if (FMT == PKV_FMT_INT8 && tid < 64) {
+      const int r = tid & 31;
+      reinterpret_cast<float*>(buf + L::S_OFF)[tid] =
+          !whole && (r >= live_n || page_dead(r)) ? 0.f : st.sc;
+    }
   };
 
   f32x4 o[kTiles][ND];

@@ -16,10 +16,12 @@
 // 16 matrix-core columns, each tile n_pos = 16 / G positions times the G
 // heads (mfma_step.h gives the tile layouts), every column with its own
 // causal bound, running maximum and sum.  Both tiles use the same K/V
-// operand registers, so each LDS read feeds two matrix-core operations.  The workgroup walks the tokens up to its last position in
-// 32-token steps: all 256 threads load the next step's K/V (and int8 scales)
-// from the pages into registers while the waves compute the current step
-// from LDS, then store it into the other LDS buffer (one barrier per step).
+// operand registers, so each LDS read feeds two matrix-core operations.
+// The workgroup walks the tokens up to its last position in blocks of two
+// 32-token steps: all 256 threads load the next block's K/V (and int8
+// scales) from the pages into registers while the waves compute the current
+// block's steps from LDS, then store it into the other pair of LDS buffers
+// (one barrier per block).
 // int8 codes are converted to bf16 once, on the way into LDS, and slots past
 // the range or on a missing page are stored as zeros, so every wave reads
 // plain bf16 operands.  Each byte read from the pages thus serves 128 query
@@ -47,7 +49,8 @@ constexpr int kXcds = 8;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTiles = 2;  // 16-column tiles per wave: both use the same K/V operands
-constexpr int kPageWin = 1024;  // page ids staged in LDS at a time
+constexpr int kPageWin = 512;  // page ids staged in LDS at a time
+constexpr int kHalves = 2;     // 32-token steps per staged block (one barrier each)
 
 template <int D>
 struct MultiLds {
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(kThreads, 2) void attend_multi_kernel(MultiArgs a) 
   constexpr int NVC = D * CV;                        // V chunks per step
   constexpr int KL = (NKC + kThreads - 1) / kThreads;
   constexpr int VL = (NVC + kThreads - 1) / kThreads;
-  __shared__ __align__(16) char lds[2 * L::BUF];
+  __shared__ __align__(16) char lds[2 * kHalves * L::BUF];
 
   const int tid = threadIdx.x;
   // wave-uniform values are made scalar so that branches on them are
@@ -181,9 +184,9 @@ __global__ __launch_bounds__(kThreads, 2) void attend_multi_kernel(MultiArgs a) 
   auto page_of = [&](int lp) {  // uniform; -1 past the range or on a bad entry
     return lp > pg_last ? -1 : __builtin_amdgcn_readfirstlane(pids[lp - win0]);
   };
-  // whether the window must move before the pages of logical page lp (and
-  // lp + 1) can be looked up
-  auto window_misses = [&](int lp) { return lp < win0 || lp + 1 >= win0 + kPageWin; };
+  // whether the window must move before the pages of logical pages lp ..
+  // lp + 4 (a staged block's) can be looked up
+  auto window_misses = [&](int lp) { return lp < win0 || lp + 4 >= win0 + kPageWin; };
 
   // ---- cooperative step load: registers, then LDS
   struct Stage {
@@ -419,23 +422,42 @@ __global__ __launch_bounds__(kThreads, 2) void attend_multi_kernel(MultiArgs a) 
   // would make every step wait for all outstanding loads.
   const int n_steps = (t_end + 31) / 32;
   if (n_steps > 0) {
+    // Blocks of kHalves 32-token steps are staged at a time, so one barrier,
+    // one round of page lookups and one load/store round serve 64 tokens.
+    // Halves past the last step load the last step again and are stored as
+    // dead slots (zeros) that no wave computes.
     const int ts_last = 32 * (n_steps - 1);
+    const int n_blocks = (n_steps + kHalves - 1) / kHalves;
+    auto at = [&](int ts) { return min(ts, ts_last); };
     stage_pages(0);
-    Stage st;
-    load_stage(0, st);
-    store_stage(0, st, lds);
-    bool la = st.page_a >= 0, lb = st.page_b >= 0;
+    Stage st[kHalves];
+    bool la[kHalves], lb[kHalves];
+#pragma unroll
+    for (int hf = 0; hf < kHalves; ++hf) {
+      load_stage(at(32 * hf), st[hf]);
+      store_stage(32 * hf, st[hf], lds + hf * L::BUF);
+      la[hf] = st[hf].page_a >= 0;
+      lb[hf] = st[hf].page_b >= 0;
+    }
     __syncthreads();
-    for (int i = 0; i < n_steps; ++i) {
-      const int ts = 32 * i;
-      const int ts1 = min(ts + 32, ts_last);
-      if (window_misses(ts1 / bs)) stage_pages(ts1 / bs);  // uniform, rare
-      load_stage(ts1, st);
-      if (ts <= w_last) compute_step(ts, lds + (i & 1) * L::BUF, la, lb);
-      if (i + 1 < n_steps) {
-        store_stage(ts + 32, st, lds + ((i + 1) & 1) * L::BUF);
-        la = st.page_a >= 0;
-        lb = st.page_b >= 0;
+    for (int i = 0; i < n_blocks; ++i) {
+      const int ts = 32 * kHalves * i;
+      const int ts1 = ts + 32 * kHalves;  // the next block
+      if (window_misses(at(ts1) / bs)) stage_pages(at(ts1) / bs);  // uniform, rare
+#pragma unroll
+      for (int hf = 0; hf < kHalves; ++hf) load_stage(at(ts1 + 32 * hf), st[hf]);
+      char* cur = lds + (i & 1) * kHalves * L::BUF;
+#pragma unroll
+      for (int hf = 0; hf < kHalves; ++hf)
+        if (ts + 32 * hf <= w_last) compute_step(ts + 32 * hf, cur + hf * L::BUF, la[hf], lb[hf]);
+      if (i + 1 < n_blocks) {
+        char* nxt = lds + ((i + 1) & 1) * kHalves * L::BUF;
+#pragma unroll
+        for (int hf = 0; hf < kHalves; ++hf) {
+          store_stage(ts1 + 32 * hf, st[hf], nxt + hf * L::BUF);
+          la[hf] = st[hf].page_a >= 0;
+          lb[hf] = st[hf].page_b >= 0;
+        }
       }
       __syncthreads();
     }

@@ -6,8 +6,11 @@
 // pages give their raw codes and per-(token, KV head) scales.
 //
 // One workgroup (one wave) copies 16 tokens of one KV head: K rows with
-// 16-byte vectors, V by reading the dim-major slab (consecutive lanes read
-// consecutive slots) through an LDS transpose.
+// 16-byte vectors; V through an LDS transpose.  When the 16 tokens are 16
+// consecutive slots of one page (page sizes that are multiples of 16, the
+// usual case), each dim's run of slots is read as 16-byte vectors and
+// scattered into token rows in LDS, which then go out as 16-byte vectors;
+// otherwise each slot's element is read on its own.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -18,12 +21,14 @@ constexpr int kTok = 16;
 
 template <int ESZ>
 __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
-  extern __shared__ uint32_t sv[];  // [kTok][D + 1] words
+  extern __shared__ __align__(16) char srow[];  // [kTok][D * ESZ + 16] bytes: token rows of V
   __shared__ int64_t slab_off[kTok];  // element offset of the slot's (page, head) slab, -1 = none
   __shared__ int slot_of[kTok];
-  const int D = a.head_dim, ld = D + 1;
+  const int D = a.head_dim;
+  const int pitch = D * ESZ + 16;
   const int lane = threadIdx.x, h = blockIdx.y;
   const int t0 = blockIdx.x * kTok;
+  const int n_tok = min(kTok, a.len - t0);
   if (lane < kTok) {
     int64_t off = -1;
     int slot = 0;
@@ -60,10 +65,30 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
       *reinterpret_cast<uint4*>(static_cast<char*>(a.k_out) + o * ESZ) = x;
     }
   }
-  // V: dim-major slab -> LDS [token][dim] -> output rows
-  {
-    const int r = lane & (kTok - 1);
-    for (int d = lane >> 4; d < D; d += 4) {
+  // V: dim-major slab -> LDS token rows -> output rows
+  const bool run = n_tok == kTok && a.page_size % kTok == 0 && slab_off[0] >= 0 &&
+                   slab_off[kTok - 1] == slab_off[0] && slot_of[0] % kTok == 0;  // uniform
+  if (run) {
+    constexpr int GS = 16 / ESZ;       // slots per 16-byte vector
+    constexpr int NGS = kTok / GS;     // vectors per dim
+    const char* vb = static_cast<const char*>(a.v_pages) +
+                     (slab_off[0] + slot_of[0]) * ESZ;
+    for (int task = lane; task < D * NGS; task += 64) {
+      const int d = task / NGS, g = task - d * NGS;
+      const uint4 x = *reinterpret_cast<const uint4*>(vb + ((int64_t)d * a.page_size + g * GS) * ESZ);
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int i = 0; i < GS; ++i) {
+        char* dst = srow + (g * GS + i) * pitch + d * ESZ;
+        const uint32_t word = w[(i * ESZ) >> 2];
+        if (ESZ == 4) *reinterpret_cast<uint32_t*>(dst) = word;
+        else if (ESZ == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(word >> (16 * (i & 1)));
+        else *reinterpret_cast<uint8_t*>(dst) = (uint8_t)(word >> (8 * (i & 3)));
+      }
+    }
+  } else {
+    for (int task = lane; task < kTok * D; task += 64) {
+      const int r = task & (kTok - 1), d = task / kTok;
       uint32_t w = 0;
       if (t0 + r < a.len && slab_off[r] >= 0) {
         const int64_t e = slab_off[r] + (int64_t)d * a.page_size + slot_of[r];
@@ -71,24 +96,20 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
         else if (ESZ == 2) w = static_cast<const uint16_t*>(a.v_pages)[e];
         else w = static_cast<const uint8_t*>(a.v_pages)[e];
       }
-      sv[r * ld + d] = w;
+      char* dst = srow + r * pitch + d * ESZ;
+      if (ESZ == 4) *reinterpret_cast<uint32_t*>(dst) = w;
+      else if (ESZ == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
+      else *reinterpret_cast<uint8_t*>(dst) = (uint8_t)w;
     }
   }
   __syncthreads();
   {
-    constexpr int EPW = 4 / ESZ;  // elements per 32-bit output word
-    const int wpr = D / EPW;
-    for (int wi = lane; wi < kTok * wpr; wi += 64) {
-      const int r = wi / wpr, d0 = (wi - r * wpr) * EPW;
-      const int t = t0 + r;
-      if (t >= a.len) continue;
-      const uint32_t* s = sv + r * ld + d0;
-      uint32_t w;
-      if (ESZ == 4) w = s[0];
-      else if (ESZ == 2) w = s[0] | (s[1] << 16);
-      else w = s[0] | (s[1] << 8) | (s[2] << 16) | (s[3] << 24);
-      const int64_t o = ((int64_t)t * a.n_kv_heads + h) * D + d0;
-      *reinterpret_cast<uint32_t*>(static_cast<char*>(a.v_out) + o * ESZ) = w;
+    const int vpr = D * ESZ / 16;  // 16-byte vectors per token row
+    for (int vi = lane; vi < n_tok * vpr; vi += 64) {
+      const int r = vi / vpr, c = vi - r * vpr;
+      const uint4 x = *reinterpret_cast<const uint4*>(srow + r * pitch + 16 * c);
+      const int64_t o = ((int64_t)(t0 + r) * a.n_kv_heads + h) * D * ESZ + 16 * c;
+      *reinterpret_cast<uint4*>(static_cast<char*>(a.v_out) + o) = x;
     }
   }
   // int8 scales
@@ -112,7 +133,7 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
 hipError_t launch_gather(const GatherArgs& a, int fmt, const Launch& l) {
   if (a.len <= 0) return hipSuccess;
   dim3 grid((a.len + kTok - 1) / kTok, a.n_kv_heads);
-  const size_t shm = kTok * (a.head_dim + 1) * sizeof(uint32_t);
+  const size_t shm = (size_t)kTok * (a.head_dim * format_bytes(fmt) + 16);
   if (fmt == PKV_FMT_F32) return launch1(gather_kernel<4>, grid, dim3(64), shm, l, a);
   if (fmt == PKV_FMT_BF16) return launch1(gather_kernel<2>, grid, dim3(64), shm, l, a);
   return launch1(gather_kernel<1>, grid, dim3(64), shm, l, a);

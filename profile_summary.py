@@ -7,7 +7,8 @@
 TRACE_DIR holds a `rocprofv3 --kernel-trace --stats --output-format csv -o trace`
 run (trace_kernel_stats.csv); --fetch and --write name `--pmc FETCH_SIZE`
 (-o fetch) and `--pmc WRITE_SIZE` (-o write) runs of the same bench.py
-command, --util a `--pmc VALUBusy MfmaUtil MemUnitStalled` run (-o util).  The
+command, --util a `--pmc VALUBusy MfmaUtil MemUnitStalled MeanOccupancyPerCU
+LDSBankConflict` run (-o util).  The
 --cmd lines are the commands, in that order.  Writes
 profiles/kernel_trace_TAG.md; with the counter runs also
 profiles/hbm_traffic_TAG.md and the per-launch traffic of the split-K pass
@@ -61,8 +62,10 @@ def mean(xs):
 def unit_busy(tag: str, util_dir: str, cmd: str) -> None:
     """Per-kernel averages of rocprofv3's derived VALUBusy (VALU instruction
     cycles over compute-unit cycles), MfmaUtil (matrix-core busy cycles over
-    SIMD cycles) and MemUnitStalled (texture-unit data-stall cycles over GPU
-    cycles and shader engines), in percent, for the dispatches of one run."""
+    SIMD cycles), MemUnitStalled (texture-unit data-stall cycles over GPU
+    cycles and shader engines), MeanOccupancyPerCU (resident waves per
+    compute unit) and LDSBankConflict (bank-conflict cycles over compute-unit
+    cycles, percent), for the dispatches of one run."""
     path = os.path.join(util_dir, "util_counter_collection.csv")
     agg: dict = {}
     for r in csv.DictReader(open(path)):
@@ -73,15 +76,19 @@ def unit_busy(tag: str, util_dir: str, cmd: str) -> None:
              "rocprofv3 derived counters, averaged over the kernel's dispatches: VALUBusy = VALU "
              "instruction cycles / (compute units x GPU cycles), MfmaUtil = matrix-core busy "
              "cycles / (SIMDs x GPU cycles), MemUnitStalled = texture-unit data-stall cycles / (GPU "
-             "cycles x shader engines).", "",
-             "| kernel | dispatches | VALUBusy % | MfmaUtil % | MemUnitStalled % |",
-             "|---|---|---|---|---|"]
+             "cycles x shader engines), MeanOccupancyPerCU = resident waves per compute unit "
+             "(time average), LDSBankConflict = LDS bank-conflict cycles / (compute units x GPU "
+             "cycles).", "",
+             "| kernel | dispatches | VALUBusy % | MfmaUtil % | MemUnitStalled % | waves per CU | "
+             "LDSBankConflict % |",
+             "|---|---|---|---|---|---|---|"]
     for k, c in agg.items():
         if not k.startswith(("attend", "reduce", "write", "gather", "copy_pages", "probe")):
             continue
         n = max(len(v) for v in c.values())
         vals = [f"{mean(c[x]):.1f}" if x in c else "-" for x in
-                ("VALUBusy", "MfmaUtil", "MemUnitStalled")]
+                ("VALUBusy", "MfmaUtil", "MemUnitStalled", "MeanOccupancyPerCU",
+                 "LDSBankConflict")]
         lines.append(f"| {k} | {n} | " + " | ".join(vals) + " |")
     out = os.path.join(ROOT, "profiles", f"unit_busy_{tag}.md")
     open(out, "w").write("\n".join(lines) + "\n")

@@ -383,9 +383,13 @@ def run_shared_prefix(args, device):
     split_ms, split_n = t["attend_split"]
     log(f"shared_prefix job: {job_s * 1e3:.3f} ms for {sp.n_steps} steps; split pass "
         f"{split_ms / split_n * 1e3:.1f} us avg; prefix page refcount {prefix_refs}")
+    # the job as a serving loop would drive it: each step's device work
+    # replayed from its captured graph (the eager job pays a Python launch
+    # cost per call on top, reported beside it)
     line = {
-        "metric": METRIC, "value": round(unique / job_s / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": jobs, "warmup": args.warmup, "ms_per_step": round(job_s * 1e3, 5),
+        "metric": METRIC, "value": round(unique / graph_job_s / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": jobs, "warmup": args.warmup,
+        "ms_per_step": round(graph_job_s * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "n_q_heads": w.n_q_heads,
@@ -394,13 +398,15 @@ def run_shared_prefix(args, device):
                    "step": f"one job = {sp.n_steps} decode steps (host table growth + "
                            "decode_step: paged_write 1 row/seq + paged_attend, one call)",
                    "split_tokens": split, "value_bytes": "unique KV bytes (shared prefix once)"},
-        "tokens_per_s": round(B * sp.n_steps / job_s, 1),
-        "logical_kv_GBps": round(logical / job_s / 1e9, 2),
-        "graph_replay": {"ms_per_job": round(graph_job_s * 1e3, 5),
-                         "GBps_unique": round(unique / graph_job_s / 1e9, 2),
-                         "note": "each step's table update + decode_step replayed from a HIP "
-                                 "graph captured once; host table growth per step"},
-        "pct_hbm_peak": round(100 * unique / job_s / 1e9 / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": round(B * sp.n_steps / graph_job_s, 1),
+        "logical_kv_GBps": round(logical / graph_job_s / 1e9, 2),
+        "job": "each step: host table growth (append_all, take_updates), then the step's "
+               "padded table update (H2D copy + table_apply) and decode_step replayed from a "
+               "HIP graph captured once",
+        "eager": {"ms_per_job": round(job_s * 1e3, 5),
+                  "GBps_unique": round(unique / job_s / 1e9, 2),
+                  "note": "the same job with every library call launched from Python"},
+        "pct_hbm_peak": round(100 * unique / graph_job_s / 1e9 / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": None, "traffic": None,
                      "avg_launch_us": round(split_ms / split_n * 1e3, 2),

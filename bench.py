@@ -123,7 +123,9 @@ def fill(w, cache, device):
     return table, [kv[b][0] for b in range(w.batch)], [kv[b][1] for b in range(w.batch)], info
 
 
-def read_probe(device, nbytes=1 << 30, reps=5) -> float:
+def read_probe(device, nbytes=4 << 30, reps=10) -> float:
+    """Achievable streaming-read rate: the probe kernel (16-byte non-temporal
+    loads, 32 768 workgroups) over 4 GiB, 10 launches back to back."""
     src = torch.empty(nbytes, dtype=torch.uint8, device=device)
     src.fill_(1)
     sink = torch.empty(pkv.lib().pkv_probe_blocks(nbytes), dtype=torch.float32, device=device)

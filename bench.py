@@ -457,15 +457,64 @@ def multi_layer_write(cp, device, kc, vc, start, cu_new, n_layers=32, reps=5):
     return out
 
 
-def run_chunked_prefill(args, device):
+def run_fork_copy(args, device, n_layers=32, n_forks=256):
+    """Copy-on-write page copies: after forks share every page, the first
+    append of each fork into the shared, partly filled last page copies that
+    page (every layer) to a fresh one.  One step = pkv_copy_pages of n_forks
+    (source, fresh page) pairs over a 32-layer bf16 store (Hkv 8, D 128, bs 16)."""
+    P, bs, Hkv, D = 4096, 16, 8, 128
+    cache = pkv.PagedKVCache(P, bs, Hkv, D, "bf16", n_layers, device=device)
+    cache.k_pages.fill_(3)
+    cache.v_pages.fill_(5)
+    rng = np.random.default_rng(9)
+    ids = rng.permutation(P)[:2 * n_forks].astype(np.int32)
+    pairs = torch.as_tensor(ids.reshape(n_forks, 2)).to(device)
+    for _ in range(args.warmup):
+        cache.copy_pages(pairs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        cache.copy_pages(pairs)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    cache.timing_read()
+    cache.timing(True)
+    for _ in range(args.steps):
+        cache.copy_pages(pairs)
+    cache.timing(False)
+    t = cache.timing_read()
+    k_ms = t["copy_pages"][0] / max(t["copy_pages"][1], 1)
+    assert cache.status() == 0
+    page_bytes = Hkv * bs * D * 2 * 2  # K and V slabs of one page of one layer
+    moved = 2 * n_forks * n_layers * page_bytes  # read + write
+    log(f"fork copy: {n_forks} pages x {n_layers} layers: {ms * 1e3:.1f} us per call, kernel "
+        f"{k_ms * 1e3:.1f} us = {moved / (k_ms / 1e3) / 1e9:.0f} GB/s read + write")
+    return {
+        "metric": "copy-on-write page copy GB/s (read + write)", "unit": "GB/s",
+        "value": round(moved / (ms / 1e3) / 1e9, 2), "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "fork_copy", "pairs": n_forks, "layers": n_layers,
+                   "n_kv_heads": Hkv, "head_dim": D, "page_size": bs},
+        "roofline": {"bound": "hbm", "achieved": round(moved / (k_ms / 1e3) / 1e9, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(moved / (k_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "kernel": "copy_pages", "avg_launch_us": round(k_ms * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+
+
+def run_chunked_prefill(args, device, kv_format="bf16"):
     """Several queries per sequence: each step writes every sequence's chunk
     of new rows (paged_write at position context[b]) and runs causal
     multi-query attention of the chunk over context + chunk tokens.  The
     context is written once before timing; each step rewrites the same chunk."""
-    cp = W.chunked_prefill()
+    cp = W.chunked_prefill(kv_format=kv_format)
     w = cp.base
     B = w.batch
-    log(f"workload chunked_prefill: B={B} context={cp.context.tolist()} "
+    log(f"workload chunked_prefill ({kv_format} pages): B={B} context={cp.context.tolist()} "
         f"chunk={cp.chunk.tolist()} Hq={w.n_q_heads} Hkv={w.n_kv_heads} D={w.head_dim} "
         f"bs={w.page_size}")
     cache = pkv.PagedKVCache(w.n_pages, w.page_size, w.n_kv_heads, w.head_dim, w.kv_format,
@@ -514,15 +563,17 @@ def run_chunked_prefill(args, device):
     tflops = flops / (attn_ms / 1e3) / 1e12
     log(f"chunked prefill step {ms_per_step * 1e3:.1f} us: write {wr_ms * 1e3:.1f} us, "
         f"multi-query attention {attn_ms * 1e3:.1f} us = {tflops:.1f} TFLOP/s")
-    layers_info = multi_layer_write(cp, device, kc, vc, start, cu_new)
-    log(f"multi-layer write: {layers_info}")
+    layers_info = multi_layer_write(cp, device, kc, vc, start, cu_new) if kv_format == "bf16" else None
+    if layers_info:
+        log(f"multi-layer write: {layers_info}")
     return {
         "metric": METRIC, "value": round(kvb / (ms_per_step / 1e3) / 1e9, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.kv_format, "data": "synthetic",
         "multi_layer_write": layers_info,
-        "config": {"workload": "chunked_prefill", "batch": B,
+        "config": {"workload": "chunked_prefill" + ("" if kv_format == "bf16" else "_" + kv_format),
+                   "pages": kv_format, "batch": B,
                    "context": cp.context.tolist(), "chunk": cp.chunk.tolist(),
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "page_size": w.page_size,
@@ -565,8 +616,12 @@ def main():
     if args.workload == "shared_prefix":
         print(json.dumps(run_shared_prefix(args, device)), flush=True)
         return
-    if args.workload == "chunked_prefill":
-        print(json.dumps(run_chunked_prefill(args, device)), flush=True)
+    if args.workload in ("chunked_prefill", "chunked_prefill_int8"):
+        fmt = "int8" if args.workload.endswith("int8") else "bf16"
+        print(json.dumps(run_chunked_prefill(args, device, fmt)), flush=True)
+        return
+    if args.workload == "fork_copy":
+        print(json.dumps(run_fork_copy(args, device)), flush=True)
         return
     w = W.by_name(args.workload)
     log(f"workload {w.name}: B={w.batch} lens={int(w.lens.min())}..{int(w.lens.max())} "

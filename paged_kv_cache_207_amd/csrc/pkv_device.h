@@ -59,16 +59,30 @@ __device__ __forceinline__ float row_bcast(float v) {
                                                     false));
 }
 
+// DPP move of lane values within 16-lane rows (dpp_ctrl C: 0xB1 and 0x4E
+// swap neighbours and pairs inside each group of 4, 0x141 mirrors each
+// half-row of 8, 0x140 each row of 16).
+template <int C>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), C, 0xf, 0xf, false));
+}
+
+// Max / sum over the whole wave, in every lane, without LDS: within rows by
+// DPP (pairs, quads, half-rows, rows), then across the four rows.
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+  x = fmaxf(x, dpp_mov<0xB1>(x));
+  x = fmaxf(x, dpp_mov<0x4E>(x));
+  x = fmaxf(x, dpp_mov<0x141>(x));
+  x = fmaxf(x, dpp_mov<0x140>(x));
+  return rows_max(x);
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  x += dpp_mov<0x141>(x);
+  x += dpp_mov<0x140>(x);
+  return rows_sum(x);
 }
 
 __device__ __forceinline__ void report(int32_t* status, uint32_t bit) {

@@ -14,9 +14,11 @@
 namespace pkv {
 namespace {
 
-// One wave per (sequence, query head).  The split weights 2^(m_s - M) / L
-// are computed once into LDS; then each lane owns pairs of dims and sums the
-// splits' partial outputs with 8 loads in flight.
+// One wave per (sequence, query head).  Up to 64 splits: one split per lane
+// for the weights 2^(m_s - M), which stay in registers, and each lane owns a
+// pair of dims, the first 8 splits' partial outputs loaded together with the
+// (m, l) pairs.  More splits: the weights go through LDS and each lane sums
+// the splits' partial outputs with 8 loads in flight.
 __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
   extern __shared__ float wsplit[];  // [n_split] weights
   const int lane = threadIdx.x;
@@ -29,6 +31,59 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
   if (a.single_done && n == 1) return;  // the split pass wrote this output
   const int64_t row0 = (int64_t)bh * a.n_split;
   const float* ml = a.ws_ml + row0 * 2;
+  const float* po = a.ws_o + row0 * D;
+  const int64_t oi0 = (int64_t)bh * D;
+
+  if (n <= 64) {
+    // one split per lane: the partial outputs of the first 8 splits are
+    // loaded together with the (m, l) pairs, and the weights stay in
+    // registers (read back per split with a lane read)
+    const int d2 = lane;  // dims 2 lane, 2 lane + 1
+    const bool has_d = 2 * d2 < D;
+    float2 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      x[u] = has_d && u < n ? *reinterpret_cast<const float2*>(po + (int64_t)u * D + 2 * d2)
+                            : float2{0.f, 0.f};
+    const float2 mlv = lane < n ? *reinterpret_cast<const float2*>(ml + 2 * lane)
+                                : float2{-INFINITY, 0.f};
+    const float M = wave_max(mlv.x);
+    const float w = lane < n ? exp2f(mlv.x - M) : 0.f;
+    const float L = wave_sum(w * mlv.y);
+    const float inv = n > 0 ? 1.f / L : 0.f;
+    float2 acc = {0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < n) {
+        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+        acc.x = fmaf(wu, x[u].x, acc.x);
+        acc.y = fmaf(wu, x[u].y, acc.y);
+      }
+    }
+    for (int s0 = 8; s0 < n; s0 += 8) {  // further splits, 8 loads in flight
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        x[u] = has_d && s0 + u < n
+                   ? *reinterpret_cast<const float2*>(po + (int64_t)(s0 + u) * D + 2 * d2)
+                   : float2{0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s0 + u));
+        acc.x = fmaf(ws, x[u].x, acc.x);
+        acc.y = fmaf(ws, x[u].y, acc.y);
+      }
+    }
+    if (has_d) {
+      const float r0 = acc.x * inv, r1 = acc.y * inv;
+      const int64_t oi = oi0 + 2 * d2;
+      if (a.q_bf16)
+        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + oi) =
+            f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
+      else
+        *reinterpret_cast<float2*>(static_cast<float*>(a.out) + oi) = float2{r0, r1};
+    }
+    return;
+  }
 
   float M = -INFINITY;
   for (int s = lane; s < n; s += 64) M = fmaxf(M, ml[2 * s]);
@@ -44,7 +99,6 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
   __syncthreads();
   const float inv = n > 0 ? 1.f / L : 0.f;
 
-  const float* po = a.ws_o + row0 * D;
   for (int d2 = lane; 2 * d2 < D; d2 += 64) {
     float2 acc = {0.f, 0.f};
     int s = 0;

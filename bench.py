@@ -594,7 +594,7 @@ def run_chunked_prefill(args, device, kv_format="bf16"):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_bf16")
     ap.add_argument("--split", type=int, default=0, help="split tokens (0 = library plan)")

@@ -46,7 +46,7 @@ namespace pkv {
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTiles = 2;  // 16-column tiles per wave: both use the same K/V operands
 constexpr int kPageWin = 512;  // page ids staged in LDS at a time
@@ -91,7 +91,7 @@ __device__ __forceinline__ uint4 zero_dead(uint4 v, uint32_t dead_bits) {
 }
 
 template <int FMT, int D, int BS>
-__global__ __launch_bounds__(kThreads, 2) void attend_multi_kernel(MultiArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) {
   using L = MultiLds<D>;
   constexpr int NC = D / 32, ND = D / 16;
   constexpr int ESZ = FMT == PKV_FMT_BF16 ? 2 : 1;  // page element bytes

@@ -11,20 +11,20 @@
 // decode rule of tiny-llm paged_kv.py when T_b = 1.  A position below 0 sees
 // nothing and gives zeros.
 //
-// How, on gfx950.  A workgroup of 4 waves owns one (sequence, KV head) and
-// 8 * n_pos consecutive positions of its chunk; each wave holds two tiles of
-// 16 matrix-core columns, each tile n_pos = 16 / G positions times the G
-// heads (mfma_step.h gives the tile layouts), every column with its own
-// causal bound, running maximum and sum.  Both tiles use the same K/V
-// operand registers, so each LDS read feeds two matrix-core operations.
-// The workgroup walks the tokens up to its last position in blocks of two
-// 32-token steps: all 256 threads load the next block's K/V (and int8
-// scales) from the pages into registers while the waves compute the current
-// block's steps from LDS, then store it into the other pair of LDS buffers
-// (one barrier per block).
+// How, on gfx950.  A workgroup of 8 waves (one per compute unit) owns one
+// (sequence, KV head) and 16 * n_pos consecutive positions of its chunk;
+// each wave holds two tiles of 16 matrix-core columns, each tile n_pos =
+// 16 / G positions times the G heads (mfma_step.h gives the tile layouts),
+// every column with its own causal bound, running maximum and sum.  Both
+// tiles use the same K/V operand registers, so each LDS read feeds two
+// matrix-core operations.  The workgroup walks the tokens up to its last
+// position in blocks of four 32-token steps: all 512 threads load the next
+// block's K/V (and int8 scales) from the pages into registers while the
+// waves compute the current block's steps from LDS, then store it into the
+// other set of LDS buffers (one barrier per 128 tokens).
 // int8 codes are converted to bf16 once, on the way into LDS, and slots past
 // the range or on a missing page are stored as zeros, so every wave reads
-// plain bf16 operands.  Each byte read from the pages thus serves 128 query
+// plain bf16 operands.  Each byte read from the pages thus serves 256 query
 // columns; there is no split of the token range, the parallelism comes from
 // the queries.  Steps that every column of a wave sees whole skip the
 // per-token masks, and the output is rescaled only when some column's
@@ -50,7 +50,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTiles = 2;  // 16-column tiles per wave: both use the same K/V operands
 constexpr int kPageWin = 512;  // page ids staged in LDS at a time
-constexpr int kHalves = 2;     // 32-token steps per staged block (one barrier each)
+constexpr int kHalves = 4;     // 32-token steps per staged block (one barrier each)
 
 template <int D>
 struct MultiLds {
@@ -184,9 +184,11 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
   auto page_of = [&](int lp) {  // uniform; -1 past the range or on a bad entry
     return lp > pg_last ? -1 : __builtin_amdgcn_readfirstlane(pids[lp - win0]);
   };
-  // whether the window must move before the pages of logical pages lp ..
-  // lp + 4 (a staged block's) can be looked up
-  auto window_misses = [&](int lp) { return lp < win0 || lp + 4 >= win0 + kPageWin; };
+  // whether the window must move before the pages of a staged block
+  // (logical pages lp .. lp + 2 kHalves at most) can be looked up
+  auto window_misses = [&](int lp) {
+    return lp < win0 || lp + 2 * kHalves + 1 >= win0 + kPageWin;
+  };
 
   // ---- cooperative step load: registers, then LDS
   struct Stage {

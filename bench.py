@@ -51,7 +51,9 @@ KERNEL_SOURCES = ["paged_kv_cache_207_amd/csrc/attend_mfma.hip",
                   "paged_kv_cache_207_amd/csrc/mfma_step.h",
                   "paged_kv_cache_207_amd/csrc/pkv_device.h"]
 KERNEL_PARTS = [("paged_kv_cache_207_amd/csrc/pkv_internal.h", "struct AttendArgs {", "};"),
-                ("paged_kv_cache_207_amd/csrc/pkv_host.hip", "int plan_split(", "\n}\n")]
+                ("paged_kv_cache_207_amd/csrc/pkv_host.hip", "int plan_split(", "\n}\n"),
+                ("paged_kv_cache_207_amd/csrc/pkv_host.hip", "constexpr int kMaxBalWavesPerCu",
+                 "\n\n")]
 
 
 def log(msg: str) -> None:
@@ -69,6 +71,17 @@ def kernel_hash() -> str:
         i = text.index(start)
         h.update(text[i:text.index(end, i) + len(end)].encode())
     return h.hexdigest()[:16]
+
+
+def schedule_name(cache, w, max_len: int, split: int) -> str:
+    """How the decode pass divides its work: the library plans bf16 pages on
+    the matrix-core path with the balanced schedule (equal shares of all
+    sequences' steps per wave) and other formats with fixed splits."""
+    if split:
+        return f"fixed splits of {split} tokens"
+    if w.kv_format == "bf16":
+        return "balanced (equal shares of the batch's 32-token steps per wave)"
+    return f"fixed splits of {cache.split_for(w.batch, w.n_q_heads, max_len)} tokens (planned)"
 
 
 def kv_bytes(w) -> int:
@@ -283,7 +296,7 @@ def run_shared_prefix(args, device):
     lens_all = torch.stack([torch.as_tensor(sp.step_lens(s)) for s in range(sp.n_steps)]).to(device)
     start_all = (lens_all - 1).contiguous()
     max_len = int(sp.step_lens(sp.n_steps - 1).max())
-    split = cache.split_for(B, w.n_q_heads, max_len)
+    split = 0  # the library's plan
     ws = cache.workspace(B, w.n_q_heads, max_len, split)
     out = torch.empty_like(qs[0])
     # one pinned buffer per step: a step's host-to-device copy may still be
@@ -399,7 +412,8 @@ def run_shared_prefix(args, device):
                    "prefix_pages": sp.prefix_pages, "suffix": "uniform [16, 2048]",
                    "step": f"one job = {sp.n_steps} decode steps (host table growth + "
                            "decode_step: paged_write 1 row/seq + paged_attend, one call)",
-                   "split_tokens": split, "value_bytes": "unique KV bytes (shared prefix once)"},
+                   "split_tokens": split, "schedule": schedule_name(cache, w, max_len, split),
+                   "value_bytes": "unique KV bytes (shared prefix once)"},
         "tokens_per_s": round(B * sp.n_steps / graph_job_s, 1),
         "logical_kv_GBps": round(logical / graph_job_s / 1e9, 2),
         "job": "each step: host table growth (append_all, take_updates), then the step's "
@@ -648,7 +662,8 @@ def main():
     q = q_host.to(device)
     out = torch.empty_like(q)
     max_len = w.max_len
-    split = args.split or cache.split_for(B, w.n_q_heads, max_len)
+    split = args.split  # 0: the library's plan
+    schedule = schedule_name(cache, w, max_len, split)
     ws = cache.workspace(B, w.n_q_heads, max_len, split)
     sweep_buf = torch.empty(512 << 20, dtype=torch.uint8, device=device)
     sweep_buf.fill_(7)
@@ -723,7 +738,7 @@ def main():
         f"split pass {split_avg * 1e3:.1f} us, combine {comb_avg * 1e3:.1f} us, write "
         f"{wr_avg * 1e3:.1f} us; after a cache sweep: split pass "
         f"{kt_cold['attend_split'] * 1e3:.1f} us, combine "
-        f"{kt_cold['attend_combine'] * 1e3:.1f} us; split_tokens={split}")
+        f"{kt_cold['attend_combine'] * 1e3:.1f} us; {schedule}")
 
     kvb = kv_bytes(w)
     value = kvb / (ms_per_step / 1e3) / 1e9
@@ -740,7 +755,7 @@ def main():
                    "table": "seeded random permutation of the pool",
                    "step": ("paged_write 1 row/seq + paged_attend" if args.separate_write else
                             "decode_step: paged_write 1 row/seq + paged_attend, one call"),
-                   "split_tokens": split},
+                   "split_tokens": split, "schedule": schedule},
         "tokens_per_s": round(B / (ms_per_step / 1e3), 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "kv_bytes_per_step": kvb,

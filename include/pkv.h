@@ -149,15 +149,16 @@ int pkv_paged_write_layers(pkv_cache* cache, int32_t layer0, int32_t n_layers,
                            const void* k, const void* v, int32_t in_dtype, int32_t format,
                            void* stream);
 
-/* Split size (tokens per split-K partition) that pkv_paged_attend uses when
- * called with split_tokens = 0: 1024 tokens (2048 when max_len > 16384),
- * halved down to 256 while batch * n_kv_heads * splits < 512; rounded up to
- * a multiple of 64 and of page_size. */
+/* The planned split size (tokens per split-K partition): 1024 tokens (2048
+ * when max_len > 16384), halved down to 256 while batch * n_kv_heads *
+ * splits < 512; rounded up to a multiple of 64 and of page_size.
+ * pkv_paged_attend called with split_tokens = 0 uses it, except where it
+ * balances the work instead (see there). */
 int pkv_attend_split(const pkv_cache* cache, int32_t batch, int32_t n_q_heads, int32_t max_len,
                      int32_t* split_tokens);
 
 /* Workspace bytes pkv_paged_attend needs for these sizes (split_tokens 0 =
- * the automatic split). */
+ * the library's plan, either schedule). */
 int pkv_attend_workspace_size(const pkv_cache* cache, int32_t batch, int32_t n_q_heads,
                               int32_t max_len, int32_t split_tokens, uint64_t* bytes);
 
@@ -168,12 +169,23 @@ int pkv_attend_workspace_size(const pkv_cache* cache, int32_t batch, int32_t n_q
  * its per-token scale).  lens[b] counts every stored token, including one
  * written in the same step, and no other mask applies (tiny-llm paged_kv.py
  * begin_step masks positions <= the pre-step length).  lens[b] = 0 gives
- * zeros.  Work is split over tokens in partitions of split_tokens (0 =
- * automatic) and the partial results (running max, sum and weighted V) are
- * combined by a second kernel or, on the matrix-core path with
- * PKV_ATTEND_COMBINE_FUSED, by the workgroup that finishes a sequence's last
- * split (through counters in the workspace).  The result of a sequence
- * depends only on its own tokens, the split size and that choice.
+ * zeros.  Work is split over tokens and the partial results (running max,
+ * sum and weighted V) are combined by a second kernel or, on the matrix-core
+ * path with PKV_ATTEND_COMBINE_FUSED, by the workgroup that finishes a
+ * sequence's last split (through counters in the workspace).
+ *   split_tokens > 0: fixed partitions of that many tokens (a multiple of 64
+ *   and of page_size).  A sequence's result depends only on its own tokens,
+ *   the split size and the combine choice.
+ *   split_tokens = 0: the library's plan.  For bf16 pages on the
+ *   matrix-core path (without PKV_ATTEND_COMBINE_FUSED) this is the
+ *   balanced schedule: every (sequence, KV head) is a run of 32-token steps
+ *   plus a fixed set-up cost, and each wave of the persistent grid takes an
+ *   equal share of that flat space, so batches of uneven lengths keep every
+ *   wave busy to the end.  Pieces then start wherever the shares fall, so a
+ *   result depends (in its last bits) on every length of the batch; with the
+ *   same lengths it is reproducible bit for bit (page permutation and prefix
+ *   sharing included).  Elsewhere the planned split size of
+ *   pkv_attend_split.
  *   q          device [batch][n_q_heads][head_dim] of q_dtype; out has the
  *              same shape and dtype (bf16 rounded to nearest even).
  *   table      device int32 [batch][table_stride].

@@ -10,26 +10,40 @@
 // table[t / page_size], slot t % page_size; query heads outnumber KV heads
 // as in metrale_storage high_speed_swap/impl_more.rs attend_layer).
 //
-// How, on gfx950 (the step machinery is in mfma_step.h).  One wave owns one
-// (b, g, s); the query group is the N dimension of the matrix-core tiles
+// How, on gfx950 (the step machinery is in mfma_step.h).  One wave works on
+// one piece (b, g, token range) at a time; the query group is the N dimension of the matrix-core tiles
 // (16 columns; columns >= G hold zeros).  The loads of step i+1 are issued
 // before step i is computed.  int8 pages are converted to bf16 exactly
 // (|code| <= 127); the per-token K scale multiplies the score and the V
 // scale the weight.
 //
-// Work distribution: a persistent grid (as many single-wave workgroups as
-// the chip holds at once) walks a work list of (split, KV head) items built
-// in LDS from the lengths, full splits first.  A sequence that fits in one
-// split gets its output written directly.  For longer sequences either the
-// combine kernel merges the partials afterwards (the default), or, when the
-// caller asks for it (fuse_combine), the workgroup that finishes a
-// (sequence, KV head)'s last split merges them in the same launch.
+// Work distribution: a persistent grid of single-wave workgroups, under one
+// of two schedules built in LDS from the lengths.
+//   Fixed splits: a work list of (split, KV head) items, full splits first.
+//   A sequence that fits in one split gets its output written directly.  For
+//   longer sequences either the combine kernel merges the partials
+//   afterwards (the default), or, when the caller asks for it
+//   (fuse_combine), the workgroup that finishes a (sequence, KV head)'s last
+//   split merges them in the same launch.
+//   Balanced (BAL): each wave takes an equal share of the flat space of all
+//   (sequence, KV head) units' 32-token steps, every unit charged a set-up
+//   cost on top, and walks the pieces of units its share covers.  A unit
+//   covered by one piece gets its output written directly; otherwise its
+//   first piece records where the partials sit and the combine kernel merges
+//   them.  Waves then finish together however uneven the lengths are.  When
+//   every non-empty sequence has the same length the BAL kernel takes the
+//   fixed splits instead (they are balanced already).
 #include <algorithm>
+#include <climits>
 
 #include "mfma_step.h"
 
 namespace pkv {
 namespace {
+
+// Balanced schedule: at least this many steps per wave (fewer waves for
+// small calls, so their partials stay few).
+constexpr int kMinWaveSteps = 8;
 
 // Partials are exchanged between workgroups, which may sit on different XCDs
 // with separate L2 caches.  Writers store them as agent-scope relaxed atomics
@@ -82,8 +96,13 @@ __device__ __forceinline__ void combine_group(const AttendArgs& a, int b, int g,
   }
 }
 
-template <int FMT, int D, int BS>
-__global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
+// The piece loop of the split pass under one schedule (SB: balanced), after
+// the kernel has built the schedule's prefix sums and lengths in LDS.  Each
+// schedule gets its own copy, so the fixed-split copy carries none of the
+// balanced schedule's loop state.
+template <int FMT, int D, int BS, bool SB>
+__device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* fpre,
+                                           const int32_t* qpre, const int32_t* lens) {
   using S = Step<FMT, D>;
   using KT = typename S::KT;
   constexpr int NC = S::NC, ND = S::ND;
@@ -97,56 +116,6 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
   const int bs = BS ? BS : a.page_size;
   const int C = a.split_tokens;
   const int B = a.batch;
-
-  // ---- work list (LDS): exclusive prefix sums over the sequences of their
-  // full splits and of their partial last splits, and the clamped lengths.
-  // Work items are (split, KV head) pairs, full splits first, so the longest
-  // items are handed out first; each workgroup takes items blockIdx.x,
-  // blockIdx.x + gridDim.x, ...
-  extern __shared__ int32_t wl[];
-  int32_t* fpre = wl;            // [B + 1]
-  int32_t* qpre = wl + B + 1;    // [B + 1]
-  int32_t* lens = wl + 2 * B + 2;  // [B]
-  {
-    int carry_f = 0, carry_q = 0;
-    for (int b0 = 0; b0 < B; b0 += 256) {
-      int lv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int bb = b0 + 64 * u + lane;
-        lv[u] = bb < B ? a.lens[bb] : 0;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int bb = b0 + 64 * u + lane;
-        const int len = clamp_len(lv[u], a.max_len, blockIdx.x == 0 ? a.status : nullptr,
-                                  PKV_DEV_LEN);
-        const int f = bb < B ? len / C : 0;
-        const int q = bb < B && len % C != 0 ? 1 : 0;
-        int sf = f, sq = q;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int tf = __shfl_up(sf, o, 64), tq = __shfl_up(sq, o, 64);
-          if (lane >= o) {
-            sf += tf;
-            sq += tq;
-          }
-        }
-        if (bb < B) {
-          fpre[bb] = carry_f + sf - f;
-          qpre[bb] = carry_q + sq - q;
-          lens[bb] = len;
-        }
-        carry_f += __shfl(sf, 63, 64);
-        carry_q += __shfl(sq, 63, 64);
-      }
-    }
-    if (lane == 0) {
-      fpre[B] = carry_f;
-      qpre[B] = carry_q;
-    }
-  }
-  __syncthreads();
   const int n_full = fpre[B];
   const int n_items = (n_full + qpre[B]) * a.n_kv_heads;
 
@@ -157,11 +126,66 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
       store_out4(a.out, a.q_bf16, (int64_t)b * a.n_q_heads * D + 4 * i, f32x4{0.f, 0.f, 0.f, 0.f});
   }
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-  const int pair = item / a.n_kv_heads;
-  const int g = item - pair * a.n_kv_heads;
-  int b, sp;
-  {
+  // balanced schedule: this wave's slots [F, F1) of the T-slot flat space
+  int64_t T = 0, F = 0, F1 = 0;
+  int n_waves = 1;
+  if constexpr (SB) {
+    T = __builtin_amdgcn_readfirstlane(fpre[B]);
+    n_waves = (int)std::min<int64_t>(gridDim.x, std::max<int64_t>(1, (T + kMinWaveSteps - 1) / kMinWaveSteps));
+    if ((int)blockIdx.x < n_waves) {
+      F = (int64_t)blockIdx.x * T / n_waves;
+      F1 = ((int64_t)blockIdx.x + 1) * T / n_waves;
+    }
+  }
+  int item = blockIdx.x;
+
+  for (;;) {
+  // ---- the next piece: tokens [t_begin, t_end) of unit (b, g); `direct`
+  // when it is the unit's only piece (normalised output written here), else
+  // its partial goes to workspace rows row_base + n * row_step (n < G)
+  int b, g, t_begin, t_end, sp = 0, n_splits_b = 1;
+  bool direct, owns_new;
+  int64_t row_base;
+  int row_step;
+  if constexpr (SB) {
+    if (F >= F1) break;
+    int lo = 0, hi = B - 1;  // the sequence owning slot F (never an empty one)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (fpre[mid] <= F) lo = mid;
+      else hi = mid - 1;
+    }
+    b = __builtin_amdgcn_readfirstlane(lo);
+    const int len_b = __builtin_amdgcn_readfirstlane(lens[b]);
+    const int pre_b = __builtin_amdgcn_readfirstlane(fpre[b]);
+    const int steps = (len_b + 31) >> 5;
+    const int cu = steps + a.unit_cost;
+    g = (int)((F - pre_b) / cu);
+    const int64_t s_first = pre_b + (int64_t)g * cu + a.unit_cost;  // slot of step 0
+    const int64_t u_end = s_first + steps;
+    const int64_t p_lo = std::max(F, s_first), p_hi = std::min(F1, u_end);
+    F = u_end;
+    if (p_lo >= p_hi) continue;  // only set-up slots of this unit fall here
+    t_begin = (int)(p_lo - s_first) * 32;
+    t_end = std::min((int)(p_hi - s_first) * 32, len_b);
+    direct = p_lo == s_first && p_hi == u_end;
+    owns_new = a.k_new != nullptr && p_hi == u_end;
+    const int unit = b * a.n_kv_heads + g;
+    const int slot = unit + (int)blockIdx.x;  // strictly increasing along the flat space
+    row_base = (int64_t)slot * G;
+    row_step = 1;
+    if (p_lo == s_first && lane == 0) {
+      // the unit's first piece records where its pieces' partials sit: the
+      // waves from this one to the one holding the unit's last step (one
+      // piece: the output is written here and the combine skips the unit)
+      const int w_last = (int)((u_end * n_waves - 1) / T);
+      *reinterpret_cast<int2*>(a.ws_desc + 2 * unit) = int2{slot, w_last - (int)blockIdx.x + 1};
+    }
+  } else {
+    if (item >= n_items) break;
+    const int pair = item / a.n_kv_heads;
+    g = item - pair * a.n_kv_heads;
+    item += gridDim.x;
     // largest b whose prefix is <= the index: that sequence owns it
     const int32_t* pre = pair < n_full ? fpre : qpre;
     const int idx = pair < n_full ? pair : pair - n_full;
@@ -173,11 +197,17 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
     }
     b = lo;
     sp = pair < n_full ? idx - fpre[b] : fpre[b + 1] - fpre[b];
+    n_splits_b = (lens[b] + C - 1) / C;
+    t_begin = sp * C;
+    t_end = min(t_begin + C, lens[b]);
+    direct = n_splits_b == 1;
+    // decode step: the sequence's new row sits at position len - 1, in the
+    // last step of its last split (see substitute_new below)
+    owns_new = a.k_new != nullptr && sp == n_splits_b - 1;
+    row_base = ((int64_t)b * a.n_q_heads + (int64_t)g * G) * a.n_split + sp;
+    row_step = a.n_split;
   }
   const int len = lens[b];
-  const int n_splits_b = (len + C - 1) / C;
-  const int t_begin = sp * C;
-  const int t_end = min(t_begin + C, len);
 
   // ---- query group as the B operand of S^T = K Q^T (zeros past the group) ----
   bf16x8 qf[NC];
@@ -191,10 +221,7 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
   const int32_t* trow = a.table + (int64_t)b * a.table_stride;
   const int pg_last = (t_end - 1) / bs;
 
-  // ---- decode step: the sequence's new row sits at position len - 1, in
-  // the last step of its last split (see substitute_new below)
-  const bool owns_new = a.k_new != nullptr && sp == n_splits_b - 1;  // item-uniform
-  const int t_new = len - 1;
+  const int t_new = len - 1;  // decode step: the position of the new row
 
   f32x4 o[ND];
 #pragma unroll
@@ -204,10 +231,9 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
 
   // The split is walked in windows of at most 64 logical pages: one table
   // entry per lane, picked out with a lane read (uniform) per tile.
-  const int tokens_per_window = 64 * bs;
-  for (int w0 = t_begin; w0 < t_end; w0 += tokens_per_window) {
-    const int w_end = min(w0 + tokens_per_window, t_end);
+  for (int w0 = t_begin; w0 < t_end; w0 = (w0 / bs + 64) * bs) {
     const int pg0 = w0 / bs;
+    const int w_end = min((pg0 + 64) * bs, t_end);  // at most 64 pages, even from inside a page
     int vpage = -1;
     {
       const int lp = pg0 + lane;
@@ -429,8 +455,8 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
   // ---- results: O^T lane layout = dims 16*dt + 4j + i of head n ----
   l = rows_sum(l);
   const int64_t hrow = (int64_t)b * a.n_q_heads + (int64_t)g * G + n;  // (b, h) row
-  if (n_splits_b == 1) {
-    // the only split of the sequence: normalise and write the output here
+  if (direct) {
+    // the unit's only piece: normalise and write the output here
     if (n < G) {
       const float inv = 1.f / l;
 #pragma unroll
@@ -438,9 +464,9 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
         store_out4(a.out, a.q_bf16, hrow * D + 16 * dt + 4 * j, o[dt] * inv);
     }
   } else if (!a.fuse_combine) {
-    // one of several splits: leave the partial for the combine kernel
+    // one of several pieces: leave the partial for the combine kernel
     if (n < G) {
-      const int64_t row = hrow * a.n_split + sp;
+      const int64_t row = row_base + (int64_t)n * row_step;
       float* wo = a.ws_o + row * D + 4 * j;
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) *reinterpret_cast<f32x4*>(wo + 16 * dt) = o[dt];
@@ -474,7 +500,127 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
       if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  }  // work items
+  }  // pieces
+}
+
+template <int FMT, int D, int BS, bool BAL>
+__global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
+  using S = Step<FMT, D>;
+  using KT = typename S::KT;
+  constexpr int NC = S::NC, ND = S::ND;
+  constexpr int ESZ = FMT == PKV_FMT_BF16 ? 2 : 1;
+  constexpr int KPL = S::KPL;
+  auto kdim = [](int c, int jj) { return kdim_of<FMT>(c, jj); };
+  const int lane = threadIdx.x;
+  const int n = lane & 15;  // head column (B/C operands), row (A operands)
+  const int j = lane >> 4;  // k group (A/B operands), row quad (C operand)
+  const int G = a.group;
+  const int bs = BS ? BS : a.page_size;
+  const int C = a.split_tokens;
+  const int B = a.batch;
+
+  // ---- work list (LDS), one of two schedules.
+  // Fixed splits: exclusive prefix sums over the sequences of their full
+  // splits and of their partial last splits, and the clamped lengths.  Work
+  // items are (split, KV head) pairs, full splits first, so the longest items
+  // are handed out first; each workgroup takes items blockIdx.x,
+  // blockIdx.x + gridDim.x, ...
+  // Balanced (BAL): every (sequence, KV head) unit is a run of 32-token steps
+  // preceded by unit_cost set-up slots (its query, table and first loads
+  // start cold); fpre holds the exclusive prefix of the sequences' costs
+  // n_kv_heads * (steps + unit_cost).  Wave w takes the slots
+  // [w T / Wn, (w + 1) T / Wn) of that flat space, so every wave gets the
+  // same share of steps plus set-ups, whatever the spread of lengths.  A
+  // batch whose non-empty sequences all have one length is already balanced
+  // by fixed splits, which cut it along KV heads and split boundaries (the
+  // balanced cut measured slower there), so the BAL kernel takes the fixed
+  // schedule for it and records the choice for the combine kernel.
+  extern __shared__ int32_t wl[];
+  int32_t* fpre = wl;              // [B + 1]
+  int32_t* qpre = wl + B + 1;      // [B + 1]
+  int32_t* lens = wl + 2 * B + 2;  // [B]
+  // clamped lengths into LDS (one load round trip), with the shortest and
+  // longest non-empty ones
+  int lmin = INT_MAX, lmax = 0;
+  for (int b0 = 0; b0 < B; b0 += 256) {
+    int lv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int bb = b0 + 64 * u + lane;
+      lv[u] = bb < B ? a.lens[bb] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int bb = b0 + 64 * u + lane;
+      const int len = clamp_len(lv[u], a.max_len, blockIdx.x == 0 ? a.status : nullptr,
+                                PKV_DEV_LEN);
+      if (bb < B) {
+        lens[bb] = len;
+        if (len > 0) {
+          lmin = min(lmin, len);
+          lmax = max(lmax, len);
+        }
+      }
+    }
+  }
+  bool balanced = false;
+  if constexpr (BAL) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      lmin = min(lmin, __shfl_xor(lmin, o, 64));
+      lmax = max(lmax, __shfl_xor(lmax, o, 64));
+    }
+    balanced = __builtin_amdgcn_readfirstlane(lmin < lmax ? 1 : 0) != 0;
+    if (blockIdx.x == 0 && lane == 0) *a.ws_sched = balanced ? 1 : 0;
+  }
+  // exclusive prefix sums of the schedule's counts, from the LDS lengths
+  // (each lane reads back the entries it wrote)
+  {
+    int carry_f = 0, carry_q = 0;
+    for (int b0 = 0; b0 < B; b0 += 256) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int bb = b0 + 64 * u + lane;
+        const int len = bb < B ? lens[bb] : 0;
+        int f, q;
+        if (balanced) {
+          const int steps = (len + 31) >> 5;
+          f = bb < B && steps > 0 ? a.n_kv_heads * (steps + a.unit_cost) : 0;
+          q = 0;
+        } else {
+          f = bb < B ? len / C : 0;
+          q = bb < B && len % C != 0 ? 1 : 0;
+        }
+        int sf = f, sq = q;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int tf = __shfl_up(sf, o, 64), tq = __shfl_up(sq, o, 64);
+          if (lane >= o) {
+            sf += tf;
+            sq += tq;
+          }
+        }
+        if (bb < B) {
+          fpre[bb] = carry_f + sf - f;
+          qpre[bb] = carry_q + sq - q;
+        }
+        carry_f += __shfl(sf, 63, 64);
+        carry_q += __shfl(sq, 63, 64);
+      }
+    }
+    if (lane == 0) {
+      fpre[B] = carry_f;
+      qpre[B] = carry_q;
+    }
+  }
+  __syncthreads();
+  if constexpr (BAL) {
+    if (balanced) {
+      run_pieces<FMT, D, BS, true>(a, fpre, qpre, lens);
+      return;
+    }
+  }
+  run_pieces<FMT, D, BS, false>(a, fpre, qpre, lens);
 }
 
 // Persistent launch: as many workgroups as the chip holds at once for this
@@ -496,13 +642,19 @@ int resident_workgroups(K kernel, size_t lds) {
   return per_cu * cus;
 }
 
-template <int FMT, int D, int BS>
-hipError_t launch_bs(const AttendArgs& a, const Launch& l) {
-  auto kernel = attend_mfma_kernel<FMT, D, BS>;
+template <int FMT, int D, int BS, bool BAL>
+hipError_t launch_sched(const AttendArgs& a, const Launch& l) {
+  auto kernel = attend_mfma_kernel<FMT, D, BS, BAL>;
   const size_t lds = (size_t)(3 * a.batch + 2) * sizeof(int32_t);
-  const int64_t bound = (int64_t)a.n_kv_heads * a.batch * a.n_split;
+  const int64_t bound = BAL ? a.bal_waves : (int64_t)a.n_kv_heads * a.batch * a.n_split;
   const int64_t grid = std::min<int64_t>(bound, resident_workgroups(kernel, lds));
   return launch1(kernel, dim3((unsigned)std::max<int64_t>(grid, 1)), dim3(64), lds, l, a);
+}
+
+template <int FMT, int D, int BS>
+hipError_t launch_bs(const AttendArgs& a, const Launch& l) {
+  return a.bal_waves > 0 ? launch_sched<FMT, D, BS, true>(a, l)
+                         : launch_sched<FMT, D, BS, false>(a, l);
 }
 
 template <int FMT, int D>

@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <map>
 #include <new>
@@ -68,22 +69,62 @@ int check_split(const pkv_cache* c, int32_t split) {
 
 // Workspace: first a fixed region of split counters (one u32 per (sequence,
 // KV head) for up to kMaxMfmaBatch sequences x kMaxMfmaKvHeads heads), then
-// the split partials o [B][Hq][S][D] f32 and (m, l) [B][Hq][S][2] f32.  The
-// counters must be zero before the first call and every call leaves them
-// zero; their region does not move with the call's shape, so one zeroed
-// workspace serves calls of any batch, length bound or split size.
+// the partials o and (m, l) in f32, then the balanced schedule's record of
+// the schedule it took (one i32, in its own 256 bytes) and its unit records
+// (two i32 per (sequence, KV head)).  The partials region holds
+// either schedule's rows: [B][Hq][S] for fixed splits, [B Hkv + waves][G]
+// for the balanced one.  The counters must be zero before the first call
+// and every call leaves them zero; their region does not move with the
+// call's shape, so one zeroed workspace serves calls of any batch, length
+// bound or split size.
 constexpr uint64_t kCounterBytes = (uint64_t)pkv::kMaxMfmaBatch * pkv::kMaxMfmaKvHeads * 4;
 
+// Compute units of the current device (256 when it cannot be asked).
+int device_cus() {
+  static thread_local int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      cus = 256;
+  }
+  return cus;
+}
+
+// Balanced schedule: its wave bound per compute unit (0 = fixed splits) and
+// the set-up cost of a (sequence, KV head) unit, in 32-token steps.
+// Measured on one MI355X (split pass, µs, fixed splits -> balanced):
+// bf16 pages with uneven lengths (32 sequences of 512-4096 tokens)
+// 59.3 -> 54.7 at 4 waves per CU and a cost of 3 (1-8 and 3-5 waves per CU
+// within 2 µs of it, 8 waves per CU no gain); 8 x 32k tokens 165.3 -> 165.6
+// (the same partition as 2048-token splits).  int8 pages were never faster
+// balanced (94.3 fixed, 96.3 at best, and up to 150 with cheap set-ups):
+// their steps are short, and every extra cold start costs more than the
+// balance gains.
+constexpr int kMaxBalWavesPerCu = 4;
+int bal_waves_per_cu(int fmt) { return fmt == PKV_FMT_BF16 ? kMaxBalWavesPerCu : 0; }
+constexpr int kUnitCost = 3;
+
 struct WsLayout {
-  uint64_t o_off, ml_off, total;
+  uint64_t o_off, ml_off, sched_off, desc_off, total;
 };
 
-WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_split) {
+WsLayout ws_layout(const pkv_cache* c, int batch, int n_q_heads, int n_split) {
   WsLayout w;
-  const uint64_t rows = (uint64_t)batch * n_q_heads * n_split;
+  const int n_kv_heads = c->L.n_kv_heads, head_dim = c->L.head_dim;
+  const uint64_t rows_split = (uint64_t)batch * n_q_heads * n_split;
+  const uint64_t rows_bal =
+      bal_waves_per_cu(c->L.format) > 0
+          ? ((uint64_t)batch * n_kv_heads + (uint64_t)kMaxBalWavesPerCu * device_cus()) *
+                (n_q_heads / std::max(n_kv_heads, 1))
+          : 0;
+  const uint64_t rows = std::max(rows_split, rows_bal);
   w.o_off = kCounterBytes;
   w.ml_off = (w.o_off + rows * head_dim * sizeof(float) + 255) / 256 * 256;
-  w.total = w.ml_off + rows * 2 * sizeof(float);
+  w.sched_off = (w.ml_off + rows * 2 * sizeof(float) + 255) / 256 * 256;
+  w.desc_off = w.sched_off + 256;
+  w.total = w.desc_off + (uint64_t)batch * n_kv_heads * 2 * sizeof(int32_t);
   return w;
 }
 
@@ -281,7 +322,7 @@ int pkv_attend_workspace_size(const pkv_cache* c, int32_t batch, int32_t n_q_hea
   if (n_split > kMaxSplits)
     return fail(PKV_EINVAL, "%d splits of %d tokens exceed %d per sequence", n_split, split,
                 kMaxSplits);
-  *bytes = ws_layout(batch, n_q_heads, c->L.head_dim, n_split).total;
+  *bytes = ws_layout(c, batch, n_q_heads, n_split).total;
   return PKV_OK;
 }
 
@@ -324,7 +365,7 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
   if (n_split > kMaxSplits)
     return fail(PKV_EINVAL, "%d splits of %d tokens exceed %d per sequence", n_split, split,
                 kMaxSplits);
-  const WsLayout w = ws_layout(batch, n_q_heads, c->L.head_dim, n_split);
+  const WsLayout w = ws_layout(c, batch, n_q_heads, n_split);
   if (workspace_bytes < w.total)
     return fail(PKV_ENOMEM, "workspace holds %llu bytes, %llu needed",
                 (unsigned long long)workspace_bytes, (unsigned long long)w.total);
@@ -342,6 +383,10 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
   a.counters = static_cast<uint32_t*>(workspace);
   a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.o_off);
   a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.ml_off);
+  a.ws_desc = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + w.desc_off);
+  a.ws_sched = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + w.sched_off);
+  a.bal_waves = 0;
+  a.unit_cost = kUnitCost;
   a.layer_page0 = (int64_t)layer * c->L.n_pages;
   a.qk_scale_log2 = scale * pkv::kLog2eHost;
   a.n_pages = c->L.n_pages;
@@ -400,6 +445,15 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
   // either.
   a.fuse_combine = mfma && (flags & PKV_ATTEND_COMBINE_FUSED) != 0;
   a.single_done = mfma && max_len > 0;
+  // The balanced schedule where the library plans the work (split_tokens 0)
+  // on the matrix-core path for the page formats it pays off on, unless the
+  // in-kernel combine is asked for (it counts fixed splits); its flat slot
+  // count must fit 31 bits.
+  const int wpc = bal_waves_per_cu(c->L.format);
+  if (mfma && wpc > 0 && !a.fuse_combine && split_tokens == 0 &&
+      (int64_t)batch * c->L.n_kv_heads * ((max_len + 31) / 32 + kUnitCost) < (int64_t)INT32_MAX) {
+    a.bal_waves = wpc * device_cus();
+  }
   if (max_len > 0) {
     Timer tm(c, PKV_T_ATTEND_SPLIT, s);
     e = mfma ? pkv::launch_attend_mfma(a, c->L.format, tm.l)

@@ -57,6 +57,15 @@ struct AttendArgs {
   const int32_t* lens;
   float* ws_o;   // [batch][n_q_heads][n_split][head_dim] unnormalised partial outputs
   float* ws_ml;  // [batch][n_q_heads][n_split][2] running max (log2 units) and sum
+  // Balanced schedule (bal_waves > 0): partials are indexed by slot * group
+  // + head-in-group instead, where a piece's slot is (b * n_kv_heads + g) +
+  // its wave; ws_desc[2 u] and [2 u + 1] give unit u's first slot and its
+  // number of pieces (written by the split pass for units of 2+ pieces).
+  int32_t* ws_desc;
+  int32_t* ws_sched;  // balanced schedule requested: 1 if the split pass used it, 0 if it
+                      // took fixed splits (every non-empty length equal)
+  int32_t bal_waves;  // 0: fixed splits; else the balanced schedule's wave bound
+  int32_t unit_cost;  // balanced schedule: set-up cost of a unit, in steps
   uint32_t* counters;  // [batch][n_kv_heads] splits finished (zero between calls)
   const void* k_new;   // decode step: [batch][n_kv_heads][head_dim] bf16 rows at len - 1,
   const void* v_new;   // written and attended by the matrix-core kernel (null: none)

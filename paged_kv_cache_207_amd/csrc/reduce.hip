@@ -1,13 +1,16 @@
 // Split-K combine: merge the per-split partials (m_s, l_s, o_s) of each
 // (sequence, query head) into the attention output
 //   M = max_s m_s,  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
-// over the splits that hold tokens (ceil(len / split_tokens) of them), then
-// round to the output dtype.  A sequence with no tokens gives zeros.  This
+// over the splits that hold tokens (ceil(len / split_tokens) of them, or,
+// under the balanced schedule, the pieces the unit's first piece recorded),
+// then round to the output dtype.  A sequence with no tokens gives zeros.  This
 // is the finalize step that follows the tile accumulation in
 // metrale_storage high_speed_swap/impl_more.rs attend_layer.
 //
 // Also here: the block-table update kernel (tiny-llm paged_kv.py begin_step
 // writes newly allocated blocks into the device table by index).
+#include <algorithm>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -27,11 +30,30 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
   const int D = a.head_dim;
   int len = a.lens[b];
   len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
-  const int n = (len + a.split_tokens - 1) / a.split_tokens;
-  if (a.single_done && n == 1) return;  // the split pass wrote this output
-  const int64_t row0 = (int64_t)bh * a.n_split;
+  // partial s of this (sequence, query head) sits in workspace row
+  // row0 + s * rstep
+  int n;
+  int64_t row0;
+  int rstep;
+  if (a.bal_waves > 0 && *a.ws_sched) {
+    // balanced schedule: the unit's pieces, as its first piece recorded them
+    if (len == 0) return;  // the split pass wrote zeros
+    const int h = bh - b * a.n_q_heads;
+    const int unit = b * a.n_kv_heads + h / a.group;
+    const int2 d = *reinterpret_cast<const int2*>(a.ws_desc + 2 * unit);
+    n = d.y;
+    if (n <= 1) return;  // one piece: the split pass wrote this output
+    row0 = (int64_t)d.x * a.group + (h - (h / a.group) * a.group);
+    rstep = a.group;
+  } else {
+    n = (len + a.split_tokens - 1) / a.split_tokens;
+    if (a.single_done && n == 1) return;  // the split pass wrote this output
+    row0 = (int64_t)bh * a.n_split;
+    rstep = 1;
+  }
   const float* ml = a.ws_ml + row0 * 2;
   const float* po = a.ws_o + row0 * D;
+  const int64_t pstep = (int64_t)rstep * D;
   const int64_t oi0 = (int64_t)bh * D;
 
   if (n <= 64) {
@@ -43,9 +65,9 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
     float2 x[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      x[u] = has_d && u < n ? *reinterpret_cast<const float2*>(po + (int64_t)u * D + 2 * d2)
+      x[u] = has_d && u < n ? *reinterpret_cast<const float2*>(po + u * pstep + 2 * d2)
                             : float2{0.f, 0.f};
-    const float2 mlv = lane < n ? *reinterpret_cast<const float2*>(ml + 2 * lane)
+    const float2 mlv = lane < n ? *reinterpret_cast<const float2*>(ml + 2 * (int64_t)rstep * lane)
                                 : float2{-INFINITY, 0.f};
     const float M = wave_max(mlv.x);
     const float w = lane < n ? exp2f(mlv.x - M) : 0.f;
@@ -64,7 +86,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         x[u] = has_d && s0 + u < n
-                   ? *reinterpret_cast<const float2*>(po + (int64_t)(s0 + u) * D + 2 * d2)
+                   ? *reinterpret_cast<const float2*>(po + (s0 + u) * pstep + 2 * d2)
                    : float2{0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -86,11 +108,11 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
   }
 
   float M = -INFINITY;
-  for (int s = lane; s < n; s += 64) M = fmaxf(M, ml[2 * s]);
+  for (int s = lane; s < n; s += 64) M = fmaxf(M, ml[2 * (int64_t)rstep * s]);
   M = wave_max(M);
   float L = 0.f;
   for (int s = lane; s < n; s += 64) {
-    const float2 x = *reinterpret_cast<const float2*>(ml + 2 * s);
+    const float2 x = *reinterpret_cast<const float2*>(ml + 2 * (int64_t)rstep * s);
     const float w = exp2f(x.x - M);
     wsplit[s] = w;
     L = fmaf(w, x.y, L);
@@ -105,7 +127,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
     for (; s + 8 <= n; s += 8) {
       float2 x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const float2*>(po + (int64_t)(s + u) * D + 2 * d2);
+      for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const float2*>(po + (s + u) * pstep + 2 * d2);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         acc.x = fmaf(wsplit[s + u], x[u].x, acc.x);
@@ -113,7 +135,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
       }
     }
     for (; s < n; ++s) {
-      const float2 x = *reinterpret_cast<const float2*>(po + (int64_t)s * D + 2 * d2);
+      const float2 x = *reinterpret_cast<const float2*>(po + s * pstep + 2 * d2);
       acc.x = fmaf(wsplit[s], x.x, acc.x);
       acc.y = fmaf(wsplit[s], x.y, acc.y);
     }
@@ -140,8 +162,9 @@ __global__ void table_apply_kernel(int32_t* table, int32_t stride, int32_t batch
 
 hipError_t launch_reduce(const AttendArgs& a, const Launch& l) {
   if (a.batch <= 0) return hipSuccess;
+  const int max_n = a.bal_waves > 0 ? std::max(a.n_split, a.bal_waves) : a.n_split;
   return launch1(reduce_kernel, dim3(a.batch * a.n_q_heads), dim3(64),
-                 (size_t)a.n_split * sizeof(float), l, a);
+                 (size_t)max_n * sizeof(float), l, a);
 }
 
 hipError_t launch_table_apply(int32_t* table, int32_t stride, int32_t batch, const int32_t* upd,

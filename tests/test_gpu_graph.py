@@ -16,7 +16,10 @@ from tests.gpu_helpers import dev, gpu_write, require_gpu, say
 pytestmark = pytest.mark.gpu
 
 
-def test_decode_steps_replayed_from_graphs():
+@pytest.mark.parametrize("fixed_splits", [False, True], ids=["planned", "fixed_splits"])
+def test_decode_steps_replayed_from_graphs(fixed_splits):
+    """Both schedules: the library's plan (split_tokens 0) and fixed splits of
+    the planned size; the eager reference makes the same calls."""
     require_gpu()
     sp = W.shared_prefix(batch=12, prefix_pages=4, lo=5, hi=60, n_steps=6, n_q_heads=8,
                          n_kv_heads=2, head_dim=64)
@@ -44,54 +47,60 @@ def test_decode_steps_replayed_from_graphs():
 
     # eager reference: per step, host growth, device table updates, decode step
     pool, seqs, table, cache = setup()
+    split = cache.split_for(B, w.n_q_heads, max_len) if fixed_splits else 0
     ref = []
     for s in range(sp.n_steps):
         seqs.append_all(1)
         upd = seqs.take_updates()
         if upd.shape[0]:
             pkv.table_apply(table, upd.cuda())
-        ref.append(cache.decode_step(table, lens_all[s], max_len, ks[s], vs[s], qs[s], w.scale))
+        ref.append(cache.decode_step(table, lens_all[s], max_len, ks[s], vs[s], qs[s], w.scale,
+                                     split_tokens=split))
     torch.cuda.synchronize()
     ref = [r.clone() for r in ref]
     ref_table = table.clone()
 
     # graphs: one per step, over static buffers
     pool2, seqs2, table2, cache2 = setup()
-    split = cache2.split_for(B, w.n_q_heads, max_len)
     ws = cache2.workspace(B, w.n_q_heads, max_len, split)
     upd_host = [torch.full((cap, 3), -1, dtype=torch.int32).pin_memory() for _ in range(sp.n_steps)]
     upd_dev = torch.full((cap, 3), -1, dtype=torch.int32, device="cuda")
     outs = [torch.empty_like(qs[0]) for _ in range(sp.n_steps)]
     stream = torch.cuda.Stream()
     graphs = []
-    with torch.cuda.stream(stream):
-        for s in range(sp.n_steps):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                upd_dev.copy_(upd_host[s], non_blocking=True)
-                pkv.table_apply(table2, upd_dev)
-                cache2.decode_step(table2, lens_all[s], max_len, ks[s], vs[s], qs[s], w.scale,
-                                   out=outs[s], workspace=ws, split_tokens=split)
-            graphs.append(g)
-    torch.cuda.synchronize()
-    say(f"captured {len(graphs)} step graphs")
-
-    for s in range(sp.n_steps):
-        seqs2.append_all(1)
-        u = seqs2.take_updates()
-        assert u.shape[0] <= cap
-        upd_host[s].fill_(-1)
-        upd_host[s][:u.shape[0]] = u
-        graphs[s].replay()
+    try:
+        with torch.cuda.stream(stream):
+            for s in range(sp.n_steps):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    upd_dev.copy_(upd_host[s], non_blocking=True)
+                    pkv.table_apply(table2, upd_dev)
+                    cache2.decode_step(table2, lens_all[s], max_len, ks[s], vs[s], qs[s], w.scale,
+                                       out=outs[s], workspace=ws, split_tokens=split)
+                graphs.append(g)
         torch.cuda.synchronize()
-        assert torch.equal(outs[s], ref[s]), s
-    assert torch.equal(table2, ref_table)
-    # replays again, with eager work between them: the same outputs every time
-    for rep in range(3):
+        say(f"captured {len(graphs)} step graphs")
+
         for s in range(sp.n_steps):
-            scratch = torch.randn(1 << 16, device="cuda").sum()  # eager work
+            seqs2.append_all(1)
+            u = seqs2.take_updates()
+            assert u.shape[0] <= cap
+            upd_host[s].fill_(-1)
+            upd_host[s][:u.shape[0]] = u
             graphs[s].replay()
             torch.cuda.synchronize()
-            assert torch.equal(outs[s], ref[s]), (rep, s)
-            del scratch
-    assert cache2.status() == 0
+            assert torch.equal(outs[s], ref[s]), s
+        assert torch.equal(table2, ref_table)
+        # replays again, with eager work between them: the same outputs every time
+        for rep in range(3):
+            for s in range(sp.n_steps):
+                scratch = torch.randn(1 << 16, device="cuda").sum()  # eager work
+                graphs[s].replay()
+                torch.cuda.synchronize()
+                assert torch.equal(outs[s], ref[s]), (rep, s)
+                del scratch
+        assert cache2.status() == 0
+    finally:
+        # drop the graphs while the runtime is up, also when an assertion failed
+        torch.cuda.synchronize()
+        graphs.clear()

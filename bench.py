@@ -76,12 +76,15 @@ def kernel_hash() -> str:
 def schedule_name(cache, w, max_len: int, split: int) -> str:
     """How the decode pass divides its work: the library plans bf16 pages on
     the matrix-core path with the balanced schedule (equal shares of all
-    sequences' steps per wave) and other formats with fixed splits."""
+    sequences' steps per wave) unless every non-empty length is equal, and
+    other formats with fixed splits."""
     if split:
         return f"fixed splits of {split} tokens"
-    if w.kv_format == "bf16":
+    live = w.lens[w.lens > 0]
+    if w.kv_format == "bf16" and live.size and live.min() < live.max():
         return "balanced (equal shares of the batch's 32-token steps per wave)"
-    return f"fixed splits of {cache.split_for(w.batch, w.n_q_heads, max_len)} tokens (planned)"
+    why = "equal lengths" if w.kv_format == "bf16" else "planned"
+    return f"fixed splits of {cache.split_for(w.batch, w.n_q_heads, max_len)} tokens ({why})"
 
 
 def kv_bytes(w) -> int:

@@ -149,9 +149,10 @@ int pkv_paged_write_layers(pkv_cache* cache, int32_t layer0, int32_t n_layers,
                            const void* k, const void* v, int32_t in_dtype, int32_t format,
                            void* stream);
 
-/* The planned split size (tokens per split-K partition): 1024 tokens (2048
- * when max_len > 16384), halved down to 256 while batch * n_kv_heads *
- * splits < 512; rounded up to a multiple of 64 and of page_size.
+/* The planned split size (tokens per split-K partition): 1024 tokens (when
+ * max_len > 16384: 4096 for bf16 pages, 2048 for the others), halved down to
+ * 256 while batch * n_kv_heads * splits < 512; rounded up to a multiple of 64
+ * and of page_size.
  * pkv_paged_attend called with split_tokens = 0 uses it, except where it
  * balances the work instead (see there). */
 int pkv_attend_split(const pkv_cache* cache, int32_t batch, int32_t n_q_heads, int32_t max_len,

@@ -43,12 +43,14 @@ int64_t split_unit(int page_size) { return 64 / gcd64(64, page_size) * page_size
 
 int plan_split(const pkv_cache* c, int batch, int n_q_heads, int max_len) {
   // Measured on the matrix-core path (persistent grid, work list): long
-  // splits are best, 1024 tokens up to 16k-token bounds and 2048 beyond
-  // (fewer partials to combine; the work list keeps the chip busy).  Halve
-  // while the batch would give fewer than 512 (split, KV head) items, so a
-  // small batch still spreads over the compute units.
+  // splits are best, 1024 tokens up to 16k-token bounds; beyond, 4096 for
+  // bf16 pages (8 x 32k tokens: step 169.4-169.8 us against 170.9-172.7 with
+  // 2048 and 198-200 with 8192, alternating runs on one box) and 2048 for
+  // the others, whose shorter steps need more waves streaming.  Halve while
+  // the batch would give fewer than 512 (split, KV head) items, so a small
+  // batch still spreads over the compute units.
   const int64_t unit = split_unit(c->L.page_size);
-  int64_t split = max_len > 16384 ? 2048 : 1024;
+  int64_t split = max_len <= 16384 ? 1024 : c->L.format == PKV_FMT_BF16 ? 4096 : 2048;
   const int64_t heads = (int64_t)std::max(batch, 1) * c->L.n_kv_heads;
   while (split > 256 && heads * ((std::max(max_len, 1) + split - 1) / split) < 512) split /= 2;
   split = (split + unit - 1) / unit * unit;

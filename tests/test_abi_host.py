@@ -286,9 +286,10 @@ def test_attend_validation():
     assert a(batch=0) == pkv.OK
     st = C.c_int32()
     assert L.pkv_attend_split(h, 8, 64, 32768, C.byref(st)) == pkv.OK
-    # 2 KV heads: 8 sequences x 2 heads x 16 splits of 2048 < 512 items -> 1024
+    # bf16 pages, 2 KV heads: 8 sequences x 2 heads x 8 splits of 4096 (then
+    # 16 of 2048) < 512 items -> 1024
     assert st.value == 1024
-    assert L.pkv_attend_split(h, 128, 4, 32768, C.byref(st)) == pkv.OK and st.value == 2048
+    assert L.pkv_attend_split(h, 128, 4, 32768, C.byref(st)) == pkv.OK and st.value == 4096
     assert L.pkv_attend_split(h, 32, 4, 4096, C.byref(st)) == pkv.OK and st.value == 512
     assert L.pkv_attend_split(h, 1, 4, 4096, C.byref(st)) == pkv.OK and st.value == 256
     L.pkv_cache_destroy(h)

@@ -66,13 +66,15 @@ __device__ __forceinline__ T stream_load(const char* p) {
   return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const R*>(p)));
 }
 
-// 4 int8 codes -> 4 bf16 (exact: an integer of at most 7 bits plus sign)
+// 4 int8 codes -> 4 bf16 (exact: an integer of at most 7 bits plus sign, so
+// its bf16 is the upper half of its float).  One byte permute packs the
+// upper halves of two floats (bytes 2-3 of the first, then of the second).
 __device__ __forceinline__ uint2 codes_to_bf16(uint32_t w) {
   float f0 = (float)(int8_t)(w & 0xffu), f1 = (float)(int8_t)((w >> 8) & 0xffu);
   float f2 = (float)(int8_t)((w >> 16) & 0xffu), f3 = (float)(int8_t)(w >> 24);
   uint2 r;
-  r.x = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
-  r.y = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
+  r.x = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  r.y = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
   return r;
 }
 

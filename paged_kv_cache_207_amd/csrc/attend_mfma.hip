@@ -290,7 +290,13 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
       m = m_new;
       uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
       if (FMT == PKV_FMT_BF16 && (ts + 32 > w_end || !r.live_a || !r.live_b)) v_keep_masks(ok, keep);
-      step_pv<FMT, D>(r, pb, keep, alpha, o);
+      // the running outputs are rescaled only when some column's maximum
+      // grew (alpha = 1 leaves them as they are, bit for bit)
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) o[dt] *= alpha;
+      }
+      step_pv<FMT, D>(r, pb, keep, o);
     };
 
     // A fused decode step: the item that owns the sequence's last split loads

@@ -215,18 +215,18 @@ __device__ __forceinline__ void step_scales(const Step<FMT, D>& r, float ksc[8],
   vsc[7] = row_bcast<15>(r.sc);
 }
 
-// O^T = alpha O^T + V^T P^T over the step.  pb holds the weights of this
-// lane's tokens 8j .. 8j+7 for its column.  With bf16 pages, dead slots
+// O^T += V^T P^T over the step (the caller rescales O^T first when a
+// column's running maximum grew).  pb holds the weights of this lane's tokens
+// 8j .. 8j+7 for its column.  With bf16 pages, dead slots
 // (past the readable range or on a missing page) are zeroed through `keep`
 // (one mask per 32-bit word of the V operand) when mask_v is set: they may
 // hold NaN, and 0 * NaN would reach the sum.  int8 codes are finite and
 // carry weight 0 there.
 template <int FMT, int D>
 __device__ __forceinline__ void step_pv(const Step<FMT, D>& r, bf16x8 pb, const uint32_t keep[4],
-                                        float alpha, f32x4* o) {
+                                        f32x4* o) {
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
-    o[dt] *= alpha;
     uint4 va;
     if constexpr (FMT == PKV_FMT_BF16) {
       va = uint4{r.v[dt].x & keep[0], r.v[dt].y & keep[1], r.v[dt].z & keep[2],

@@ -293,6 +293,23 @@ def test_attend_validation():
     assert L.pkv_attend_split(h, 32, 4, 4096, C.byref(st)) == pkv.OK and st.value == 512
     assert L.pkv_attend_split(h, 1, 4, 4096, C.byref(st)) == pkv.OK and st.value == 256
     L.pkv_cache_destroy(h)
+    # int8 pages keep 2048-token splits beyond 16k tokens (their steps carry
+    # half the bytes, so more waves must stream); up to 16k both use 1024
+    L, h = _cache(fmt=pkv.FMT_INT8, Hkv=8, D=128, bs=32)
+    assert L.pkv_attend_split(h, 8, 64, 32768, C.byref(st)) == pkv.OK and st.value == 2048
+    assert L.pkv_attend_split(h, 64, 64, 16384, C.byref(st)) == pkv.OK and st.value == 1024
+    L.pkv_cache_destroy(h)
+    L, h = _cache(fmt=pkv.FMT_BF16, Hkv=8, D=128, bs=16)
+    assert L.pkv_attend_split(h, 8, 64, 32768, C.byref(st)) == pkv.OK and st.value == 4096
+    assert L.pkv_attend_split(h, 8, 64, 16384, C.byref(st)) == pkv.OK and st.value == 1024
+    # a bf16 workspace holds either schedule's partials: fixed splits need
+    # B * Hq * S rows, the balanced schedule (B * Hkv + 4 waves per CU) * G
+    # rows (256 CUs when no device can be asked), each D + 2 floats
+    need = C.c_uint64()
+    assert L.pkv_attend_workspace_size(h, 32, 32, 4096, 0, C.byref(need)) == pkv.OK
+    rows = max(32 * 32 * 4, (32 * 8 + 4 * 256) * 4)
+    assert need.value >= (1 << 20) + rows * (128 + 2) * 4 + 32 * 8 * 8
+    L.pkv_cache_destroy(h)
 
 
 def test_attend_multi_validation():

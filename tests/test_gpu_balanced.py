@@ -168,3 +168,35 @@ def test_balanced_decode_step_matches_write_then_attend():
         assert c.status() == 0
     assert torch.equal(outs[0], outs[1])
     assert torch.equal(pages[0][0], pages[1][0]) and torch.equal(pages[0][1], pages[1][1])
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "int8"])
+def test_many_sequences_scan_blocks(fmt):
+    """700 short sequences, some empty: the kernel's length scan runs over
+    LDS in blocks of 256 sequences with a carry between blocks, for the
+    balanced schedule (bf16) and fixed splits (int8)."""
+    require_gpu()
+    rng = np.random.default_rng(700)
+    lens = rng.integers(0, 90, size=700).astype(np.int32)
+    lens[::37] = 0
+    lens[5] = 400
+    bs = 16
+    npg = [-(-int(n) // bs) for n in lens]
+    P = sum(npg) + 4
+    perm = rng.permutation(P).astype(np.int32)
+    tables = np.full((len(lens), max(npg)), -1, np.int32)
+    o_ = 0
+    for b, n in enumerate(npg):
+        tables[b, :n] = perm[o_:o_ + n]
+        o_ += n
+    w = W.Workload("many", P, bs, 2, 64, 8, fmt, torch.bfloat16, torch.bfloat16,
+                   float(np.float32(64 ** -0.5)), tables, lens, 77)
+    c, tdev, o = _filled(w)
+    q = w.query()
+    ref = attend(o, 0, np_bits(q), dtype_name(q), w.tables, w.lens, w.scale)
+    out = c.attend(q.cuda(), tdev, dev(w.lens), w.max_len, w.scale)
+    e = max_err(out, ref)
+    say(f"700 sequences ({fmt}): max err {e:.3e}")
+    assert e <= TOL[fmt]
+    assert not out[np.flatnonzero(w.lens == 0)].float().abs().any()
+    assert c.status() == 0

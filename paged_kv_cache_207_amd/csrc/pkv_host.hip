@@ -45,7 +45,7 @@ int plan_split(const pkv_cache* c, int batch, int n_q_heads, int max_len) {
   // Measured on the matrix-core path (persistent grid, work list): long
   // splits are best, 1024 tokens up to 16k-token bounds; beyond, 4096 for
   // bf16 pages (8 x 32k tokens: step 169.4-169.8 us against 170.9-172.7 with
-  // 2048 and 198-200 with 8192, alternating runs on one box) and 2048 for
+  // 2048 and 198-200 with 8192, alternating runs on one MI355X) and 2048 for
   // the others, whose shorter steps need more waves streaming.  Halve while
   // the batch would give fewer than 512 (split, KV head) items, so a small
   // batch still spreads over the compute units.

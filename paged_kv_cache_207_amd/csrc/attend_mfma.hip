@@ -11,8 +11,8 @@
 // as in metrale_storage high_speed_swap/impl_more.rs attend_layer).
 //
 // How, on gfx950 (the step machinery is in mfma_step.h).  One wave works on
-// one piece (b, g, token range) at a time; the query group is the N dimension of the matrix-core tiles
-// (16 columns; columns >= G hold zeros).  The loads of step i+1 are issued
+// one piece (b, g, token range) at a time; the query group is the N
+// dimension of the matrix-core tiles (16 columns; columns >= G hold zeros).  The loads of step i+1 are issued
 // before step i is computed.  int8 pages are converted to bf16 exactly
 // (|code| <= 127); the per-token K scale multiplies the score and the V
 // scale the weight.
@@ -131,7 +131,8 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
   int n_waves = 1;
   if constexpr (SB) {
     T = __builtin_amdgcn_readfirstlane(fpre[B]);
-    n_waves = (int)std::min<int64_t>(gridDim.x, std::max<int64_t>(1, (T + kMinWaveSteps - 1) / kMinWaveSteps));
+    const int64_t want = std::max<int64_t>(1, (T + kMinWaveSteps - 1) / kMinWaveSteps);
+    n_waves = (int)std::min<int64_t>(gridDim.x, want);
     if ((int)blockIdx.x < n_waves) {
       F = (int64_t)blockIdx.x * T / n_waves;
       F1 = ((int64_t)blockIdx.x + 1) * T / n_waves;

@@ -127,7 +127,8 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
     for (; s + 8 <= n; s += 8) {
       float2 x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const float2*>(po + (s + u) * pstep + 2 * d2);
+      for (int u = 0; u < 8; ++u)
+        x[u] = *reinterpret_cast<const float2*>(po + (s + u) * pstep + 2 * d2);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         acc.x = fmaf(wsplit[s + u], x[u].x, acc.x);

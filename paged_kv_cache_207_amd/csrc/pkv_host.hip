@@ -450,9 +450,10 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
   // The balanced schedule where the library plans the work (split_tokens 0)
   // on the matrix-core path for the page formats it pays off on, unless the
   // in-kernel combine is asked for (it counts fixed splits); its flat slot
-  // count must fit 31 bits.
+  // count must fit 31 bits.  Not for max_len 0: no split pass runs then to
+  // record its choice, and the combine writes the zero outputs itself.
   const int wpc = bal_waves_per_cu(c->L.format);
-  if (mfma && wpc > 0 && !a.fuse_combine && split_tokens == 0 &&
+  if (mfma && wpc > 0 && max_len > 0 && !a.fuse_combine && split_tokens == 0 &&
       (int64_t)batch * c->L.n_kv_heads * ((max_len + 31) / 32 + kUnitCost) < (int64_t)INT32_MAX) {
     a.bal_waves = wpc * device_cus();
   }

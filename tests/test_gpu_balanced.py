@@ -200,3 +200,22 @@ def test_many_sequences_scan_blocks(fmt):
     assert e <= TOL[fmt]
     assert not out[np.flatnonzero(w.lens == 0)].float().abs().any()
     assert c.status() == 0
+
+
+def test_max_len_zero_after_balanced_call():
+    """A call with max_len 0 (every length 0) on a workspace that a balanced
+    call used before: no split pass runs, and the combine must still write
+    the zero outputs rather than follow the earlier call's schedule record."""
+    require_gpu()
+    w = _workload("zero", [900, 20, 1700, 5], Hq=16, Hkv=4, D=128, bs=16, seed=21)
+    c, tdev, o = _filled(w)
+    q = w.query().cuda()
+    ws = c.workspace(w.batch, w.n_q_heads, w.max_len)
+    first = c.attend(q, tdev, dev(w.lens), w.max_len, w.scale, workspace=ws)
+    assert first.float().abs().sum() > 0
+    zeros = np.zeros(w.batch, np.int32)
+    out = torch.full_like(q, 7.0)
+    c.attend(q, tdev, dev(zeros), 0, w.scale, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert not out.float().abs().any()
+    assert c.status() == 0

@@ -1,5 +1,5 @@
-"""Seeded random shapes against the float64 oracle, for decode attention
-and for chunked prefill.  Decode cases: formats (f32, bf16,
+"""Seeded random shapes against the float64 oracle, for page writes, decode
+attention and chunked prefill.  Decode cases: formats (f32, bf16,
 int8), query groups of 1 to 16 heads, head dims 64 and 128, pages of 16, 32
 and 64 tokens, batches of uneven, equal or log-uniform lengths with empty
 sequences, the planned schedule or fixed splits, and the vector-ALU and
@@ -19,8 +19,8 @@ import torch
 from oracle import attend, attend_multi
 from paged_kv_cache_207_amd import pkv
 from paged_kv_cache_207_amd import workloads as W
-from tests.gpu_helpers import (TOL, dev, gpu_write, make_cache, max_err, require_gpu, say,
-                               sentinel_oracle)
+from tests.gpu_helpers import (TOL, dev, gpu_write, make_cache, max_err, pages_in_oracle_order,
+                               require_gpu, say, sentinel_oracle)
 from tests.helpers import dtype_name, np_bits, oracle_write_rounds
 
 pytestmark = pytest.mark.gpu
@@ -165,4 +165,56 @@ def test_random_multi_query_case(i):
     e = float(np.max(np.abs(g - ref))) if g.size else 0.0
     say(f"  max err {e:.3e} (tol {TOL[fmt]})")
     assert e <= TOL[fmt]
+    assert c.status() == 0
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_write_case(i):
+    """Page writes on seeded random shapes, bit for bit on whole sentinel-filled
+    pools: f32/bf16 pages and int8 pages fed with bf16 or f32 rows, pages of
+    16-128 tokens, several rounds per batch starting at arbitrary positions
+    (empty rows for some sequences), head dims 64/128."""
+    require_gpu()
+    rng = np.random.default_rng(zlib.crc32(f"random-write-{i}".encode()))
+    fmt = str(rng.choice(["f32", "bf16", "int8", "int8"]))
+    in_dt = {"f32": torch.float32, "bf16": torch.bfloat16}.get(
+        fmt, [torch.bfloat16, torch.float32][int(rng.integers(0, 2))])
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32, 64, 128]))
+    B = int(rng.integers(1, 12))
+    n_rounds = int(rng.integers(1, 4))
+    # per sequence, the rows each round writes, one round after the other
+    rows = rng.integers(0, 150, size=(n_rounds, B))
+    rows[rng.random((n_rounds, B)) < 0.2] = 0
+    lens = rows.sum(axis=0).astype(np.int32)
+    npg = [-(-int(n) // bs) for n in lens]
+    P = sum(npg) + 2
+    perm = rng.permutation(P).astype(np.int32)
+    tables = np.full((B, max(max(npg), 1)), -1, np.int32)
+    o_ = 0
+    for b, n in enumerate(npg):
+        tables[b, :n] = perm[o_:o_ + n]
+        o_ += n
+    w = W.Workload("random_write", P, bs, Hkv, D, Hkv, fmt, in_dt, in_dt, 0.125, tables, lens,
+                   7000 + i)
+    say(f"write case {i}: {fmt} rows {in_dt} Hkv={Hkv} D={D} bs={bs} rounds={rows.tolist()}")
+    g = torch.Generator().manual_seed(i)
+    rounds, pos = [], np.zeros(B, np.int32)
+    for r in range(n_rounds):
+        n = rows[r].astype(np.int32)
+        cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        k = (torch.randn(int(cu[-1]), Hkv, D, generator=g) * 3).to(in_dt)
+        v = (torch.randn(int(cu[-1]), Hkv, D, generator=g) * 3).to(in_dt)
+        rounds.append(W.WriteRound(pos.copy(), cu, k, v))
+        pos += n
+    c = make_cache(w)
+    gpu_write(c, dev(tables), rounds)
+    o = sentinel_oracle(w)
+    oracle_write_rounds(o, w, rounds)
+    K, V, KS, VS = pages_in_oracle_order(c)
+    assert np.array_equal(K, o.k) and np.array_equal(V, o.v)
+    if fmt == "int8":
+        assert np.array_equal(KS.view(np.uint32), o.k_scale.view(np.uint32))
+        assert np.array_equal(VS.view(np.uint32), o.v_scale.view(np.uint32))
     assert c.status() == 0

@@ -281,10 +281,12 @@ int pkv_gather(pkv_cache* cache, int32_t layer, const int32_t* table_row, int32_
 int pkv_copy_pages(pkv_cache* cache, const int32_t* pairs, int32_t n, void* stream);
 
 /* Apply n block-table updates: table[upd[3i] * table_stride + upd[3i+1]] =
- * upd[3i+2], with upd a device int32 [n][3] list (sequence, logical block,
+ * upd[3i+2], with upd an int32 [n][3] list (sequence, logical block,
  * physical page), as tiny-llm paged_kv.py's begin_step mirrors newly
- * allocated blocks into its device table.  Entries outside the table are
- * skipped. */
+ * allocated blocks into its device table.  upd is device memory or pinned
+ * host memory (hipHostMalloc), which the kernel reads in place, so a host
+ * list needs no copy launch; the host must not change it until the stream
+ * has run the update.  Entries outside the table are skipped. */
 int pkv_table_apply(int32_t* table, int32_t table_stride, int32_t batch, const int32_t* upd,
                     int32_t n, void* stream);
 

@@ -339,10 +339,17 @@ def probe_stream(src: torch.Tensor, dst: torch.Tensor | None = None,
 
 
 def table_apply(table: torch.Tensor, upd: torch.Tensor) -> None:
-    """Apply (sequence, block, page) triples [n, 3] to a device block table."""
+    """Apply (sequence, block, page) triples [n, 3] to a device block table.
+    ``upd`` is a GPU tensor or a pinned host tensor, which the kernel reads
+    in place (no copy launch)."""
+    if not upd.is_cuda and upd.is_pinned():
+        if not upd.is_contiguous() or upd.dtype != torch.int32:
+            raise ValueError("upd must be contiguous int32")
+        up = C.c_void_p(upd.data_ptr())
+    else:
+        up = _dev(upd, torch.int32, "upd")
     _check(lib().pkv_table_apply(_dev(table, torch.int32, "table"), table.shape[1], table.shape[0],
-                                 _dev(upd, torch.int32, "upd"), upd.shape[0],
-                                 _stream(table.device)))
+                                 up, upd.shape[0], _stream(table.device)))
 
 
 class PagePool:

@@ -104,3 +104,32 @@ def test_decode_steps_replayed_from_graphs(fixed_splits):
         # drop the graphs while the runtime is up, also when an assertion failed
         torch.cuda.synchronize()
         graphs.clear()
+
+
+def test_table_apply_reads_pinned_host_list():
+    """pkv_table_apply takes the update list from pinned host memory in place
+    (no copy launch), inside a captured graph too: the same table as with the
+    list in device memory, replay after replay with the host list rewritten
+    between replays."""
+    require_gpu()
+    B, stride = 6, 9
+    rng = np.random.default_rng(4)
+    host = torch.full((16, 3), -1, dtype=torch.int32).pin_memory()
+    t_dev = torch.full((B, stride), -1, dtype=torch.int32, device="cuda")
+    t_pin = torch.full((B, stride), -1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            pkv.table_apply(t_pin, host)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        n = int(rng.integers(1, 16))
+        upd = np.stack([rng.integers(0, B + 1, n), rng.integers(0, stride, n),
+                        rng.integers(0, 1000, n)], axis=1).astype(np.int32)  # b = B: skipped
+        host.fill_(-1)
+        host[:n] = torch.from_numpy(upd)
+        g.replay()
+        pkv.table_apply(t_dev, torch.from_numpy(upd).cuda())
+        torch.cuda.synchronize()
+        assert torch.equal(t_pin, t_dev), rep

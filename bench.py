@@ -306,7 +306,6 @@ def run_shared_prefix(args, device):
     # pending when the host prepares the next step's updates
     upd_host = [torch.empty((B + 8, 3), dtype=torch.int32).pin_memory()
                 for _ in range(sp.n_steps)]
-    upd_dev = torch.empty((B + 8, 3), dtype=torch.int32, device=device)
     torch.cuda.synchronize()
 
     ones = np.ones(B, np.int32)
@@ -315,9 +314,8 @@ def run_shared_prefix(args, device):
         for s in range(sp.n_steps):
             seqs.append_all(ones)  # every sequence grows by its new token
             n = seqs.take_updates(upd_host[s]).shape[0]
-            if n:
-                upd_dev[:n].copy_(upd_host[s][:n], non_blocking=True)
-                pkv.table_apply(table, upd_dev[:n])
+            if n:  # the kernel reads the step's pinned list in place
+                pkv.table_apply(table, upd_host[s][:n])
             cache.decode_step(table, lens_all[s], max_len, ks[s], vs[s], qs[s], w.scale,
                               out=out, workspace=ws, split_tokens=split)
 

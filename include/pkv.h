@@ -285,10 +285,17 @@ int pkv_copy_pages(pkv_cache* cache, const int32_t* pairs, int32_t n, void* stre
  * physical page), as tiny-llm paged_kv.py's begin_step mirrors newly
  * allocated blocks into its device table.  upd is device memory or pinned
  * host memory (hipHostMalloc), which the kernel reads in place, so a host
- * list needs no copy launch; the host must not change it until the stream
- * has run the update.  Entries outside the table are skipped. */
+ * list needs no copy launch; the host must neither change nor free it until
+ * the stream has run the update.  EINVAL if upd is neither device memory nor
+ * pinned host memory.  Entries outside the table are skipped. */
 int pkv_table_apply(int32_t* table, int32_t table_stride, int32_t batch, const int32_t* upd,
                     int32_t n, void* stream);
+
+/* Copy the cache's device status word (the PKV_DEV_* bits the kernels have
+ * OR-ed in) to host *out, after everything already enqueued on `stream`:
+ * this call synchronises the stream, so it is meant for tests and checks,
+ * not for a decode loop.  EHIP if the copy or the wait fails. */
+int pkv_read_device_status(pkv_cache* cache, void* stream, int32_t* out);
 
 const char* pkv_last_error(void);
 
@@ -326,9 +333,15 @@ int pkv_probe_stream(const void* src, void* dst, float* sink, uint64_t bytes, in
  * reference and the page is free again at zero.  retain adds one (the
  * sharing of libmir-metal PagedStore::snapshot).  Releasing or retaining a
  * page that is not in use is EDOUBLEFREE / EINVAL (tiny-llm BlockAllocator).
- * One pool is used from one thread at a time. */
+ * One pool is used from one thread at a time.
+ *   shuffle_seed  0: lowest free page first (AstrAI's rule).  Otherwise the
+ *                 pages are ranked by one SplitMix64 draw each (page i gets
+ *                 output i of the generator seeded with shuffle_seed, ties by
+ *                 page id) and the free page of lowest rank is handed out
+ *                 first, so a fresh pool hands out a seeded permutation of
+ *                 its pages, the shuffled page ids of a fragmented cache. */
 typedef struct pkv_pool pkv_pool;
-int pkv_pool_create(int32_t n_pages, pkv_pool** out);
+int pkv_pool_create(int32_t n_pages, uint64_t shuffle_seed, pkv_pool** out);
 void pkv_pool_destroy(pkv_pool* pool);
 int pkv_pool_alloc(pkv_pool* pool, int32_t* id);                /* ENOMEM when full */
 int pkv_pool_alloc_n(pkv_pool* pool, int32_t n, int32_t* ids); /* host ids[n]; ENOMEM, nothing granted */

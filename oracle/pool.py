@@ -18,19 +18,51 @@ class PoolError(Exception):
     pass
 
 
+_MASK64 = (1 << 64) - 1
+
+
+def splitmix64(seed: int, n: int) -> list[int]:
+    """The first n outputs of SplitMix64 seeded with ``seed`` (Steele, Lea and
+    Flood, "Fast splittable pseudorandom number generators", OOPSLA 2014, as
+    in Vigna's reference splitmix64.c): the state advances by the golden-ratio
+    gamma 0x9e3779b97f4a7c15 per output and each output is the state passed
+    through the variant-13 finalizer (xor-shift 30, multiply, xor-shift 27,
+    multiply, xor-shift 31)."""
+    out, state = [], seed & _MASK64
+    for _ in range(n):
+        state = (state + 0x9E3779B97F4A7C15) & _MASK64
+        z = state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _MASK64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _MASK64
+        out.append(z ^ (z >> 31))
+    return out
+
+
 class PoolModel:
-    def __init__(self, n_pages: int):
+    """``shuffle_seed`` 0 hands out the lowest free page (AstrAI's rule).
+    Otherwise page i is ranked by output i of SplitMix64 seeded with
+    ``shuffle_seed`` (ties by page id), and the free page of lowest rank
+    goes first: a fresh pool hands out a seeded permutation of its pages.
+    This ordering is the build's own choice (the pages name no shuffled
+    allocator); what the pages fix is only that any order is allowed."""
+
+    def __init__(self, n_pages: int, shuffle_seed: int = 0):
         self.refs = [0] * n_pages
+        if shuffle_seed:
+            draws = splitmix64(shuffle_seed, n_pages)
+            self.order = sorted(range(n_pages), key=lambda i: (draws[i], i))
+        else:
+            self.order = list(range(n_pages))
 
     def alloc(self) -> int:
-        for i, r in enumerate(self.refs):
-            if r == 0:
+        for i in self.order:
+            if self.refs[i] == 0:
                 self.refs[i] = 1
                 return i
         return -1
 
     def alloc_n(self, n: int):
-        free = [i for i, r in enumerate(self.refs) if r == 0]
+        free = [i for i in self.order if self.refs[i] == 0]
         if n > len(free):
             return None
         got = free[:n]
@@ -171,6 +203,7 @@ class SeqModel:
         trial = SeqModel(PoolModel(len(self.pool.refs)), self.batch, self.stride, self.bs)
         trial.pool.refs = list(self.pool.refs) + [0] * sum(
             -(-int(n) // self.bs) + 1 for n in ns)
+        trial.pool.order = list(range(len(trial.pool.refs)))  # the count ignores the order
         trial.pages = [list(p) for p in self.pages]
         trial.lens = list(self.lens)
         before = trial.pool.num_free()

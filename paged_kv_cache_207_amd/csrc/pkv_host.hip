@@ -612,9 +612,26 @@ int pkv_table_apply(int32_t* table, int32_t table_stride, int32_t batch, const i
   if (n < 0 || table_stride < 1 || batch < 0) return fail(PKV_EINVAL, "bad sizes");
   if (n == 0) return PKV_OK;
   if (!table || !upd) return fail(PKV_EINVAL, "null device pointer");
+  // the kernel reads upd in place: it must be device memory or pinned host
+  // memory (a pageable host list would fault the device)
+  hipPointerAttribute_t at;
+  const hipError_t pe = hipPointerGetAttributes(&at, upd);
+  if (pe != hipSuccess || at.type == hipMemoryTypeUnregistered || !at.devicePointer) {
+    (void)hipGetLastError();  // leave no sticky error for later launches
+    return fail(PKV_EINVAL, "upd is neither device memory nor pinned host memory");
+  }
   hipError_t e = pkv::launch_table_apply(table, table_stride, batch, upd, n,
                                          static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_EHIP, "table update launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+int pkv_read_device_status(pkv_cache* c, void* stream, int32_t* out) {
+  if (!c || !out) return fail(PKV_EINVAL, "null argument");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(out, c->status, sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(PKV_EHIP, "status read failed: %s", hipGetErrorString(e));
   return PKV_OK;
 }
 
@@ -649,17 +666,52 @@ int pkv_copy_pages(pkv_cache* c, const int32_t* pairs, int32_t n, void* stream) 
 
 struct pkv_pool {
   std::vector<int32_t> refs;
-  std::set<int32_t> free_ids;  // ordered: begin() is the lowest free page
+  // Hand-out order: page order[k] is the k-th choice.  Lowest-first is the
+  // identity; a shuffled pool sorts the pages by a SplitMix64 draw per page.
+  std::vector<int32_t> order, rank_of;  // rank_of[order[k]] = k
+  std::set<int32_t> free_ranks;         // ordered: begin() is the next page handed out
+  int32_t take() {
+    const int32_t k = *free_ranks.begin();
+    free_ranks.erase(free_ranks.begin());
+    const int32_t i = order[k];
+    refs[i] = 1;
+    return i;
+  }
 };
+
+namespace {
+
+// SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+// generators", OOPSLA 2014; the reference splitmix64.c of Vigna): output n
+// (n = 0, 1, ...) of the generator seeded with `seed` is the mix of
+// seed + (n + 1) * 0x9e3779b97f4a7c15.
+uint64_t splitmix64_at(uint64_t seed, uint64_t n) {
+  uint64_t z = seed + (n + 1) * 0x9e3779b97f4a7c15ull;
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+  return z ^ (z >> 31);
+}
+
+}  // namespace
 
 extern "C" {
 
-int pkv_pool_create(int32_t n_pages, pkv_pool** out) {
+int pkv_pool_create(int32_t n_pages, uint64_t shuffle_seed, pkv_pool** out) {
   if (!out || n_pages < 1) return fail(PKV_EINVAL, "bad pool size or null out");
   pkv_pool* p = new (std::nothrow) pkv_pool;
   if (!p) return fail(PKV_ENOMEM, "out of host memory");
   p->refs.assign(n_pages, 0);
-  for (int32_t i = 0; i < n_pages; ++i) p->free_ids.insert(p->free_ids.end(), i);
+  p->order.resize(n_pages);
+  for (int32_t i = 0; i < n_pages; ++i) p->order[i] = i;
+  if (shuffle_seed != 0) {
+    std::vector<uint64_t> key(n_pages);
+    for (int32_t i = 0; i < n_pages; ++i) key[i] = splitmix64_at(shuffle_seed, (uint64_t)i);
+    std::stable_sort(p->order.begin(), p->order.end(),
+                     [&](int32_t x, int32_t y) { return key[x] < key[y]; });
+  }
+  p->rank_of.resize(n_pages);
+  for (int32_t k = 0; k < n_pages; ++k) p->rank_of[p->order[k]] = k;
+  for (int32_t k = 0; k < n_pages; ++k) p->free_ranks.insert(p->free_ranks.end(), k);
   *out = p;
   return PKV_OK;
 }
@@ -668,24 +720,16 @@ void pkv_pool_destroy(pkv_pool* p) { delete p; }
 
 int pkv_pool_alloc(pkv_pool* p, int32_t* id) {
   if (!p || !id) return fail(PKV_EINVAL, "null argument");
-  if (p->free_ids.empty()) return fail(PKV_ENOMEM, "all %zu pages in use", p->refs.size());
-  const int32_t i = *p->free_ids.begin();
-  p->free_ids.erase(p->free_ids.begin());
-  p->refs[i] = 1;
-  *id = i;
+  if (p->free_ranks.empty()) return fail(PKV_ENOMEM, "all %zu pages in use", p->refs.size());
+  *id = p->take();
   return PKV_OK;
 }
 
 int pkv_pool_alloc_n(pkv_pool* p, int32_t n, int32_t* ids) {
   if (!p || n < 0 || (n > 0 && !ids)) return fail(PKV_EINVAL, "bad arguments");
-  if ((size_t)n > p->free_ids.size())
-    return fail(PKV_ENOMEM, "%d pages asked, %zu free", n, p->free_ids.size());
-  for (int32_t k = 0; k < n; ++k) {
-    const int32_t i = *p->free_ids.begin();
-    p->free_ids.erase(p->free_ids.begin());
-    p->refs[i] = 1;
-    ids[k] = i;
-  }
+  if ((size_t)n > p->free_ranks.size())
+    return fail(PKV_ENOMEM, "%d pages asked, %zu free", n, p->free_ranks.size());
+  for (int32_t k = 0; k < n; ++k) ids[k] = p->take();
   return PKV_OK;
 }
 
@@ -699,7 +743,7 @@ int pkv_pool_retain(pkv_pool* p, int32_t id) {
 int pkv_pool_release(pkv_pool* p, int32_t id) {
   if (!p || id < 0 || (size_t)id >= p->refs.size()) return fail(PKV_EINVAL, "page id out of range");
   if (p->refs[id] == 0) return fail(PKV_EDOUBLEFREE, "page %d released twice or never allocated", id);
-  if (--p->refs[id] == 0) p->free_ids.insert(id);
+  if (--p->refs[id] == 0) p->free_ranks.insert(p->rank_of[id]);
   return PKV_OK;
 }
 
@@ -708,7 +752,7 @@ int32_t pkv_pool_refcount(const pkv_pool* p, int32_t id) {
   return p->refs[id];
 }
 
-int32_t pkv_pool_num_free(const pkv_pool* p) { return p ? (int32_t)p->free_ids.size() : -1; }
+int32_t pkv_pool_num_free(const pkv_pool* p) { return p ? (int32_t)p->free_ranks.size() : -1; }
 
 }  // extern "C"
 

@@ -18,9 +18,9 @@ namespace pkv {
 namespace {
 
 // One wave per (sequence, query head).  Up to 64 splits: one split per lane
-// for the weights 2^(m_s - M), which stay in registers, and each lane owns a
-// pair of dims, the first 8 splits' partial outputs loaded together with the
-// (m, l) pairs.  More splits: the weights go through LDS and each lane sums
+// for the weights 2^(m_s - M), which stay in registers, and each lane owns
+// every 64th pair of dims (one pair up to head_dim 128, two up to 256), the
+// first 8 splits' partial outputs loaded together with the (m, l) pairs.  More splits: the weights go through LDS and each lane sums
 // the splits' partial outputs with 8 loads in flight.
 __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
   extern __shared__ float wsplit[];  // [n_split] weights
@@ -57,52 +57,61 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttendArgs a) {
   const int64_t oi0 = (int64_t)bh * D;
 
   if (n <= 64) {
-    // one split per lane: the partial outputs of the first 8 splits are
-    // loaded together with the (m, l) pairs, and the weights stay in
-    // registers (read back per split with a lane read)
-    const int d2 = lane;  // dims 2 lane, 2 lane + 1
-    const bool has_d = 2 * d2 < D;
+    // one split per lane: the weights stay in registers (read back per split
+    // with a lane read); each lane owns dims 2 d2, 2 d2 + 1 for d2 = lane,
+    // lane + 64, ...  The first dim pair's partial outputs of the first 8
+    // splits are loaded together with the (m, l) pairs.
     float2 x[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      x[u] = has_d && u < n ? *reinterpret_cast<const float2*>(po + u * pstep + 2 * d2)
-                            : float2{0.f, 0.f};
+      x[u] = 2 * lane < D && u < n ? *reinterpret_cast<const float2*>(po + u * pstep + 2 * lane)
+                                   : float2{0.f, 0.f};
     const float2 mlv = lane < n ? *reinterpret_cast<const float2*>(ml + 2 * (int64_t)rstep * lane)
                                 : float2{-INFINITY, 0.f};
     const float M = wave_max(mlv.x);
     const float w = lane < n ? exp2f(mlv.x - M) : 0.f;
     const float L = wave_sum(w * mlv.y);
     const float inv = n > 0 ? 1.f / L : 0.f;
-    float2 acc = {0.f, 0.f};
+    for (int d2 = lane; 2 * (d2 - lane) < D; d2 += 64) {  // uniform trip count
+      const bool has_d = 2 * d2 < D;
+      if (d2 != lane) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (u < n) {
-        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
-        acc.x = fmaf(wu, x[u].x, acc.x);
-        acc.y = fmaf(wu, x[u].y, acc.y);
+        for (int u = 0; u < 8; ++u)
+          x[u] = has_d && u < n ? *reinterpret_cast<const float2*>(po + u * pstep + 2 * d2)
+                                : float2{0.f, 0.f};
       }
-    }
-    for (int s0 = 8; s0 < n; s0 += 8) {  // further splits, 8 loads in flight
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        x[u] = has_d && s0 + u < n
-                   ? *reinterpret_cast<const float2*>(po + (s0 + u) * pstep + 2 * d2)
-                   : float2{0.f, 0.f};
+      float2 acc = {0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s0 + u));
-        acc.x = fmaf(ws, x[u].x, acc.x);
-        acc.y = fmaf(ws, x[u].y, acc.y);
+        if (u < n) {
+          const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+          acc.x = fmaf(wu, x[u].x, acc.x);
+          acc.y = fmaf(wu, x[u].y, acc.y);
+        }
       }
-    }
-    if (has_d) {
-      const float r0 = acc.x * inv, r1 = acc.y * inv;
-      const int64_t oi = oi0 + 2 * d2;
-      if (a.q_bf16)
-        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + oi) =
-            f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
-      else
-        *reinterpret_cast<float2*>(static_cast<float*>(a.out) + oi) = float2{r0, r1};
+      for (int s0 = 8; s0 < n; s0 += 8) {  // further splits, 8 loads in flight
+        float2 y[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          y[u] = has_d && s0 + u < n
+                     ? *reinterpret_cast<const float2*>(po + (s0 + u) * pstep + 2 * d2)
+                     : float2{0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s0 + u));
+          acc.x = fmaf(ws, y[u].x, acc.x);
+          acc.y = fmaf(ws, y[u].y, acc.y);
+        }
+      }
+      if (has_d) {
+        const float r0 = acc.x * inv, r1 = acc.y * inv;
+        const int64_t oi = oi0 + 2 * d2;
+        if (a.q_bf16)
+          *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + oi) =
+              f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
+        else
+          *reinterpret_cast<float2*>(static_cast<float*>(a.out) + oi) = float2{r0, r1};
+      }
     }
     return;
   }

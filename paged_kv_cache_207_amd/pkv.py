@@ -48,13 +48,14 @@ SYMBOLS = [
      [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _F, _P, _P]),
     ("pkv_gather", C.c_int, [_P, _I32, _P, _I32, _P, _P, _P, _P, _P]),
     ("pkv_table_apply", C.c_int, [_P, _I32, _I32, _P, _I32, _P]),
+    ("pkv_read_device_status", C.c_int, [_P, _P, _PI32]),
     ("pkv_copy_pages", C.c_int, [_P, _P, _I32, _P]),
     ("pkv_last_error", C.c_char_p, []),
     ("pkv_timing_enable", C.c_int, [_P, _I32]),
     ("pkv_timing_read", C.c_int, [_P, C.POINTER(C.c_double), _PI32]),
     ("pkv_probe_blocks", C.c_int32, [_U64]),
     ("pkv_probe_stream", C.c_int, [_P, _P, _P, _U64, _I32, _P]),
-    ("pkv_pool_create", C.c_int, [_I32, C.POINTER(_P)]),
+    ("pkv_pool_create", C.c_int, [_I32, _U64, C.POINTER(_P)]),
     ("pkv_pool_destroy", None, [_P]),
     ("pkv_pool_alloc", C.c_int, [_P, _PI32]),
     ("pkv_pool_alloc_n", C.c_int, [_P, _I32, _PI32]),
@@ -179,8 +180,11 @@ class PagedKVCache:
         return self.k_scales.view(L, P, H, bs), self.v_scales.view(L, P, H, bs)
 
     def status(self) -> int:
-        """The device status word (synchronises: for tests and checks)."""
-        return int(self.status_word.item())
+        """The device status word, read through the library after the current
+        stream's work (synchronises that stream: for tests and checks)."""
+        out = C.c_int32()
+        _check(lib().pkv_read_device_status(self._h, _stream(self.device), C.byref(out)))
+        return out.value
 
     def clear_status(self) -> None:
         """Zero the device status word (on the current stream)."""
@@ -230,11 +234,25 @@ class PagedKVCache:
         n = self.workspace_size(batch, n_q_heads, max_len, split_tokens)
         return torch.zeros(max(n, 1), dtype=torch.uint8, device=self.device)
 
+    def _check_decode_shapes(self, q, table, lens, out):
+        """The sizes the C ABI trusts: q [B, Hq, head_dim], lens [B], table
+        [>= B, stride], out shaped like q."""
+        if q.dim() != 3 or q.shape[2] != self.head_dim:
+            raise ValueError(f"q must be [batch, n_q_heads, {self.head_dim}], got {tuple(q.shape)}")
+        B = q.shape[0]
+        if lens.dim() != 1 or lens.shape[0] != B:
+            raise ValueError(f"lens must hold {B} lengths, got {tuple(lens.shape)}")
+        if table.dim() != 2 or table.shape[0] < B:
+            raise ValueError(f"table must be [>= {B}, stride], got {tuple(table.shape)}")
+        if out is not None and tuple(out.shape) != tuple(q.shape):
+            raise ValueError(f"out must be shaped like q {tuple(q.shape)}, got {tuple(out.shape)}")
+
     def attend(self, q, table, lens, max_len: int, scale: float, out=None, workspace=None,
                split_tokens: int = 0, flags: int = 0, layer: int = 0) -> torch.Tensor:
-        B, Hq, D = q.shape
         if q.dtype not in DTYPE_CODE:
             raise ValueError("q must be float32 or bfloat16")
+        self._check_decode_shapes(q, table, lens, out)
+        B, Hq, D = q.shape
         if out is None:
             out = torch.empty_like(q)
         if workspace is None:
@@ -251,6 +269,7 @@ class PagedKVCache:
     def decode_step(self, table, lens, max_len: int, k_new, v_new, q, scale: float, out=None,
                     workspace=None, split_tokens: int = 0, flags: int = 0,
                     layer: int = 0) -> torch.Tensor:
+        self._check_decode_shapes(q, table, lens, out)
         B, Hq, D = q.shape
         if tuple(k_new.shape) != (B, self.n_kv_heads, self.head_dim) or v_new.shape != k_new.shape:
             raise ValueError("k_new and v_new must be [batch, n_kv_heads, head_dim]")
@@ -274,14 +293,20 @@ class PagedKVCache:
                      out=None, layer: int = 0) -> torch.Tensor:
         """q [total_q, Hq, D] bf16; rows cu_q[b] .. cu_q[b+1] are sequence b's
         last tokens, each attending causally to its sequence."""
+        if q.dim() != 3 or q.shape[2] != self.head_dim:
+            raise ValueError(f"q must be [total_q, n_q_heads, {self.head_dim}]")
         total_q, Hq, D = q.shape
         if q.dtype != torch.bfloat16:
             raise ValueError("q must be bfloat16")
+        if out is not None and tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out must be shaped like q")
         if out is None:
             out = torch.empty_like(q)
         B = lens.shape[0]
         if cu_q.shape[0] != B + 1:
             raise ValueError("cu_q must hold batch + 1 offsets")
+        if table.dim() != 2 or table.shape[0] < B:
+            raise ValueError("table must have a row per sequence")
         _check(lib().pkv_paged_attend_multi(
             self._h, layer, _dev(q, name="q"), DTYPE_CODE[q.dtype], Hq,
             _dev(table, torch.int32, "table"), table.shape[1], _dev(lens, torch.int32, "lens"),
@@ -338,11 +363,27 @@ def probe_stream(src: torch.Tensor, dst: torch.Tensor | None = None,
         _check(lib().pkv_probe_stream(_dev(src), _dev(dst), None, nbytes, 1, _stream(src.device)))
 
 
+# Pinned host update lists handed to the device, held until the stream that
+# reads them has passed an event recorded after the update (torch's host
+# allocator does not know the kernel reads them, and would hand a freed list
+# out again).
+_pinned_in_flight: list = []
+
+
 def table_apply(table: torch.Tensor, upd: torch.Tensor) -> None:
     """Apply (sequence, block, page) triples [n, 3] to a device block table.
     ``upd`` is a GPU tensor or a pinned host tensor, which the kernel reads
-    in place (no copy launch)."""
-    if not upd.is_cuda and upd.is_pinned():
+    in place (no copy launch).  Outside graph capture a pinned list is kept
+    alive here until the stream has run the update; under capture the caller
+    keeps it alive for as long as the graph may be replayed."""
+    if upd.dim() != 2 or upd.shape[1] != 3:
+        raise ValueError(f"upd must be [n, 3], got {tuple(upd.shape)}")
+    if table.dim() != 2:
+        raise ValueError("table must be [batch, stride]")
+    host = not upd.is_cuda
+    if host:
+        if not upd.is_pinned():
+            raise ValueError("a host update list must be pinned")
         if not upd.is_contiguous() or upd.dtype != torch.int32:
             raise ValueError("upd must be contiguous int32")
         up = C.c_void_p(upd.data_ptr())
@@ -350,14 +391,21 @@ def table_apply(table: torch.Tensor, upd: torch.Tensor) -> None:
         up = _dev(upd, torch.int32, "upd")
     _check(lib().pkv_table_apply(_dev(table, torch.int32, "table"), table.shape[1], table.shape[0],
                                  up, upd.shape[0], _stream(table.device)))
+    if host and upd.shape[0] > 0 and not torch.cuda.is_current_stream_capturing():
+        while _pinned_in_flight and _pinned_in_flight[0][0].query():
+            _pinned_in_flight.pop(0)
+        ev = torch.cuda.Event()
+        ev.record(torch.cuda.current_stream(table.device))
+        _pinned_in_flight.append((ev, upd))
 
 
 class PagePool:
-    """Host refcounted page pool."""
+    """Host refcounted page pool: lowest free page first, or (shuffle_seed
+    != 0) the free page of lowest seeded SplitMix64 rank."""
 
-    def __init__(self, n_pages: int):
+    def __init__(self, n_pages: int, shuffle_seed: int = 0):
         h = C.c_void_p()
-        _check(lib().pkv_pool_create(n_pages, C.byref(h)))
+        _check(lib().pkv_pool_create(n_pages, shuffle_seed, C.byref(h)))
         self._h = h
 
     def close(self):

@@ -34,10 +34,12 @@ def test_library_exports_every_declared_symbol():
 
 # ------------------------------------------------------------------ pool ----
 
-def test_pool_fixture_through_abi():
-    lines = [l.split("#")[0].strip() for l in open(os.path.join(GOLDEN, "pool_ops.txt"))]
+@pytest.mark.parametrize("fixture", ["pool_ops.txt", "pool_shuffled.txt"])
+def test_pool_fixture_through_abi(fixture):
+    lines = [l.split("#")[0].strip() for l in open(os.path.join(GOLDEN, fixture))]
     lines = [l for l in lines if l]
-    p = pkv.PagePool(int(lines[0].split()[1]))
+    head = lines[0].split()
+    p = pkv.PagePool(int(head[1]), int(head[2]) if len(head) > 2 else 0)
     for line in lines[1:]:
         lhs, want = [s.strip() for s in line.split("->")]
         op, *args = lhs.split()
@@ -63,10 +65,11 @@ def test_pool_fixture_through_abi():
         assert got == want, line
 
 
-def test_pool_matches_model_on_random_ops():
-    rng = random.Random(7)
+@pytest.mark.parametrize("seed", [0, 1, 0xDEADBEEF, (1 << 64) - 1])
+def test_pool_matches_model_on_random_ops(seed):
+    rng = random.Random(7 + seed % 1000)
     n = 40
-    p, m = pkv.PagePool(n), PoolModel(n)
+    p, m = pkv.PagePool(n, seed), PoolModel(n, seed)
     held = []
     for _ in range(3000):
         op = rng.random()

@@ -50,12 +50,14 @@ def test_addressing_fixture():
 
 # ------------------------------------------------------------------- pool ---
 
-def test_pool_fixture():
-    with open(os.path.join(GOLDEN, "pool_ops.txt")) as f:
+@pytest.mark.parametrize("fixture", ["pool_ops.txt", "pool_shuffled.txt"])
+def test_pool_fixture(fixture):
+    with open(os.path.join(GOLDEN, fixture)) as f:
         lines = [l.split("#")[0].strip() for l in f]
     lines = [l for l in lines if l]
-    n = int(lines[0].split()[1])
-    p = PoolModel(n)
+    head = lines[0].split()
+    n = int(head[1])
+    p = PoolModel(n, int(head[2]) if len(head) > 2 else 0)
     for line in lines[1:]:
         lhs, want = [s.strip() for s in line.split("->")]
         op, *args = lhs.split()
@@ -79,6 +81,29 @@ def test_pool_fixture():
             assert str(p.refcount(args[0])) == want, line
         else:
             raise AssertionError(op)
+
+
+def test_splitmix64_published_vectors():
+    """The seeded pool order draws from SplitMix64; its outputs match the
+    generator's published test vectors."""
+    from oracle.pool import splitmix64
+    with open(os.path.join(GOLDEN, "splitmix64.txt")) as f:
+        rows = [l.split("->") for l in f if l.strip() and not l.startswith("#")]
+    assert len(rows) == 2
+    for seed, outs in rows:
+        want = [int(x) for x in outs.split()]
+        assert splitmix64(int(seed), len(want)) == want
+
+
+def test_shuffled_pool_is_a_permutation():
+    """A fresh shuffled pool hands out every page once, in an order that is
+    not the identity, and the same seed gives the same order."""
+    for seed in (1, 7, 1234567):
+        a, b = PoolModel(64, seed), PoolModel(64, seed)
+        got = a.alloc_n(64)
+        assert sorted(got) == list(range(64)) and got != list(range(64))
+        assert b.alloc_n(64) == got
+        assert a.alloc() == -1
 
 
 # ------------------------------------------------------------------ write ---
@@ -215,6 +240,75 @@ def test_int8_properties():
     c1, s1 = quantize_int8_rows(e)
     assert list(c1[0]) == [0, 0, 0, -127, 0, 0, 0, 0]
     assert s1[0] == np.float32(np.float32(2.75) / np.float32(127))
+
+
+# ------------------------------------------------------------------ bf16 ----
+
+def test_bf16_decode_every_bit_pattern():
+    """The oracle's bf16 decode equals torch's bfloat16 -> float32 conversion
+    on all 65 536 bit patterns (bf16 is the upper half of a float32), and a
+    few values fixed by the format itself."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.bf16_bits_to_f32(bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    assert got.dtype == np.float32
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    fixed = {0x3F80: 1.0, 0xC000: -2.0, 0x3E80: 0.25, 0x4049: 3.140625, 0x0000: 0.0,
+             0x0001: 2.0 ** -133, 0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127, 0x7F80: math.inf,
+             0xFF80: -math.inf}
+    vals = oracle.bf16_bits_to_f32(np.array(list(fixed), np.uint16))
+    assert [float(x) for x in vals] == list(fixed.values())
+    neg0 = oracle.bf16_bits_to_f32(np.array([0x8000], np.uint16))[0]
+    assert neg0 == 0 and math.copysign(1.0, float(neg0)) == -1.0
+    assert np.isnan(oracle.bf16_bits_to_f32(np.array([0x7FC0, 0xFFC1], np.uint16))).all()
+
+
+@pytest.mark.parametrize("G,D,n", [(1, 16, 33), (4, 32, 100), (8, 64, 21)])
+def test_identity_table_matches_contiguous_sdpa_bf16(G, D, n):
+    """As the f32 pin, with bf16 pages and a bf16 query: the oracle's decode
+    of the stored bit patterns and of q feeds attention equal to SDPA on
+    torch's own bf16 -> float64 conversion of the same tensors."""
+    Hkv, bs = 2, 16
+    P = -(-n // bs)
+    g = torch.Generator().manual_seed(G * 101 + D)
+    k = torch.randn(n, Hkv, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(n, Hkv, D, generator=g).to(torch.bfloat16)
+    q = torch.randn(1, Hkv * G, D, generator=g).to(torch.bfloat16)
+    c = OracleCache(1, P, bs, Hkv, D, "bf16")
+    table = np.arange(P, dtype=np.int32)[None]
+    c.write(0, table, np.zeros(1, np.int32), np.array([0, n], np.int32), np_bits(k), np_bits(v),
+            "bf16")
+    scale = float(np.float32(1 / math.sqrt(D)))
+    out = attend(c, 0, np_bits(q), "bf16", table, np.array([n]), scale)
+    ref = _contiguous_sdpa(k.double().numpy(), v.double().numpy(), q[0].double().numpy(), scale, G)
+    assert np.max(np.abs(out[0] - ref)) < 1e-12
+
+
+def test_int8_write_from_bf16_rows_matches_scalar_reference():
+    """int8 pages written from bf16 rows: the codes and scales the oracle
+    stores equal the scalar reference applied to torch's float conversion of
+    the rows (planted ties included)."""
+    g = torch.Generator().manual_seed(12)
+    n, Hkv, D = 40, 2, 16
+    x = torch.randn(n, Hkv, D, generator=g)
+    x[0, 0] = 0.0
+    x[0, 0, :6] = torch.tensor([127.0, 0.5, 1.5, 2.5, -0.5, -2.5])  # exact in bf16
+    x[1, 1] = 0.0
+    xb = x.to(torch.bfloat16)
+    vb = (-x).to(torch.bfloat16)
+    c = OracleCache(1, 10, 4, Hkv, D, "int8")
+    table = np.arange(10, dtype=np.int32)[None]
+    c.write(0, table, np.zeros(1, np.int32), np.array([0, n], np.int32), np_bits(xb), np_bits(vb),
+            "bf16")
+    K, V, KS, VS = c.gather(0, table[0], n)
+    xf, vf = xb.float().numpy(), vb.float().numpy()
+    for i in range(n):
+        for h in range(Hkv):
+            for rows, codes, scales in ((xf, K, KS), (vf, V, VS)):
+                cref, sref = _quantize_scalar(rows[i, h])
+                assert scales[i, h] == np.float32(sref)
+                assert list(codes[i, h]) == cref
+    assert list(K[0, 0, :6]) == [127, 0, 2, 2, 0, -2]
 
 
 # ------------------------------------------------------------- attention ----
@@ -507,3 +601,21 @@ def test_planted_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(oracle_attention, "query_positions", from_zero)
     with pytest.raises(AssertionError):
         test_multi_query_matches_masked_sdpa(1, 16, 40, 9)
+    monkeypatch.undo()
+    # bf16 decoded with a wrong shift, or with its sign dropped -> the bit
+    # pattern pin, the bf16 SDPA pin and the bf16-fed int8 pin fail
+    import oracle.attention as oa
+    for wrong in (lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << np.uint32(15))
+                  .view(np.float32),
+                  lambda b: ((np.asarray(b, np.uint16).astype(np.uint32) & np.uint32(0x7FFF))
+                             << np.uint32(16)).view(np.float32)):
+        monkeypatch.setattr(pc, "bf16_bits_to_f32", wrong)
+        monkeypatch.setattr(oa, "bf16_bits_to_f32", wrong)
+        monkeypatch.setattr(oracle, "bf16_bits_to_f32", wrong)
+        with pytest.raises(AssertionError):
+            test_bf16_decode_every_bit_pattern()
+        with pytest.raises(AssertionError):
+            test_identity_table_matches_contiguous_sdpa_bf16(4, 32, 100)
+        with pytest.raises(AssertionError):
+            test_int8_write_from_bf16_rows_matches_scalar_reference()
+        monkeypatch.undo()

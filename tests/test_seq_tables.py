@@ -18,8 +18,8 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "seq_ops.txt")
 class Lib:
     """The library's pool + block tables behind the model's interface."""
 
-    def __init__(self, n_pages, batch, stride, bs):
-        self.pool = pkv.PagePool(n_pages)
+    def __init__(self, n_pages, batch, stride, bs, seed=0):
+        self.pool = pkv.PagePool(n_pages, seed)
         self.s = pkv.SeqTables(self.pool, batch, stride, bs)
         self.batch = batch
 
@@ -68,8 +68,8 @@ class Lib:
 
 
 class Model:
-    def __init__(self, n_pages, batch, stride, bs):
-        self.m = SeqModel(PoolModel(n_pages), batch, stride, bs)
+    def __init__(self, n_pages, batch, stride, bs, seed=0):
+        self.m = SeqModel(PoolModel(n_pages, seed), batch, stride, bs)
         self.batch = batch
 
     def __getattr__(self, k):
@@ -106,6 +106,9 @@ def replay(make):
                 got = "ok"
             elif op == "fork":
                 t.fork(*args)
+                got = "ok"
+            elif op == "share":
+                t.share(*args)
                 got = "ok"
             elif op == "release":
                 t.release(*args)
@@ -144,11 +147,11 @@ def snapshot(t):
             t.num_free())
 
 
-@pytest.mark.parametrize("seed", [1, 2, 3])
-def test_seq_random_ops_match_model(seed):
+@pytest.mark.parametrize("seed,pool_seed", [(1, 0), (2, 0), (3, 0), (4, 99), (5, 1234567)])
+def test_seq_random_ops_match_model(seed, pool_seed):
     rng = random.Random(seed)
     P, B, stride, bs = 30, 5, 6, 4
-    lib, mod = Lib(P, B, stride, bs), Model(P, B, stride, bs)
+    lib, mod = Lib(P, B, stride, bs, pool_seed), Model(P, B, stride, bs, pool_seed)
     for step in range(400):
         r = rng.random()
         if r < 0.35:

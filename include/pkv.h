@@ -213,6 +213,26 @@ int pkv_paged_attend(pkv_cache* cache, int32_t layer, const void* q, int32_t q_d
                      void* workspace, uint64_t workspace_bytes, int32_t split_tokens,
                      uint32_t flags, void* stream);
 
+/* pkv_paged_attend without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the split partials go to a static
+ * device array of the library, 64 MiB per device, which each device the
+ * library runs on holds until the process ends.  The call allocates
+ * nothing itself (no hipMalloc, hipFree, events or library allocations; the
+ * caller still passes q, out, table and lens) and enqueues exactly what
+ * pkv_paged_attend with the same arguments enqueues, so its outputs are
+ * identical.  Every call on a device shares that device's array and leaves
+ * in it the last call's partials: calls that may overlap on one device
+ * (other streams, other threads) race and must not be issued.  Nothing in
+ * the array has to start at zero.
+ *   Errors as pkv_paged_attend, plus ENOMEM when the sizes need more than
+ *   the 64 MiB (pkv_attend_workspace_size gives the need) and EINVAL for
+ *   PKV_ATTEND_COMBINE_FUSED, whose counters this variant does not keep. */
+int pkv_paged_attend_noalloc(pkv_cache* cache, int32_t layer, const void* q, int32_t q_dtype,
+                             int32_t n_q_heads, const int32_t* table, int32_t table_stride,
+                             const int32_t* lens, int32_t batch, int32_t max_len, float scale,
+                             void* out, int32_t split_tokens, uint32_t flags, void* stream);
+
 /* One decode step: paged_write of one new row per sequence, then
  * paged_attend, as a single call.  Row b of k_new / v_new (device
  * [batch][n_kv_heads][head_dim] of in_dtype) is stored at position

@@ -6,6 +6,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <map>
+#include <mutex>
 #include <new>
 #include <set>
 #include <vector>
@@ -137,9 +138,9 @@ struct Timer {
   pkv_cache* c;
   int kind;
   pkv::Launch l;
-  Timer(pkv_cache* c_, int kind_, hipStream_t s) : c(c_), kind(kind_) {
+  Timer(pkv_cache* c_, int kind_, hipStream_t s, bool allowed = true) : c(c_), kind(kind_) {
     l.s = s;
-    if (!c->timing) return;
+    if (!c->timing || !allowed) return;
     if (hipEventCreate(&l.e0) != hipSuccess) {
       l.e0 = nullptr;
     } else if (hipEventCreate(&l.e1) != hipSuccess) {
@@ -338,7 +339,7 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
                 const int32_t* table, int32_t table_stride, const int32_t* lens, int32_t batch,
                 int32_t max_len, float scale, void* out, void* workspace,
                 uint64_t workspace_bytes, int32_t split_tokens, uint32_t flags, void* stream,
-                const void* k_new, const void* v_new, int32_t in_dtype) {
+                const void* k_new, const void* v_new, int32_t in_dtype, bool timed = true) {
   if (!c) return fail(PKV_EINVAL, "cache is null");
   if (layer < 0 || layer >= c->L.n_layers)
     return fail(PKV_ERANGE, "layer %d outside [0, %d)", layer, c->L.n_layers);
@@ -435,7 +436,7 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
       w.batch = batch;
       w.total_new = batch;
       w.decode_lens = lens;
-      Timer tw(c, PKV_T_WRITE, s);
+      Timer tw(c, PKV_T_WRITE, s, timed);
       e = pkv::launch_write(w, c->L.format, in_dtype, tw.l);
       tw.stop(e);
       if (e != hipSuccess) return fail(PKV_EHIP, "write launch failed: %s", hipGetErrorString(e));
@@ -458,14 +459,14 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
     a.bal_waves = wpc * device_cus();
   }
   if (max_len > 0) {
-    Timer tm(c, PKV_T_ATTEND_SPLIT, s);
+    Timer tm(c, PKV_T_ATTEND_SPLIT, s, timed);
     e = mfma ? pkv::launch_attend_mfma(a, c->L.format, tm.l)
              : pkv::launch_attend_valu(a, c->L.format, tm.l);
     tm.stop(e);
     if (e != hipSuccess) return fail(PKV_EHIP, "attend launch failed: %s", hipGetErrorString(e));
     if (a.fuse_combine) return PKV_OK;  // the split pass combined the splits itself
   }
-  Timer tm(c, PKV_T_ATTEND_COMBINE, s);
+  Timer tm(c, PKV_T_ATTEND_COMBINE, s, timed);
   e = pkv::launch_reduce(a, tm.l);
   tm.stop(e);
   if (e != hipSuccess) return fail(PKV_EHIP, "reduce launch failed: %s", hipGetErrorString(e));
@@ -484,6 +485,75 @@ int pkv_paged_attend(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype
   return attend_impl(c, layer, q, q_dtype, n_q_heads, table, table_stride, lens, batch, max_len,
                      scale, out, workspace, workspace_bytes, split_tokens, flags, stream, nullptr,
                      nullptr, 0);
+}
+
+}  // extern "C"
+
+// The allocation-free attend's workspace: one static array per device, held
+// until the process ends.  Host code never passes `scratch` itself to a
+// kernel (in host code the name stands for a host-side shadow, not device
+// memory): each device's address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address is used.
+static constexpr uint64_t kScratchBytes = 64ull << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The current device's scratch address (null and a message on failure).
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+    (void)hipGetLastError();
+    fail(PKV_EHIP, "no usable current device for the static scratch");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      fail(PKV_EHIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+           hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attend_noalloc(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype,
+                             int32_t n_q_heads, const int32_t* table, int32_t table_stride,
+                             const int32_t* lens, int32_t batch, int32_t max_len, float scale,
+                             void* out, int32_t split_tokens, uint32_t flags, void* stream) {
+  if (!c) return fail(PKV_EINVAL, "cache is null");
+  if (flags & PKV_ATTEND_COMBINE_FUSED)
+    return fail(PKV_EINVAL, "the static-scratch attend has no in-kernel combine");
+  if (n_q_heads < 1 || batch < 0 || max_len < 0) return fail(PKV_EINVAL, "bad sizes");
+  if (int e = check_split(c, split_tokens)) return e;
+  const int split = split_tokens ? split_tokens : plan_split(c, batch, n_q_heads, max_len);
+  const int n_split = std::max(1, (max_len + split - 1) / split);
+  if (n_split > kMaxSplits)
+    return fail(PKV_EINVAL, "%d splits of %d tokens exceed %d per sequence", n_split, split,
+                kMaxSplits);
+  const uint64_t need = ws_layout(c, batch, n_q_heads, n_split).total;
+  if (need > kScratchBytes)
+    return fail(PKV_ENOMEM, "these sizes need %llu bytes of workspace, the static scratch holds %llu",
+                (unsigned long long)need, (unsigned long long)kScratchBytes);
+  if (batch == 0) return PKV_OK;
+  void* ws = device_scratch();
+  if (!ws) return PKV_EHIP;
+  return attend_impl(c, layer, q, q_dtype, n_q_heads, table, table_stride, lens, batch, max_len,
+                     scale, out, ws, kScratchBytes, split_tokens, flags, stream, nullptr, nullptr,
+                     0, /*timed=*/false);  // kernel timing would create events
 }
 
 int pkv_paged_attend_multi(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype,

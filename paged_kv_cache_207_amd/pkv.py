@@ -41,6 +41,8 @@ SYMBOLS = [
     ("pkv_attend_workspace_size", C.c_int, [_P, _I32, _I32, _I32, _I32, C.POINTER(C.c_uint64)]),
     ("pkv_paged_attend", C.c_int,
      [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _I32, _I32, _F, _P, _P, _U64, _I32, _U32, _P]),
+    ("pkv_paged_attend_noalloc", C.c_int,
+     [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _I32, _I32, _F, _P, _I32, _U32, _P]),
     ("pkv_decode_step", C.c_int,
      [_P, _I32, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _I32, _I32, _F, _P, _P, _U64, _I32,
       _U32, _P]),
@@ -262,6 +264,23 @@ class PagedKVCache:
             _dev(table, torch.int32, "table"), table.shape[1], _dev(lens, torch.int32, "lens"), B,
             max_len, float(scale), _dev(out, q.dtype, "out"), _dev(workspace, name="workspace"),
             workspace.numel() * workspace.element_size(), split_tokens, flags,
+            _stream(self.device)))
+        return out
+
+    def attend_noalloc(self, q, table, lens, max_len: int, scale: float, out,
+                       split_tokens: int = 0, flags: int = 0, layer: int = 0) -> torch.Tensor:
+        """attend() through the library's static scratch: no workspace, and
+        the call allocates nothing (``out`` is the caller's)."""
+        if q.dtype not in DTYPE_CODE:
+            raise ValueError("q must be float32 or bfloat16")
+        if out is None:
+            raise ValueError("out must be given: this call allocates nothing")
+        self._check_decode_shapes(q, table, lens, out)
+        B, Hq, D = q.shape
+        _check(lib().pkv_paged_attend_noalloc(
+            self._h, layer, _dev(q, name="q"), DTYPE_CODE[q.dtype], Hq,
+            _dev(table, torch.int32, "table"), table.shape[1], _dev(lens, torch.int32, "lens"), B,
+            max_len, float(scale), _dev(out, q.dtype, "out"), split_tokens, flags,
             _stream(self.device)))
         return out
 

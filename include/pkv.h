@@ -76,6 +76,10 @@ extern "C" {
 #define PKV_DEV_WRITE_ROWS 32u  /* paged_write met a sequence whose rows cu_new[b] ..
                                    cu_new[b+1] are decreasing or outside [0, total_new]
                                    (that sequence skipped) */
+#define PKV_DEV_PREFIX 64u      /* shared-prefix attend met a table row whose first pages
+                                   differ from the shared list (its result is wrong), or a
+                                   decode-step row that would land inside the shared prefix
+                                   (not written) */
 
 typedef enum { PKV_FMT_F32 = 0, PKV_FMT_BF16 = 1, PKV_FMT_INT8 = 2 } pkv_format;
 typedef enum { PKV_DT_F32 = 0, PKV_DT_BF16 = 1 } pkv_dtype;
@@ -254,6 +258,43 @@ int pkv_decode_step(pkv_cache* cache, int32_t layer, const int32_t* table, int32
                     uint64_t workspace_bytes, int32_t split_tokens, uint32_t flags,
                     void* stream);
 
+/* Decode attention (and, with k_new, the decode step's row write) for a
+ * batch whose sequences share their first prefix_len tokens: the pages that
+ * hold them are listed once, in prefix_pages, and every table row lists the
+ * same pages first (the refcounted sharing of libmir-metal
+ * PagedStore::snapshot; tiny-llm paged_kv.py: one block serves every reader).
+ * The results are those of pkv_decode_step / pkv_paged_attend over the same
+ * tables, computed so that the shared pages are read once for all sequences:
+ * a prefix pass attends over them with (sequence, query head) pairs as the
+ * columns of its matrix-core tiles, the split pass covers only each
+ * sequence's tokens past prefix_len, and the combine merges both.
+ *   prefix_pages  device int32 [prefix_len / page_size]; prefix_len a
+ *                 positive multiple of page_size within the table row.
+ *                 Sequence b sees t < min(lens[b], prefix_len) of the shared
+ *                 tokens; its table row must list prefix_pages for those
+ *                 tokens (a row that does not is reported as PKV_DEV_PREFIX
+ *                 and its result is wrong).
+ *   k_new, v_new  null (attend only) or device bf16 [batch][n_kv_heads]
+ *                 [head_dim]: row b is written at position lens[b] - 1 and
+ *                 attended, as in pkv_decode_step; a position inside the
+ *                 shared prefix is not written and sets PKV_DEV_PREFIX.
+ *   workspace     at least pkv_prefix_workspace_size bytes, 256-byte aligned,
+ *                 zeroed once (as for pkv_paged_attend).
+ *   flags         0 or PKV_ATTEND_COMBINE_KERNEL (EINVAL otherwise).
+ * Matrix-core shapes only (bf16/int8 pages, bf16 q, head_dim 64/128, page
+ * size 16 or a multiple of 32, groups of at most 16): EFORMAT otherwise.
+ * Other arguments and errors as pkv_decode_step. */
+int pkv_prefix_workspace_size(const pkv_cache* cache, int32_t batch, int32_t n_q_heads,
+                              int32_t max_len, int32_t prefix_len, int32_t split_tokens,
+                              uint64_t* bytes);
+int pkv_decode_step_prefix(pkv_cache* cache, int32_t layer, const int32_t* table,
+                           int32_t table_stride, const int32_t* lens, int32_t batch,
+                           int32_t max_len, const int32_t* prefix_pages, int32_t prefix_len,
+                           const void* k_new, const void* v_new, int32_t in_dtype, const void* q,
+                           int32_t q_dtype, int32_t n_q_heads, float scale, void* out,
+                           void* workspace, uint64_t workspace_bytes, int32_t split_tokens,
+                           uint32_t flags, void* stream);
+
 /* Several queries per sequence (a chunk of new tokens, as in chunked
  * prefill).  Sequence b's T_b = cu_q[b+1] - cu_q[b] query rows stand for its
  * last T_b tokens, which a page write has already stored (AstrAI cache.py
@@ -334,7 +375,8 @@ const char* pkv_last_error(void);
 #define PKV_T_GATHER 3
 #define PKV_T_ATTEND_MULTI 4
 #define PKV_T_COPY_PAGES 5
-#define PKV_T_COUNT 6
+#define PKV_T_ATTEND_PREFIX 6  /* the shared-prefix pass */
+#define PKV_T_COUNT 7
 int pkv_timing_enable(pkv_cache* cache, int32_t on);
 int pkv_timing_read(pkv_cache* cache, double* ms, int32_t* counts);
 

@@ -119,8 +119,9 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
   const int n_full = fpre[B];
   const int n_items = (n_full + qpre[B]) * a.n_kv_heads;
 
-  // sequences with no tokens have no work item: their output is zero
-  for (int b = blockIdx.x; b < B; b += gridDim.x) {
+  // sequences with no tokens have no work item: their output is zero (with a
+  // shared prefix the combine writes every output)
+  for (int b = blockIdx.x; b < (a.prefix_len > 0 ? 0 : B); b += gridDim.x) {
     if (lens[b] != 0) continue;
     for (int i = lane; i < a.n_q_heads * D / 4; i += 64)
       store_out4(a.out, a.q_bf16, (int64_t)b * a.n_q_heads * D + 4 * i, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -169,7 +170,7 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
     if (p_lo >= p_hi) continue;  // only set-up slots of this unit fall here
     t_begin = (int)(p_lo - s_first) * 32;
     t_end = std::min((int)(p_hi - s_first) * 32, len_b);
-    direct = p_lo == s_first && p_hi == u_end;
+    direct = p_lo == s_first && p_hi == u_end && a.prefix_len == 0;
     owns_new = a.k_new != nullptr && p_hi == u_end;
     const int unit = b * a.n_kv_heads + g;
     const int slot = unit + (int)blockIdx.x;  // strictly increasing along the flat space
@@ -201,7 +202,7 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
     n_splits_b = (lens[b] + C - 1) / C;
     t_begin = sp * C;
     t_end = min(t_begin + C, lens[b]);
-    direct = n_splits_b == 1;
+    direct = n_splits_b == 1 && a.prefix_len == 0;
     // decode step: the sequence's new row sits at position len - 1, in the
     // last step of its last split (see substitute_new below)
     owns_new = a.k_new != nullptr && sp == n_splits_b - 1;
@@ -308,7 +309,8 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
     // flight behind it, so the row costs no registers during the loop.
     auto substitute_new = [&](int ts, S& r) {
       if (!owns_new || t_new < ts || t_new >= ts + 32) return;
-      if (a.lens[b] != len) return;  // an out-of-range length (reported, clamped): no write
+      // an out-of-range length (reported, clamped): no write
+      if (a.lens[b] - a.prefix_len != len) return;
       const int x_new = t_new - ts;                          // slot of the token in the step
       const int tau_new = (x_new >> 2) & 1;                  // score tile holding it
       const int n_new = ((x_new >> 3) << 2) | (x_new & 3);  // its K row lane
@@ -559,8 +561,15 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int bb = b0 + 64 * u + lane;
-      const int len = clamp_len(lv[u], a.max_len, blockIdx.x == 0 ? a.status : nullptr,
-                                PKV_DEV_LEN);
+      int len = clamp_len(lv[u], a.max_len, blockIdx.x == 0 ? a.status : nullptr,
+                          PKV_DEV_LEN);
+      if (a.prefix_len > 0) {
+        // the private suffix past the shared prefix; a decode step's new row
+        // must land in it
+        if (a.k_new && bb < B && len > 0 && len <= a.prefix_len && blockIdx.x == 0)
+          report(a.status, PKV_DEV_PREFIX);
+        len = max(len - a.prefix_len, 0);
+      }
       if (bb < B) {
         lens[bb] = len;
         if (len > 0) {

@@ -1,0 +1,275 @@
+// Shared-prefix pass: attention of every sequence's decode queries over the
+// tokens its block table shares with all the others, reading those pages
+// once for many sequences instead of once per sequence.
+//
+// Pages shared by reference count (libmir-metal src/engine/kv/paged/mod.rs,
+// PagedStore::snapshot; tiny-llm paged_kv.py: one block serves every reader
+// of it) hold the same K/V for every sequence that lists them, so the scores
+// of all those sequences' queries against one shared token can come from one
+// read of it.  Here the columns of the matrix-core tiles are (sequence, query
+// head) pairs of one KV head: a wave holds two tiles of 16 columns (the G
+// heads of consecutive sequences), walks one chunk of the shared tokens in
+// 32-token steps (the step machinery of mfma_step.h, with cached loads, since
+// every wave of the launch reads the same pages), and leaves per column the
+// running maximum m (log2 units), the sum l and the unnormalised weighted V
+// sum of that chunk: the tile accumulation of metrale_storage
+// high_speed_swap/impl_more.rs attend_layer, finalised by the combine kernel
+// together with the pieces of the private suffix.
+//
+// Column (b, h) sees the shared tokens t < min(lens[b], prefix_len), the
+// decode length rule of tiny-llm paged_kv.py begin_step.  Each wave also
+// checks that its sequences' table rows list the shared pages it read, and
+// reports PKV_DEV_PREFIX otherwise.
+#include <algorithm>
+
+#include "mfma_step.h"
+
+namespace pkv {
+namespace {
+
+// One step of cached (not streamed) loads: the same pages serve every wave.
+template <int FMT, int D, int BS>
+__device__ __forceinline__ void load_step_cached(Step<FMT, D>& r, const PageSrc& s, int page_a,
+                                                 int page_b, int slot0, int g, int lane) {
+  using S = Step<FMT, D>;
+  constexpr int ESZ = FMT == PKV_FMT_BF16 ? 2 : 1;
+  const int n = lane & 15, j = lane >> 4;
+  const int bs = BS ? BS : s.bs;
+  r.live_a = page_a >= 0;
+  r.live_b = page_b >= 0;
+  const int64_t slab_a = (s.layer_page0 + (page_a >= 0 ? page_a : 0)) * s.n_kv_heads + g;
+  const int64_t slab_b = (s.layer_page0 + (page_b >= 0 ? page_b : 0)) * s.n_kv_heads + g;
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    const int tok = 8 * (n >> 2) + 4 * tau + (n & 3);
+    const bool on_b = BS == 16 && tok >= 16;
+    const char* kb = s.k + (on_b ? slab_b : slab_a) * s.slab_bytes;
+    const int row = BS == 16 ? (tok & 15) : slot0 + tok;
+#pragma unroll
+    for (int c = 0; c < S::NK; ++c)
+      r.k[tau][c] = *reinterpret_cast<const typename S::KT*>(
+          kb + (row * D + kdim_of<FMT>(S::KPL * c, j)) * ESZ);
+  }
+  const bool v_on_b = BS == 16 && j >= 2;
+  const char* vb = s.v + (v_on_b ? slab_b : slab_a) * s.slab_bytes;
+  const int col = BS == 16 ? 8 * (j & 1) : slot0 + 8 * j;
+  const int voff = (n * bs + col) * ESZ;
+#pragma unroll
+  for (int dt = 0; dt < S::ND; ++dt)
+    r.v[dt] = *reinterpret_cast<const typename S::VT*>(vb + voff + 16 * dt * bs * ESZ);
+  if (FMT == PKV_FMT_INT8) {
+    const int x = 8 * j + (n & 7);
+    const bool s_on_b = BS == 16 && x >= 16;
+    const int slot = BS == 16 ? (x & 15) : slot0 + x;
+    const float* sb = n < 8 ? s.ks : s.vs;
+    r.sc = sb[(s_on_b ? slab_b : slab_a) * bs + slot];
+  }
+}
+
+// Online-softmax state of one 16-column tile.
+template <int ND>
+struct Tile {
+  float m, l;
+  f32x4 o[ND];
+};
+
+template <int FMT, int D, int BS>
+__global__ __launch_bounds__(64) void attend_prefix_kernel(AttendArgs a) {
+  using S = Step<FMT, D>;
+  constexpr int NC = S::NC, ND = S::ND;
+  const int lane = threadIdx.x;
+  const int n = lane & 15, j = lane >> 4;
+  const int G = a.group, g = blockIdx.y, chunk = blockIdx.z;
+  const int bs = BS ? BS : a.page_size;
+  const int ncols = a.batch * G;
+  const int c0 = blockIdx.x * 32;
+  const int P0 = a.prefix_len;
+
+  // the two tiles' columns: (sequence, head in group) of column c0 + 16 t + n,
+  // and how many shared tokens each may see
+  int bcol[2], hcol[2], bound[2];
+  bf16x8 qf[2][NC];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int c = c0 + 16 * t + n;
+    const bool used = c < ncols;
+    const int b = used ? c / G : 0;
+    bcol[t] = b;
+    hcol[t] = c - b * G;
+    int len = used ? a.lens[b] : 0;
+    len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);  // reported by the split pass
+    bound[t] = used ? min(len, P0) : 0;
+    load_q<FMT, D>(qf[t], static_cast<const uint16_t*>(a.q) +
+                             ((int64_t)b * a.n_q_heads + (int64_t)g * G + hcol[t]) * D,
+                   used, j);
+  }
+  const int t_begin = chunk * kPrefixChunk;
+  const int t_end = min(t_begin + kPrefixChunk, P0);
+  // steps past every column's bound are skipped; slots at or past the wave's
+  // largest bound may never have been written (NaN), so their V is zeroed
+  int bmax = max(bound[0], bound[1]);
+#pragma unroll
+  for (int o1 = 1; o1 < 64; o1 <<= 1) bmax = max(bmax, __shfl_xor(bmax, o1, 64));
+  bmax = __builtin_amdgcn_readfirstlane(bmax);
+  const int t_stop = min(t_end, bmax);
+
+  Tile<ND> st[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    st[t].m = -INFINITY;
+    st[t].l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) st[t].o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float qs = a.qk_scale_log2;
+  const int64_t slab_bytes = (int64_t)bs * D * (FMT == PKV_FMT_BF16 ? 2 : 1);
+  const PageSrc src{static_cast<const char*>(a.k_pages), static_cast<const char*>(a.v_pages),
+                    a.k_scales, a.v_scales, a.layer_page0, slab_bytes, a.n_kv_heads, bs};
+
+  auto page_at = [&](int lp) -> int {
+    const int pg = a.prefix_pages[lp];
+    if (pg < 0 || pg >= a.n_pages) {
+      if (lane == 0) report(a.status, PKV_DEV_READ_PAGE);
+      return -1;
+    }
+    return pg;
+  };
+  auto load_at = [&](int ts, S& r) {
+    const int lp = ts / bs;
+    const int pa = page_at(lp);
+    int pb = pa;
+    if (BS == 16) pb = ts + 16 < t_stop ? page_at(lp + 1) : -1;
+    load_step_cached<FMT, D, BS>(r, src, pa, pb, ts - lp * bs, g, lane);
+  };
+  auto compute = [&](int ts, S& r) {
+    const bool lane_live = BS == 16 && j >= 2 ? r.live_b : r.live_a;
+    float ksc[8], vsc[8];
+    if constexpr (FMT == PKV_FMT_INT8) step_scales<FMT, D>(r, ksc, vsc);
+    // V slots no column may see are zeroed (they may hold NaN)
+    bool vok[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) vok[x] = lane_live && ts + 8 * j + x < t_stop;
+    uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
+    if (FMT == PKV_FMT_BF16 && (ts + 32 > t_stop || !r.live_a || !r.live_b)) v_keep_masks(vok, keep);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x4 sacc[2];
+      step_scores<FMT, D>(r, qf[t], sacc);
+      float sv[8];
+      bool ok[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        ok[x] = vok[x] && ts + 8 * j + x < bound[t];
+        float y = sacc[x >> 2][x & 3] * qs;
+        if (FMT == PKV_FMT_INT8) y *= ksc[x];
+        sv[x] = ok[x] ? y : -INFINITY;
+        mx = fmaxf(mx, sv[x]);
+      }
+      mx = rows_max(mx);
+      const float m_new = fmaxf(st[t].m, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(st[t].m - m_use);
+      float psum = 0.f;
+      float pw[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const float p = ok[x] ? __builtin_amdgcn_exp2f(sv[x] - m_use) : 0.f;
+        psum += p;
+        pw[x] = FMT == PKV_FMT_INT8 ? p * vsc[x] : p;
+      }
+      const bf16x8 pb = as_bf16x8(uint4{pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3]),
+                                        pack_bf16x2(pw[4], pw[5]), pack_bf16x2(pw[6], pw[7])});
+      st[t].l = st[t].l * alpha + psum;
+      st[t].m = m_new;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) st[t].o[dt] *= alpha;
+      }
+      step_pv<FMT, D>(r, pb, keep, st[t].o);
+    }
+  };
+
+  // two register sets, loads one step ahead; the last steps are peeled so no
+  // load sits under a condition
+  const int n_steps = t_stop > t_begin ? (t_stop - t_begin + 31) / 32 : 0;
+  if (n_steps > 0) {
+    auto T = [&](int i) { return t_begin + 32 * i; };
+    S r0, r1;
+    load_at(T(0), r0);
+    int s = 0;
+    for (; s + 2 < n_steps; s += 2) {
+      load_at(T(s + 1), r1);
+      compute(T(s), r0);
+      load_at(T(s + 2), r0);
+      compute(T(s + 1), r1);
+    }
+    if (s + 1 < n_steps) {
+      load_at(T(s + 1), r1);
+      compute(T(s), r0);
+      compute(T(s + 1), r1);
+    } else {
+      compute(T(s), r0);
+    }
+  }
+
+  // ---- partials of this chunk: O^T lane layout = dims 16 dt + 4 j + i of column n ----
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float l = rows_sum(st[t].l);
+    if (c0 + 16 * t + n < ncols) {
+      const int64_t row =
+          (((int64_t)bcol[t] * a.n_q_heads + (int64_t)g * G + hcol[t]) * a.n_pchunks + chunk);
+      float* wo = a.ws_pre_o + row * D + 4 * j;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) *reinterpret_cast<f32x4*>(wo + 16 * dt) = st[t].o[dt];
+      if (j == 0) *reinterpret_cast<float2*>(a.ws_pre_ml + row * 2) = float2{st[t].m, l};
+    }
+  }
+
+  // ---- the promise behind this pass: every sequence read here lists the
+  // shared pages of this chunk in its own table row (one check per column
+  // lane with j = 0; heads of one sequence repeat it) ----
+  if (j == 0) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int lp_end = (min(t_end, bound[t]) + bs - 1) / bs;
+      const int32_t* row = a.table_full + (int64_t)bcol[t] * a.table_stride;
+      bool bad = false;
+      for (int lp = t_begin / bs; lp < lp_end; ++lp) bad |= row[lp] != a.prefix_pages[lp];
+      if (bad) report(a.status, PKV_DEV_PREFIX);
+    }
+  }
+}
+
+template <int FMT, int D, int BS>
+hipError_t launch_bs(const AttendArgs& a, const Launch& l) {
+  const int64_t blocks = ((int64_t)a.batch * a.group + 31) / 32;
+  if (blocks > 0x7fffffff || a.n_pchunks > 65535 || a.n_kv_heads > 65535)
+    return hipErrorInvalidValue;
+  return launch1(attend_prefix_kernel<FMT, D, BS>,
+                 dim3((unsigned)blocks, a.n_kv_heads, a.n_pchunks), dim3(64), 0, l, a);
+}
+
+template <int FMT, int D>
+hipError_t launch_d(const AttendArgs& a, const Launch& l) {
+  if (a.page_size == 16) return launch_bs<FMT, D, 16>(a, l);
+  if (a.page_size == 32) return launch_bs<FMT, D, 32>(a, l);
+  return launch_bs<FMT, D, 0>(a, l);
+}
+
+template <int FMT>
+hipError_t launch_fmt(const AttendArgs& a, const Launch& l) {
+  return a.head_dim == 128 ? launch_d<FMT, 128>(a, l) : launch_d<FMT, 64>(a, l);
+}
+
+}  // namespace
+
+hipError_t launch_attend_prefix(const AttendArgs& a, int fmt, const Launch& l) {
+  if (!mfma_supported(fmt, a.q_bf16, a.head_dim, a.page_size, a.group, a.batch, a.n_kv_heads))
+    return hipErrorNotSupported;
+  if (a.batch <= 0 || a.prefix_len <= 0 || a.n_pchunks <= 0) return hipSuccess;
+  return fmt == PKV_FMT_BF16 ? launch_fmt<PKV_FMT_BF16>(a, l) : launch_fmt<PKV_FMT_INT8>(a, l);
+}
+
+}  // namespace pkv

@@ -111,6 +111,7 @@ constexpr int kUnitCost = 3;
 
 struct WsLayout {
   uint64_t o_off, ml_off, sched_off, desc_off, total;
+  uint64_t pre_o_off = 0, pre_ml_off = 0;  // shared-prefix partials (after the rest)
 };
 
 WsLayout ws_layout(const pkv_cache* c, int batch, int n_q_heads, int n_split) {
@@ -130,6 +131,26 @@ WsLayout ws_layout(const pkv_cache* c, int batch, int n_q_heads, int n_split) {
   w.total = w.desc_off + (uint64_t)batch * n_kv_heads * 2 * sizeof(int32_t);
   return w;
 }
+
+// Prefix chunks of a shared prefix of prefix_len tokens (one partial each).
+int prefix_chunks(int prefix_len) { return (prefix_len + pkv::kPrefixChunk - 1) / pkv::kPrefixChunk; }
+
+// ws_layout plus the shared-prefix partials: [batch][n_q_heads][chunks] rows.
+WsLayout ws_layout_prefix(const pkv_cache* c, int batch, int n_q_heads, int n_split,
+                          int prefix_len) {
+  WsLayout w = ws_layout(c, batch, n_q_heads, n_split);
+  const uint64_t rows = (uint64_t)batch * n_q_heads * prefix_chunks(prefix_len);
+  w.pre_o_off = (w.total + 255) / 256 * 256;
+  w.pre_ml_off = (w.pre_o_off + rows * c->L.head_dim * sizeof(float) + 255) / 256 * 256;
+  w.total = w.pre_ml_off + rows * 2 * sizeof(float);
+  return w;
+}
+
+// A shared prefix: the first `len` tokens of every sequence sit in `pages`.
+struct Prefix {
+  const int32_t* pages;
+  int32_t len;
+};
 
 // Timing: while enabled, each kernel pass is launched with an event pair
 // that its dispatch stamps with the kernel's start and end; the pairs are
@@ -339,7 +360,8 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
                 const int32_t* table, int32_t table_stride, const int32_t* lens, int32_t batch,
                 int32_t max_len, float scale, void* out, void* workspace,
                 uint64_t workspace_bytes, int32_t split_tokens, uint32_t flags, void* stream,
-                const void* k_new, const void* v_new, int32_t in_dtype, bool timed = true) {
+                const void* k_new, const void* v_new, int32_t in_dtype, bool timed = true,
+                const Prefix* pre = nullptr) {
   if (!c) return fail(PKV_EINVAL, "cache is null");
   if (layer < 0 || layer >= c->L.n_layers)
     return fail(PKV_ERANGE, "layer %d outside [0, %d)", layer, c->L.n_layers);
@@ -359,16 +381,37 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
   if ((flags & PKV_ATTEND_COMBINE_KERNEL) && (flags & PKV_ATTEND_COMBINE_FUSED))
     return fail(PKV_EINVAL, "conflicting combine flags");
   if (int e = check_split(c, split_tokens)) return e;
+  const int P0 = pre ? pre->len : 0;
+  if (pre) {
+    if (P0 < 1 || P0 % c->L.page_size || (int64_t)P0 > (int64_t)table_stride * c->L.page_size)
+      return fail(PKV_EINVAL, "prefix_len %d must be a positive multiple of page_size %d within "
+                  "the table row", P0, c->L.page_size);
+    if (flags & (PKV_ATTEND_VALU | PKV_ATTEND_COMBINE_FUSED))
+      return fail(PKV_EINVAL, "the shared-prefix attend takes neither PKV_ATTEND_VALU nor "
+                  "PKV_ATTEND_COMBINE_FUSED");
+    if (!pkv::mfma_supported(c->L.format, q_dtype == PKV_DT_BF16, c->L.head_dim,
+                             c->L.page_size, n_q_heads / c->L.n_kv_heads, std::max(batch, 1),
+                             c->L.n_kv_heads))
+      return fail(PKV_EFORMAT, "no shared-prefix kernel for this cache (needs bf16/int8 pages, "
+                  "a bf16 query, head_dim 64 or 128, page_size 16 or a multiple of 32, at most "
+                  "16 query heads per KV head)");
+    if (k_new && in_dtype != PKV_DT_BF16)
+      return fail(PKV_EFORMAT, "the shared-prefix decode step takes bf16 rows");
+  }
   if (batch == 0) return PKV_OK;
   if (!q || !out || !table || !lens || !workspace) return fail(PKV_EINVAL, "null device pointer");
+  if (pre && !pre->pages) return fail(PKV_EINVAL, "null prefix page list");
   if (reinterpret_cast<uintptr_t>(workspace) & 255)
     return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
-  const int split = split_tokens ? split_tokens : plan_split(c, batch, n_q_heads, max_len);
-  const int n_split = std::max(1, (max_len + split - 1) / split);
+  // the split pass covers the tokens past the shared prefix
+  const int sfx_max = std::max(max_len - P0, 0);
+  const int split = split_tokens ? split_tokens : plan_split(c, batch, n_q_heads, sfx_max);
+  const int n_split = std::max(1, (sfx_max + split - 1) / split);
   if (n_split > kMaxSplits)
     return fail(PKV_EINVAL, "%d splits of %d tokens exceed %d per sequence", n_split, split,
                 kMaxSplits);
-  const WsLayout w = ws_layout(c, batch, n_q_heads, n_split);
+  const WsLayout w = pre ? ws_layout_prefix(c, batch, n_q_heads, n_split, P0)
+                         : ws_layout(c, batch, n_q_heads, n_split);
   if (workspace_bytes < w.total)
     return fail(PKV_ENOMEM, "workspace holds %llu bytes, %llu needed",
                 (unsigned long long)workspace_bytes, (unsigned long long)w.total);
@@ -404,6 +447,15 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
   a.split_tokens = split;
   a.n_split = n_split;
   a.q_bf16 = q_dtype == PKV_DT_BF16;
+  if (pre) {
+    a.table = table + P0 / c->L.page_size;  // the split pass sees the private suffixes
+    a.table_full = table;
+    a.prefix_pages = pre->pages;
+    a.prefix_len = P0;
+    a.n_pchunks = prefix_chunks(P0);
+    a.ws_pre_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.pre_o_off);
+    a.ws_pre_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.pre_ml_off);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   const bool mfma = !(flags & PKV_ATTEND_VALU) &&
@@ -411,7 +463,7 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
                                         batch, c->L.n_kv_heads);
   a.k_new = a.v_new = nullptr;
   if (k_new) {
-    if (mfma && max_len > 0 && in_dtype == PKV_DT_BF16) {
+    if (mfma && (sfx_max > 0 || pre) && in_dtype == PKV_DT_BF16) {
       a.k_new = k_new;  // the split pass writes and uses the new rows
       a.v_new = v_new;
     } else {
@@ -447,18 +499,28 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
   // wave per (sequence, KV head) and lengthens the tail).  Flags can force
   // either.
   a.fuse_combine = mfma && (flags & PKV_ATTEND_COMBINE_FUSED) != 0;
-  a.single_done = mfma && max_len > 0;
+  a.single_done = mfma && max_len > 0 && !pre;
   // The balanced schedule where the library plans the work (split_tokens 0)
   // on the matrix-core path for the page formats it pays off on, unless the
   // in-kernel combine is asked for (it counts fixed splits); its flat slot
   // count must fit 31 bits.  Not for max_len 0: no split pass runs then to
   // record its choice, and the combine writes the zero outputs itself.
   const int wpc = bal_waves_per_cu(c->L.format);
-  if (mfma && wpc > 0 && max_len > 0 && !a.fuse_combine && split_tokens == 0 &&
-      (int64_t)batch * c->L.n_kv_heads * ((max_len + 31) / 32 + kUnitCost) < (int64_t)INT32_MAX) {
+  if (mfma && wpc > 0 && sfx_max > 0 && !a.fuse_combine && split_tokens == 0 &&
+      (int64_t)batch * c->L.n_kv_heads * ((sfx_max + 31) / 32 + kUnitCost) < (int64_t)INT32_MAX) {
     a.bal_waves = wpc * device_cus();
   }
-  if (max_len > 0) {
+  if (pre && max_len > 0) {
+    // the shared prefix, once for every sequence
+    Timer tp(c, PKV_T_ATTEND_PREFIX, s, timed);
+    e = pkv::launch_attend_prefix(a, c->L.format, tp.l);
+    tp.stop(e);
+    if (e != hipSuccess)
+      return fail(PKV_EHIP, "prefix pass launch failed: %s", hipGetErrorString(e));
+  }
+  // (a shared-prefix decode step runs the split pass even without suffix
+  // tokens: it reports rows that would land inside the prefix)
+  if (sfx_max > 0 || (pre && a.k_new)) {
     Timer tm(c, PKV_T_ATTEND_SPLIT, s, timed);
     e = mfma ? pkv::launch_attend_mfma(a, c->L.format, tm.l)
              : pkv::launch_attend_valu(a, c->L.format, tm.l);
@@ -639,6 +701,40 @@ int pkv_decode_step(pkv_cache* c, int32_t layer, const int32_t* table, int32_t t
   return attend_impl(c, layer, q, q_dtype, n_q_heads, table, table_stride, lens, batch, max_len,
                      scale, out, workspace, workspace_bytes, split_tokens, flags, stream, k_new,
                      v_new, in_dtype);
+}
+
+int pkv_prefix_workspace_size(const pkv_cache* c, int32_t batch, int32_t n_q_heads,
+                              int32_t max_len, int32_t prefix_len, int32_t split_tokens,
+                              uint64_t* bytes) {
+  if (!c || !bytes) return fail(PKV_EINVAL, "null argument");
+  if (batch < 0 || n_q_heads < 1 || max_len < 0 || prefix_len < 1)
+    return fail(PKV_EINVAL, "bad sizes");
+  if (int e = check_split(c, split_tokens)) return e;
+  const int sfx_max = std::max(max_len - prefix_len, 0);
+  const int split = split_tokens ? split_tokens : plan_split(c, batch, n_q_heads, sfx_max);
+  const int n_split = std::max(1, (sfx_max + split - 1) / split);
+  if (n_split > kMaxSplits)
+    return fail(PKV_EINVAL, "%d splits of %d tokens exceed %d per sequence", n_split, split,
+                kMaxSplits);
+  *bytes = ws_layout_prefix(c, batch, n_q_heads, n_split, prefix_len).total;
+  return PKV_OK;
+}
+
+int pkv_decode_step_prefix(pkv_cache* c, int32_t layer, const int32_t* table,
+                           int32_t table_stride, const int32_t* lens, int32_t batch,
+                           int32_t max_len, const int32_t* prefix_pages, int32_t prefix_len,
+                           const void* k_new, const void* v_new, int32_t in_dtype, const void* q,
+                           int32_t q_dtype, int32_t n_q_heads, float scale, void* out,
+                           void* workspace, uint64_t workspace_bytes, int32_t split_tokens,
+                           uint32_t flags, void* stream) {
+  if (!c) return fail(PKV_EINVAL, "cache is null");
+  if (!k_new != !v_new) return fail(PKV_EINVAL, "k_new and v_new must both be given or both null");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+    return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
+  const Prefix pre{prefix_pages, prefix_len};
+  return attend_impl(c, layer, q, q_dtype, n_q_heads, table, table_stride, lens, batch, max_len,
+                     scale, out, workspace, workspace_bytes, split_tokens, flags, stream, k_new,
+                     v_new, in_dtype, true, &pre);
 }
 
 int pkv_gather(pkv_cache* c, int32_t layer, const int32_t* table_row, int32_t len, void* k_out,

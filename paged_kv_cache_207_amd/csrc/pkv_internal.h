@@ -76,7 +76,24 @@ struct AttendArgs {
   int32_t q_bf16;  // 1: q and out are bf16, 0: float32
   int32_t fuse_combine;  // matrix-core path: 1 = combine in the split pass, 0 = combine kernel
   int32_t single_done;   // combine kernel: single-split sequences are already written
+  // Shared-prefix mode (prefix_len > 0): the first prefix_len tokens of every
+  // sequence sit in the pages prefix_pages lists (the same physical pages in
+  // every table row).  The prefix pass attends over them for all sequences at
+  // once and leaves n_pchunks partials per (sequence, query head) in
+  // ws_pre_o / ws_pre_ml ([batch][n_q_heads][n_pchunks] rows); the split
+  // pass then sees table + prefix_len / page_size and lengths lens -
+  // prefix_len (the private suffixes) and leaves partials for every piece;
+  // the combine merges both.
+  const int32_t* prefix_pages = nullptr;
+  const int32_t* table_full = nullptr;  // the unshifted table (the prefix pass checks its rows)
+  float* ws_pre_o = nullptr;
+  float* ws_pre_ml = nullptr;
+  int32_t prefix_len = 0;
+  int32_t n_pchunks = 0;
 };
+
+// Tokens of the shared prefix per prefix-pass partial.
+constexpr int kPrefixChunk = 256;
 
 // Arguments of the several-queries-per-sequence kernel (one launch = one
 // pkv_paged_attend_multi call).
@@ -160,6 +177,8 @@ constexpr int kMaxMfmaKvHeads = 64;  // split counters: a fixed region of the wo
 bool mfma_supported(int fmt, int q_bf16, int head_dim, int page_size, int group, int batch,
                     int n_kv_heads);
 hipError_t launch_reduce(const AttendArgs& a, const Launch& l);
+// The shared-prefix pass (matrix-core shapes only; hipErrorNotSupported otherwise).
+hipError_t launch_attend_prefix(const AttendArgs& a, int fmt, const Launch& l);
 // Returns hipErrorNotSupported when the shape has no matrix-core variant.
 hipError_t launch_attend_multi(const MultiArgs& a, int fmt, const Launch& l);
 int64_t multi_grid(int batch, int n_kv_heads, int n_qgroups);

@@ -19,9 +19,11 @@ OK, EINVAL, ERANGE, EFORMAT, ENOMEM, EHIP, EDOUBLEFREE = 0, -1, -2, -3, -4, -5, 
 FMT_F32, FMT_BF16, FMT_INT8 = 0, 1, 2
 DT_F32, DT_BF16 = 0, 1
 DEV_WRITE_PAGE, DEV_WRITE_TABLE, DEV_READ_PAGE, DEV_LEN, DEV_QROWS, DEV_WRITE_ROWS = 1, 2, 4, 8, 16, 32
+DEV_PREFIX = 64
 ATTEND_VALU, ATTEND_COMBINE_KERNEL, ATTEND_COMBINE_FUSED = 1, 2, 4
 T_WRITE, T_ATTEND_SPLIT, T_ATTEND_COMBINE, T_GATHER, T_ATTEND_MULTI, T_COPY_PAGES = 0, 1, 2, 3, 4, 5
-T_COUNT = 6
+T_ATTEND_PREFIX = 6
+T_COUNT = 7
 
 FORMAT_CODE = {"f32": FMT_F32, "bf16": FMT_BF16, "int8": FMT_INT8}
 DTYPE_CODE = {torch.float32: DT_F32, torch.bfloat16: DT_BF16}
@@ -46,6 +48,11 @@ SYMBOLS = [
     ("pkv_decode_step", C.c_int,
      [_P, _I32, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _I32, _I32, _F, _P, _P, _U64, _I32,
       _U32, _P]),
+    ("pkv_prefix_workspace_size", C.c_int,
+     [_P, _I32, _I32, _I32, _I32, _I32, C.POINTER(C.c_uint64)]),
+    ("pkv_decode_step_prefix", C.c_int,
+     [_P, _I32, _P, _I32, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _I32, _F, _P, _P, _U64,
+      _I32, _U32, _P]),
     ("pkv_paged_attend_multi", C.c_int,
      [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _F, _P, _P]),
     ("pkv_gather", C.c_int, [_P, _I32, _P, _I32, _P, _P, _P, _P, _P]),
@@ -307,6 +314,49 @@ class PagedKVCache:
             split_tokens, flags, _stream(self.device)))
         return out
 
+    # -- a shared prefix read once for every sequence ---------------------------
+    def prefix_workspace(self, batch, n_q_heads, max_len, prefix_len, split_tokens=0):
+        n = C.c_uint64()
+        _check(lib().pkv_prefix_workspace_size(self._h, batch, n_q_heads, max_len, prefix_len,
+                                               split_tokens, C.byref(n)))
+        return torch.zeros(max(n.value, 1), dtype=torch.uint8, device=self.device)
+
+    def decode_step_prefix(self, table, lens, max_len: int, prefix_pages, prefix_len: int, q,
+                           scale: float, k_new=None, v_new=None, out=None, workspace=None,
+                           split_tokens: int = 0, flags: int = 0,
+                           layer: int = 0) -> torch.Tensor:
+        """Attention of one query per sequence whose first prefix_len tokens sit
+        in the shared pages prefix_pages (device int32, prefix_len / page_size
+        ids, the same first entries in every table row): the shared pages are
+        read once for all sequences.  With k_new / v_new (bf16 [B, Hkv, D])
+        each sequence first gets its new row at lens[b] - 1, as decode_step."""
+        self._check_decode_shapes(q, table, lens, out)
+        B, Hq, D = q.shape
+        if q.dtype not in DTYPE_CODE:
+            raise ValueError("q must be float32 or bfloat16")
+        if (k_new is None) != (v_new is None):
+            raise ValueError("give both k_new and v_new, or neither")
+        if k_new is not None:
+            if tuple(k_new.shape) != (B, self.n_kv_heads, self.head_dim) or v_new.shape != k_new.shape:
+                raise ValueError("k_new and v_new must be [batch, n_kv_heads, head_dim]")
+            if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+                raise ValueError("k_new and v_new must be bfloat16")
+        if prefix_pages.dim() != 1 or prefix_pages.shape[0] * self.page_size < prefix_len:
+            raise ValueError("prefix_pages must list prefix_len / page_size pages")
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = self.prefix_workspace(B, Hq, max_len, prefix_len, split_tokens)
+        _check(lib().pkv_decode_step_prefix(
+            self._h, layer, _dev(table, torch.int32, "table"), table.shape[1],
+            _dev(lens, torch.int32, "lens"), B, max_len,
+            _dev(prefix_pages, torch.int32, "prefix_pages"), prefix_len,
+            _dev(k_new, name="k_new"), _dev(v_new, name="v_new"), DT_BF16,
+            _dev(q, name="q"), DTYPE_CODE[q.dtype], Hq, float(scale), _dev(out, q.dtype, "out"),
+            _dev(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
+            split_tokens, flags, _stream(self.device)))
+        return out
+
     # -- several queries per sequence (a chunk of new tokens) -------------------
     def attend_multi(self, q, table, lens, cu_q, max_q: int, max_len: int, scale: float,
                      out=None, layer: int = 0) -> torch.Tensor:
@@ -352,7 +402,7 @@ class PagedKVCache:
         n = (C.c_int32 * T_COUNT)()
         _check(lib().pkv_timing_read(self._h, ms, n))
         names = ["write", "attend_split", "attend_combine", "gather", "attend_multi",
-                 "copy_pages"]
+                 "copy_pages", "attend_prefix"]
         return {k: (ms[i], n[i]) for i, k in enumerate(names)}
 
     # -- gather ------------------------------------------------------------------

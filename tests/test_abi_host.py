@@ -350,3 +350,39 @@ def test_gather_and_table_validation():
     assert L.pkv_table_apply(P, 0, 2, P, 3, None) == pkv.EINVAL
     assert L.pkv_table_apply(P, 4, 2, P, 0, None) == pkv.OK
     L.pkv_cache_destroy(h)
+
+
+def test_prefix_validation():
+    L, h = _cache()  # bf16 pages, Hkv 2, D 64, bs 16, 16 pages
+    P = C.c_void_p(FAKE)
+    need = C.c_uint64()
+    assert L.pkv_prefix_workspace_size(h, 2, 4, 50, 32, 0, C.byref(need)) == pkv.OK
+    plain = C.c_uint64()
+    assert L.pkv_attend_workspace_size(h, 2, 4, 50, 0, C.byref(plain)) == pkv.OK
+    assert need.value > plain.value - (1 << 20)  # room for the prefix partials as well
+    assert L.pkv_prefix_workspace_size(h, 2, 4, 50, 0, 0, C.byref(need)) == pkv.EINVAL
+    assert L.pkv_prefix_workspace_size(h, 2, 4, 50, 32, 0, C.byref(need)) == pkv.OK
+
+    def s(prefix_len=32, flags=0, k=None, v=None, in_dt=pkv.DT_BF16, hq=4, pages=P,
+          ws_bytes=None, q_dt=pkv.DT_BF16, batch=2):
+        return L.pkv_decode_step_prefix(h, 0, P, 4, P, batch, 50, pages, prefix_len, k, v, in_dt,
+                                        P, q_dt, hq, 0.125, P, P,
+                                        need.value if ws_bytes is None else ws_bytes, 0, flags,
+                                        None)
+
+    assert s(prefix_len=0) == pkv.EINVAL
+    assert s(prefix_len=24) == pkv.EINVAL  # not a multiple of the page size
+    assert s(prefix_len=80) == pkv.EINVAL  # past the 4-page table row
+    assert s(flags=pkv.ATTEND_VALU) == pkv.EINVAL
+    assert s(flags=pkv.ATTEND_COMBINE_FUSED) == pkv.EINVAL
+    assert s(hq=34) == pkv.EFORMAT  # 17 query heads per KV head
+    assert s(q_dt=pkv.DT_F32) == pkv.EFORMAT
+    assert s(k=P) == pkv.EINVAL  # k_new without v_new
+    assert s(k=P, v=P, in_dt=pkv.DT_F32) == pkv.EFORMAT
+    assert s(pages=None) == pkv.EINVAL
+    assert s(ws_bytes=need.value - 1) == pkv.ENOMEM
+    assert s(batch=0) == pkv.OK
+    L.pkv_cache_destroy(h)
+    L, h = _cache(fmt=pkv.FMT_F32)
+    assert s() == pkv.EFORMAT  # no matrix-core kernels for f32 pages
+    L.pkv_cache_destroy(h)

@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
-"""Paged KV cache decode step on one MI355X.
+"""Paged KV cache decode steps on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_bf16]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all]
 
 A step is one pass of the hot path over the batch: one pkv_decode_step call
 that writes one new K/V row per sequence (at position len-1, the newest
@@ -10,11 +10,19 @@ per sequence over all len tokens, read in place through a fully fragmented
 block table.  The K/V pages are filled once before timing.  Prints one JSON
 line (stdout); details go to stderr.
 
+The default run measures the headline (the 32k-token bf16 workload: 8
+sequences x 32 768 tokens, 64 query / 8 KV heads, head_dim 128, 16-token
+pages) and, under "configs", the other four workloads: the tiny f32 one, the
+uneven bf16 decode batch, the int8 batch and the shared-prefix job (32 steps
+of host table growth + decode step with the shared pages read once).  Each
+carries its own timing, roofline fraction and CPU-oracle baseline.
+
 Timing: W warmup steps, then K steps back to back between two
 synchronisations (the timed region: value, ms_per_step); then the same K
 steps again with the library's kernel events, whose dispatch-stamped
-durations give the split-K kernel's average (roofline.achieved); then K
-steps each after a 512 MiB read-only sweep of the caches (cold_cache).
+durations give the split-K kernel's average (roofline.achieved); for the
+headline also K steps each after a 512 MiB read-only sweep of the caches
+(cold_cache).
 
 value = KV bytes the attention reads per step / step time (GB/s);
 roofline = the split-K partial kernel (the dominant one): its algorithmic
@@ -184,49 +192,68 @@ def load_traffic(workload: str):
     return t.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, ks, vs, q, budget_s: float):
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    decode steps of whole sequences (the oracle page write of the step's row,
-    then its float64 gather and attention over every query head), repeated
-    over the batch until about budget_s of CPU time has been spent."""
-    from oracle import OracleCache, attend
+def host_threads():
+    """(cores this process may run on, BLAS threads NumPy uses)."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        threads = 1
+        blas = int(os.environ.get("OMP_NUM_THREADS", "1") or 1)
+    return len(os.sched_getaffinity(0)), int(blas)
+
+
+def cpu_baseline(w, ks, vs, q, budget_s: float, lens=None, note=""):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    decode steps of whole sequences (the oracle page write of the step's row,
+    then its float64 gather and attention over every query head), sequence
+    after sequence, until about budget_s of CPU time has been spent.  ks[b] /
+    vs[b] hold sequence b's rows, lens[b] (default w.lens) its length after
+    the step; each sequence's other rows are written untimed first."""
+    from oracle import OracleCache, attend
+    cores, blas = host_threads()
+
     def bits(t):
         t = t.contiguous()
         return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
     in_dt = "bf16" if w.in_dtype == torch.bfloat16 else "f32"
     q_dt = "bf16" if w.q_dtype == torch.bfloat16 else "f32"
     qb = bits(q)
-    caches = []
-    for b in range(w.batch):  # untimed: the pages as the GPU holds them before the step
-        L = int(w.lens[b])
-        npg = -(-L // w.page_size)
-        oc = OracleCache(1, npg, w.page_size, w.n_kv_heads, w.head_dim, w.kv_format)
-        table = np.arange(npg, dtype=np.int32)[None]
-        kb, vb = bits(ks[b]), bits(vs[b])
-        oc.write(0, table, [0], [0, L - 1], kb[:L - 1], vb[:L - 1], in_dt)
-        caches.append((oc, table, kb[L - 1:L], vb[L - 1:L], L))
-    per_tok = kv_bytes(w) // max(int(w.lens.astype(np.int64).sum()), 1)  # K/V (+ scales) bytes
-    elapsed, steps, kv_done = 0.0, 0, 0
+    lens = w.lens if lens is None else lens
+    elem = {"f32": 4, "bf16": 2, "int8": 1}[w.kv_format]
+    per_tok = w.n_kv_heads * w.head_dim * elem * 2 + (w.n_kv_heads * 8 if w.kv_format == "int8"
+                                                     else 0)
+    caches = {}
+
+    def state(b):  # untimed: the pages as the GPU holds them before the step
+        if b not in caches:
+            L = int(lens[b])
+            npg = -(-L // w.page_size)
+            oc = OracleCache(1, npg, w.page_size, w.n_kv_heads, w.head_dim, w.kv_format)
+            table = np.arange(npg, dtype=np.int32)[None]
+            kb, vb = bits(ks[b]), bits(vs[b])
+            oc.write(0, table, [0], [0, L - 1], kb[:L - 1], vb[:L - 1], in_dt)
+            caches[b] = (oc, table, kb[L - 1:L], vb[L - 1:L], L)
+        return caches[b]
+    live = [b for b in range(w.batch) if int(lens[b]) > 0]
+    elapsed, steps, kv_done, i = 0.0, 0, 0, 0
     while elapsed < budget_s:
-        for b, (oc, table, kr, vr, L) in enumerate(caches):
-            t0 = time.perf_counter()
-            oc.write(0, table, [L - 1], [0, 1], kr, vr, in_dt)
-            attend(oc, 0, qb[b:b + 1], q_dt, table, np.array([L]), w.scale)
-            elapsed += time.perf_counter() - t0
-            steps += 1
-            kv_done += L * per_tok
+        b = live[i % len(live)]
+        i += 1
+        oc, table, kr, vr, L = state(b)
+        t0 = time.perf_counter()
+        oc.write(0, table, [L - 1], [0, 1], kr, vr, in_dt)
+        attend(oc, 0, qb[b:b + 1], q_dt, table, np.array([L]), w.scale)
+        elapsed += time.perf_counter() - t0
+        steps += 1
+        kv_done += L * per_tok
+    lo, hi = int(min(lens[b] for b in live)), int(max(lens[b] for b in live))
     return {"value": round(kv_done / elapsed / 1e9, 4), "unit": "GB/s",
-            "tokens_per_s": round(steps / elapsed, 3), "cores": int(threads), "kind": "oracle",
-            "sample": f"{steps} sequence decode steps over the {w.batch} sequences of the "
-                      f"workload ({int(w.lens.min())}..{int(w.lens.max())} tokens, all "
-                      f"{w.n_q_heads} query heads each): "
-                      f"oracle page write of the step's row + float64 gather and attention; "
-                      f"{elapsed:.1f} s of CPU time"}
+            "tokens_per_s": round(steps / elapsed, 3), "cores": blas, "kind": "oracle",
+            "host_cores": cores, "blas_threads": blas,
+            "sample": f"{steps} sequence decode steps over the {len(live)} non-empty sequences "
+                      f"of the workload ({lo}..{hi} tokens, all {w.n_q_heads} query heads "
+                      f"each): oracle page write of the step's row + float64 gather and "
+                      f"attention; {elapsed:.1f} s of CPU time" + note}
 
 
 def gather_compare(w, cache, table, device, reps=5):
@@ -263,21 +290,27 @@ def gather_compare(w, cache, table, device, reps=5):
             "gather_GBps_read_plus_write": round(moved / (per_batch_ms / 1e3) / 1e9, 1)}
 
 
-def run_shared_prefix(args, device):
+def run_shared_prefix(args, device, cpu_seconds: float = 0.0):
     """The shared-prefix workload as one job of n_steps decode steps after the
     fill.  Each step = host table growth (pool-backed block tables: a sequence
     whose length reaches a page boundary gets the lowest free page; the new
     entries go to the device as update triples) + paged_write of one row per
-    sequence at its length + paged_attend over length + 1 tokens.  Every timed
-    job starts from the same rebuilt pool state (untimed)."""
+    sequence at its length + paged_attend over length + 1 tokens.  The
+    attention reads the 64 shared prefix pages once for all sequences
+    (pkv_decode_step_prefix: a prefix pass over the shared pages, the split
+    pass over the private suffixes, the combine); the same job through
+    pkv_decode_step, which streams the prefix once per sequence, is timed
+    beside it.  Every timed job starts from the same rebuilt pool state
+    (untimed)."""
     sp = W.shared_prefix()
     w = sp.base
     B, bs = w.batch, w.page_size
+    P0 = sp.prefix_tokens
 
     def build_tables():
         pool = pkv.PagePool(w.n_pages)
         seqs = pkv.SeqTables(pool, B, w.table_stride, bs)
-        seqs.append(0, sp.prefix_tokens)
+        seqs.append(0, P0)
         for b in range(1, B):
             seqs.share(b, 0, sp.prefix_pages)
         for b in range(B):
@@ -288,6 +321,8 @@ def run_shared_prefix(args, device):
     pool, seqs = build_tables()
     pkv.table_apply(table, seqs.take_updates().to(device))
     prefix_refs = pool.refcount(seqs.table()[0][0])
+    seqs.close()
+    pool.close()
     cache = pkv.PagedKVCache(w.n_pages, bs, w.n_kv_heads, w.head_dim, w.kv_format, device=device)
     for r in sp.fill_rounds():
         cache.write(table, torch.as_tensor(r.start_pos).to(device),
@@ -295,63 +330,77 @@ def run_shared_prefix(args, device):
     ks, vs = sp.step_rows_all()
     ks, vs = ks.to(device), vs.to(device)
     qs = torch.stack([w.query(step=s) for s in range(sp.n_steps)]).to(device)
-    cu = torch.arange(B + 1, dtype=torch.int32, device=device)
     lens_all = torch.stack([torch.as_tensor(sp.step_lens(s)) for s in range(sp.n_steps)]).to(device)
-    start_all = (lens_all - 1).contiguous()
     max_len = int(sp.step_lens(sp.n_steps - 1).max())
-    split = 0  # the library's plan
-    ws = cache.workspace(B, w.n_q_heads, max_len, split)
+    # every table row lists the shared pages first: row 0's entries are the list
+    prefix_pages = table[0, :sp.prefix_pages]
+    ws_pre = cache.prefix_workspace(B, w.n_q_heads, max_len, P0)
+    ws_seq = cache.workspace(B, w.n_q_heads, max_len)
     out = torch.empty_like(qs[0])
-    # one pinned buffer per step: a step's host-to-device copy may still be
-    # pending when the host prepares the next step's updates
     upd_host = [torch.empty((B + 8, 3), dtype=torch.int32).pin_memory()
                 for _ in range(sp.n_steps)]
     torch.cuda.synchronize()
-
     ones = np.ones(B, np.int32)
 
-    def job(seqs):
+    def step(s, shared):
+        if shared:
+            cache.decode_step_prefix(table, lens_all[s], max_len, prefix_pages, P0, qs[s],
+                                     w.scale, k_new=ks[s], v_new=vs[s], out=out,
+                                     workspace=ws_pre)
+        else:
+            cache.decode_step(table, lens_all[s], max_len, ks[s], vs[s], qs[s], w.scale,
+                              out=out, workspace=ws_seq)
+
+    def fresh():
+        pool, seqs = build_tables()
+        table.fill_(-1)
+        pkv.table_apply(table, seqs.take_updates().to(device))
+        torch.cuda.synchronize()
+        return pool, seqs
+
+    def job(seqs, shared):
         for s in range(sp.n_steps):
             seqs.append_all(ones)  # every sequence grows by its new token
             n = seqs.take_updates(upd_host[s]).shape[0]
             if n:  # the kernel reads the step's pinned list in place
                 pkv.table_apply(table, upd_host[s][:n])
-            cache.decode_step(table, lens_all[s], max_len, ks[s], vs[s], qs[s], w.scale,
-                              out=out, workspace=ws, split_tokens=split)
+            step(s, shared)
 
     jobs = max(1, args.steps)
-    times = []
-    # warmup jobs, the timed jobs, then one more job with the library's
-    # kernel events on (for the split-pass duration only)
-    for rep in range(args.warmup + jobs + 1):
-        if rep:
+    res = {}
+    for shared in (True, False):
+        times = []
+        # warmup jobs, the timed jobs, then one more job with the library's
+        # kernel events on (for the kernel durations only)
+        for rep in range(args.warmup + jobs + 1):
+            pool, seqs = fresh()
+            timed = args.warmup <= rep < args.warmup + jobs
+            if rep == args.warmup + jobs:
+                cache.timing_read()
+                cache.timing(True)
+            t0 = time.perf_counter()
+            job(seqs, shared)
+            torch.cuda.synchronize()
+            if timed:
+                times.append(time.perf_counter() - t0)
+            if rep == 0:
+                assert seqs.lens() == [int(x) for x in sp.step_lens(sp.n_steps - 1)]
+                assert cache.status() == 0
             seqs.close()
             pool.close()
-            pool, seqs = build_tables()
-            table.fill_(-1)
-            pkv.table_apply(table, seqs.take_updates().to(device))
-        torch.cuda.synchronize()
-        timed = args.warmup <= rep < args.warmup + jobs
-        if rep == args.warmup + jobs:
-            cache.timing_read()
-            cache.timing(True)
-        t0 = time.perf_counter()
-        job(seqs)
-        torch.cuda.synchronize()
-        if timed:
-            times.append(time.perf_counter() - t0)
-        if rep == 0:
-            assert seqs.lens() == [int(x) for x in sp.step_lens(sp.n_steps - 1)]
-            assert cache.status() == 0
-    cache.timing(False)
-    t = cache.timing_read()
-    seqs.close()
-    pool.close()
-    job_s = float(np.mean(times))
+        cache.timing(False)
+        t = cache.timing_read()
+        res[shared] = {"job_s": float(np.mean(times)),
+                       "kern": {k: (v[0] / max(v[1], 1)) for k, v in t.items()},
+                       "last_out": out.clone()}
+    assert cache.status() == 0
+    # the two paths compute the same attention: agreement within the bf16 tolerance
+    diff = float((res[True]["last_out"].float() - res[False]["last_out"].float()).abs().max())
+    assert diff <= 2e-2, diff
 
-    # The same job with each step's device work replayed from a HIP graph
-    # captured once (padded update list of fixed size: padding rows name no
-    # sequence and are skipped), the host table growth still done per step.
+    # The shared-prefix job with each step's device work replayed from a HIP
+    # graph captured once (padded update list of fixed size: padding rows
+    # name no sequence and are skipped), the host table growth still per step.
     cap = B + 8
     g_upd_host = [torch.full((cap, 3), -1, dtype=torch.int32).pin_memory()
                   for _ in range(sp.n_steps)]
@@ -362,8 +411,7 @@ def run_shared_prefix(args, device):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=g_stream):
                 pkv.table_apply(table, g_upd_host[s])  # reads the pinned list in place
-                cache.decode_step(table, lens_all[s], max_len, ks[s], vs[s], qs[s], w.scale,
-                                  out=out, workspace=ws, split_tokens=split)
+                step(s, True)
             graphs.append(g)
     torch.cuda.synchronize()
 
@@ -376,32 +424,41 @@ def run_shared_prefix(args, device):
 
     g_times = []
     for rep in range(args.warmup + jobs):
-        pool, seqs = build_tables()
-        table.fill_(-1)
-        pkv.table_apply(table, seqs.take_updates().to(device))
-        torch.cuda.synchronize()
+        pool, seqs = fresh()
         t0 = time.perf_counter()
         graph_job(seqs)
         torch.cuda.synchronize()
         if rep >= args.warmup:
             g_times.append(time.perf_counter() - t0)
+        # the replayed job leaves the tables the host grew and the eager
+        # job's last output, bit for bit
+        assert table.cpu().tolist() == seqs.table()
+        assert torch.equal(out, res[True]["last_out"])
         seqs.close()
         pool.close()
     assert cache.status() == 0
     graph_job_s = float(np.mean(g_times))
-    log(f"shared_prefix job with per-step graphs: {graph_job_s * 1e3:.3f} ms")
     lens_steps = [sp.step_lens(s).astype(np.int64) for s in range(sp.n_steps)]
     per_tok = w.n_kv_heads * w.head_dim * 2 * 2
     logical = sum(int(l.sum()) for l in lens_steps) * per_tok
-    unique = sum(int((l - sp.prefix_tokens).sum()) + sp.prefix_tokens for l in lens_steps) * per_tok
-    split_ms, split_n = t["attend_split"]
-    split_s = split_ms / split_n / 1e3
-    unique_per_launch = unique / sp.n_steps
-    log(f"shared_prefix job: {job_s * 1e3:.3f} ms for {sp.n_steps} steps; split pass "
-        f"{split_ms / split_n * 1e3:.1f} us avg; prefix page refcount {prefix_refs}")
-    # the job as a serving loop would drive it: each step's device work
-    # replayed from its captured graph (the eager job pays a Python launch
-    # cost per call on top, reported beside it)
+    private = sum(int((l - P0).sum()) for l in lens_steps) * per_tok
+    unique = private + sp.n_steps * P0 * per_tok
+    kp, ks_ = res[True]["kern"], res[False]["kern"]
+    split_s, comb_s = kp["attend_split"] / 1e3, kp["attend_combine"] / 1e3
+    attn_s = split_s + comb_s
+    # the split launch's algorithmic bytes: the private K/V and their table
+    # entries, the shared pages once (read by its prefix waves) and their
+    # table entries, the queries and the new rows it reads and stores
+    priv_pages = sum(int((-(-(l) // bs)).sum()) - B * sp.prefix_pages for l in lens_steps)
+    qb = B * w.n_q_heads * w.head_dim * 2
+    rows = B * w.n_kv_heads * w.head_dim * 2 * (2 + 2)
+    split_bytes = ((private + 4 * priv_pages) / sp.n_steps + P0 * per_tok + 4 * sp.prefix_pages
+                   + qb + rows)
+    log(f"shared_prefix: job {graph_job_s * 1e3:.3f} ms (graphs), eager "
+        f"{res[True]['job_s'] * 1e3:.3f} ms; per step: split pass with prefix waves "
+        f"{split_s * 1e6:.1f} us, combine {comb_s * 1e6:.1f} us; per-sequence path: split "
+        f"{ks_['attend_split'] * 1e3:.1f} us, combine {ks_['attend_combine'] * 1e3:.1f} us, job "
+        f"{res[False]['job_s'] * 1e3:.3f} ms eager; prefix refcount {prefix_refs}")
     line = {
         "metric": METRIC, "value": round(unique / graph_job_s / 1e9, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": jobs, "warmup": args.warmup,
@@ -412,29 +469,54 @@ def run_shared_prefix(args, device):
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "page_size": bs,
                    "prefix_pages": sp.prefix_pages, "suffix": "uniform [16, 2048]",
                    "step": f"one job = {sp.n_steps} decode steps (host table growth + "
-                           "decode_step: paged_write 1 row/seq + paged_attend, one call)",
-                   "split_tokens": split, "schedule": schedule_name(cache, w, max_len, split),
+                           "decode_step_prefix: paged_write 1 row/seq + paged_attend with the "
+                           "shared prefix read once, one call)",
                    "value_bytes": "unique KV bytes (shared prefix once)"},
         "tokens_per_s": round(B * sp.n_steps / graph_job_s, 1),
         "logical_kv_GBps": round(logical / graph_job_s / 1e9, 2),
         "job": "each step: host table growth (append_all, take_updates), then the step's "
                "padded table update (table_apply reading the pinned list in place) and "
-               "decode_step replayed from a HIP graph captured once",
-        "eager": {"ms_per_job": round(job_s * 1e3, 5),
-                  "GBps_unique": round(unique / job_s / 1e9, 2),
+               "decode_step_prefix replayed from a HIP graph captured once",
+        "eager": {"ms_per_job": round(res[True]["job_s"] * 1e3, 5),
+                  "GBps_unique": round(unique / res[True]["job_s"] / 1e9, 2),
                   "note": "the same job with every library call launched from Python"},
         "pct_hbm_peak": round(100 * unique / graph_job_s / 1e9 / HBM_PEAK_GBPS, 2),
-        "roofline": {"bound": "hbm", "achieved": round(unique_per_launch / split_s / 1e9, 2),
+        "attention_per_step_us": {"split_pass_with_prefix_waves": round(split_s * 1e6, 2),
+                                  "combine": round(comb_s * 1e6, 2),
+                                  "total": round(attn_s * 1e6, 2),
+                                  "unique_GBps": round(unique / sp.n_steps / attn_s / 1e9, 2)},
+        "per_sequence_path": {
+            "ms_per_job_eager": round(res[False]["job_s"] * 1e3, 5),
+            "split_pass_us": round(ks_["attend_split"] * 1e3, 2),
+            "combine_us": round(ks_["attend_combine"] * 1e3, 2),
+            "note": "pkv_decode_step over the same tables: every sequence streams the shared "
+                    "prefix itself"},
+        "roofline": {"bound": "hbm", "achieved": round(split_bytes / split_s / 1e9, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(unique_per_launch / split_s / 1e9 / HBM_PEAK_GBPS, 4),
-                     "traffic": None,
-                     "achieved_logical": round(logical / sp.n_steps / split_s / 1e9, 2),
+                     "frac": round(split_bytes / split_s / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": load_traffic(w.name),
+                     "kernel": "attend_mfma (split-K partial pass over the private suffixes, "
+                               "with the shared-prefix waves in the same launch)",
                      "avg_launch_us": round(split_s * 1e6, 2),
-                     "note": "split pass: the steps' mean unique KV bytes (shared prefix "
-                             "counted once) over its mean launch time; achieved_logical counts "
-                             "the prefix once per sequence"},
-        "cpu_baseline": None,
+                     "bytes_per_launch": int(split_bytes),
+                     "note": "the dominant kernel: the private K/V of a step and their table "
+                             "entries, the shared pages once, the queries and the new rows, over "
+                             "its mean launch time"},
     }
+    if cpu_seconds > 0:
+        pk, pv = sp.prefix_kv()
+        kl, vl = [], []
+        for b in range(B):
+            k, v = sp.private_kv(b)
+            n = int(sp.suffix[b]) + 1
+            kl.append(torch.cat([pk, k[:n]]))
+            vl.append(torch.cat([pv, v[:n]]))
+        line["cpu_baseline"] = cpu_baseline(w, kl, vl, qs[0].cpu(), cpu_seconds,
+                                            lens=sp.step_lens(0),
+                                            note="; the shared prefix is part of every "
+                                                 "sequence's own oracle copy")
+    else:
+        line["cpu_baseline"] = None
     return line
 
 
@@ -624,45 +706,19 @@ def run_chunked_prefill(args, device, kv_format="bf16"):
     }
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="long_bf16")
-    ap.add_argument("--split", type=int, default=0, help="split tokens (0 = library plan)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--separate-write", action="store_true",
-                    help="run the step as pkv_paged_write + pkv_paged_attend instead of one "
-                         "pkv_decode_step call")
-    ap.add_argument("--gather-compare", type=int, default=1,
-                    help="1: also time gathering every sequence into a contiguous copy")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for {args.gpus}); this library has no "
-              "multi-GPU path: run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
-    device = torch.device("cuda:0")
-    if args.workload == "shared_prefix":
-        print(json.dumps(run_shared_prefix(args, device)), flush=True)
-        return
-    if args.workload in ("chunked_prefill", "chunked_prefill_int8"):
-        fmt = "int8" if args.workload.endswith("int8") else "bf16"
-        print(json.dumps(run_chunked_prefill(args, device, fmt)), flush=True)
-        return
-    if args.workload == "fork_copy":
-        print(json.dumps(run_fork_copy(args, device)), flush=True)
-        return
-    w = W.by_name(args.workload)
+def run_decode(args, device, name: str, headline: bool, cpu_seconds: float):
+    """One decode workload: fill its pages, then W warmup steps and K timed
+    steps of pkv_decode_step (one row written per sequence, one query per
+    sequence attending over all its tokens).  The headline run also measures
+    the streaming probes, cold-cache steps and the gather comparison."""
+    w = W.by_name(name)
     log(f"workload {w.name}: B={w.batch} lens={int(w.lens.min())}..{int(w.lens.max())} "
         f"Hq={w.n_q_heads} Hkv={w.n_kv_heads} D={w.head_dim} bs={w.page_size} P={w.n_pages}")
 
-    read_gbps = read_probe(device)
-    copy_gbps = calibration_copy(device)
-    log(f"probe: streaming read {read_gbps:.0f} GB/s, copy {copy_gbps:.0f} GB/s")
+    if headline:
+        read_gbps = read_probe(device)
+        copy_gbps = calibration_copy(device)
+        log(f"probe: streaming read {read_gbps:.0f} GB/s, copy {copy_gbps:.0f} GB/s")
 
     cache = pkv.PagedKVCache(w.n_pages, w.page_size, w.n_kv_heads, w.head_dim, w.kv_format,
                              device=device)
@@ -684,10 +740,11 @@ def main():
     split = args.split  # 0: the library's plan
     schedule = schedule_name(cache, w, max_len, split)
     ws = cache.workspace(B, w.n_q_heads, max_len, split)
-    sweep_buf = torch.empty(512 << 20, dtype=torch.uint8, device=device)
-    sweep_buf.fill_(7)
-    sweep_sink = torch.empty(pkv.lib().pkv_probe_blocks(sweep_buf.numel()), dtype=torch.float32,
-                             device=device)
+    if headline:  # the read-only sweep that flushes the caches between cold steps
+        sweep_buf = torch.empty(512 << 20, dtype=torch.uint8, device=device)
+        sweep_buf.fill_(7)
+        sweep_sink = torch.empty(pkv.lib().pkv_probe_blocks(sweep_buf.numel()),
+                                 dtype=torch.float32, device=device)
 
     def step():
         if args.separate_write:
@@ -729,35 +786,34 @@ def main():
     kt = kernel_times()
     split_avg = kt["attend_split"]
 
-    # (3) cold caches: each step after a 512 MiB read-only sweep (which leaves
-    # no dirty lines behind), kernels timed by the library's events: whether
-    # the back-to-back steps gain anything from data left in the caches
-    cache.timing(True)
-    for i in range(args.steps):
-        pkv.probe_stream(sweep_buf, sink=sweep_sink)
-        step()
-    torch.cuda.synchronize()
-    cache.timing(False)
-    kt_cold = kernel_times()
+    if headline:
+        # (3) cold caches: each step after a 512 MiB read-only sweep (which leaves
+        # no dirty lines behind), kernels timed by the library's events: whether
+        # the back-to-back steps gain anything from data left in the caches
+        cache.timing(True)
+        for i in range(args.steps):
+            pkv.probe_stream(sweep_buf, sink=sweep_sink)
+            step()
+        torch.cuda.synchronize()
+        cache.timing(False)
+        kt_cold = kernel_times()
 
-    # (4) the same cold steps timed one by one with events on the stream (no
-    # library timing): median and minimum step time with flushed caches
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for ea, eb in evs:
-        pkv.probe_stream(sweep_buf, sink=sweep_sink)
-        ea.record()
-        step()
-        eb.record()
-    torch.cuda.synchronize()
-    cold_steps = sorted(ea.elapsed_time(eb) * 1e3 for ea, eb in evs)
+        # (4) the same cold steps timed one by one with events on the stream (no
+        # library timing): median and minimum step time with flushed caches
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for ea, eb in evs:
+            pkv.probe_stream(sweep_buf, sink=sweep_sink)
+            ea.record()
+            step()
+            eb.record()
+        torch.cuda.synchronize()
+        cold_steps = sorted(ea.elapsed_time(eb) * 1e3 for ea, eb in evs)
     assert cache.status() == 0
     comb_avg, wr_avg = kt["attend_combine"], kt["write"]
-    log(f"step: {ms_per_step * 1e3:.1f} us back to back (wall {wall_ms * 1e3:.1f} us); "
+    log(f"{w.name} step: {ms_per_step * 1e3:.1f} us back to back (wall {wall_ms * 1e3:.1f} us); "
         f"split pass {split_avg * 1e3:.1f} us, combine {comb_avg * 1e3:.1f} us, write "
-        f"{wr_avg * 1e3:.1f} us; after a cache sweep: split pass "
-        f"{kt_cold['attend_split'] * 1e3:.1f} us, combine "
-        f"{kt_cold['attend_combine'] * 1e3:.1f} us; {schedule}")
+        f"{wr_avg * 1e3:.1f} us; {schedule}")
 
     kvb = kv_bytes(w)
     value = kvb / (ms_per_step / 1e3) / 1e9
@@ -778,16 +834,7 @@ def main():
         "tokens_per_s": round(B / (ms_per_step / 1e3), 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "kv_bytes_per_step": kvb,
-        "achievable_read_GBps": round(read_gbps, 1),
-        "split_pass_frac_of_achievable_read": round(achieved / read_gbps, 4),
         "wall_ms_per_step": round(wall_ms, 5),
-        "cold_cache": {"split_pass_us": round(kt_cold["attend_split"] * 1e3, 2),
-                       "combine_us": round(kt_cold["attend_combine"] * 1e3, 2),
-                       "step_us_median": round(float(np.median(cold_steps)), 2),
-                       "step_us_min": round(cold_steps[0], 2),
-                       "note": "each step follows a 512 MiB read-only sweep of the caches: "
-                               "kernel durations from the library's events, step median and "
-                               "minimum from events on the stream around each step"},
         "fill_write": fill_info,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -795,14 +842,88 @@ def main():
                      "avg_launch_us": round(split_avg * 1e3, 2),
                      "timing": "library kernel events over a second run of the K steps"},
     }
-    if args.gather_compare:
-        line["gather_compare"] = gather_compare(w, cache, table, device)
-        line["gather_compare"]["inplace_attend_us"] = round((split_avg + comb_avg) * 1e3, 2)
-        log(f"gather compare: {line['gather_compare']}")
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, ks, vs, q_host, args.cpu_seconds)
-    else:
-        line["cpu_baseline"] = None
+    if headline:
+        line["achievable_read_GBps"] = round(read_gbps, 1)
+        line["split_pass_frac_of_achievable_read"] = round(achieved / read_gbps, 4)
+        line["cold_cache"] = {
+            "split_pass_us": round(kt_cold["attend_split"] * 1e3, 2),
+            "combine_us": round(kt_cold["attend_combine"] * 1e3, 2),
+            "step_us_median": round(float(np.median(cold_steps)), 2),
+            "step_us_min": round(cold_steps[0], 2),
+            "note": "each step follows a 512 MiB read-only sweep of the caches: kernel "
+                    "durations from the library's events, step median and minimum from events "
+                    "on the stream around each step"}
+        log(f"after a cache sweep: split pass {kt_cold['attend_split'] * 1e3:.1f} us, combine "
+            f"{kt_cold['attend_combine'] * 1e3:.1f} us")
+        if args.gather_compare:
+            line["gather_compare"] = gather_compare(w, cache, table, device)
+            line["gather_compare"]["inplace_attend_us"] = round((split_avg + comb_avg) * 1e3, 2)
+            log(f"gather compare: {line['gather_compare']}")
+    line["cpu_baseline"] = (cpu_baseline(w, ks, vs, q_host, cpu_seconds) if cpu_seconds > 0
+                            else None)
+    del cache, table, ks, vs
+    torch.cuda.empty_cache()
+    return line
+
+
+def compact(line: dict) -> dict:
+    """The fields a config keeps inside the headline line."""
+    keep = ("value", "unit", "ms_per_step", "tokens_per_s", "pct_hbm_peak", "dtype", "config",
+            "kv_bytes_per_step", "roofline", "cpu_baseline", "logical_kv_GBps",
+            "attention_per_step_us", "per_sequence_path", "eager")
+    return {k: line[k] for k in keep if k in line}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="all",
+                    help="all (the 32k-token headline plus the other four configs), or one of "
+                         "long_bf16, tiny_f32, decode_bf16, int8_kv, shared_prefix, "
+                         "chunked_prefill, chunked_prefill_int8, fork_copy")
+    ap.add_argument("--split", type=int, default=0, help="split tokens (0 = library plan)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle time for the headline's CPU baseline")
+    ap.add_argument("--config-cpu-seconds", type=float, default=4.0,
+                    help="oracle time for each other config's CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="run the step as pkv_paged_write + pkv_paged_attend instead of one "
+                         "pkv_decode_step call")
+    ap.add_argument("--gather-compare", type=int, default=1,
+                    help="1: also time gathering every sequence into a contiguous copy")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this library has no "
+              "multi-GPU path: run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    device = torch.device("cuda:0")
+    cpu_main = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+    cpu_cfg = 0.0 if args.no_cpu_baseline else args.config_cpu_seconds
+    if args.workload == "shared_prefix":
+        print(json.dumps(run_shared_prefix(args, device, cpu_main)), flush=True)
+        return
+    if args.workload in ("chunked_prefill", "chunked_prefill_int8"):
+        fmt = "int8" if args.workload.endswith("int8") else "bf16"
+        print(json.dumps(run_chunked_prefill(args, device, fmt)), flush=True)
+        return
+    if args.workload == "fork_copy":
+        print(json.dumps(run_fork_copy(args, device)), flush=True)
+        return
+    if args.workload != "all":
+        print(json.dumps(run_decode(args, device, args.workload, True, cpu_main)), flush=True)
+        return
+    # the headline: the 32k-token workload; the other four configs beside it
+    line = run_decode(args, device, "long_bf16", True, cpu_main)
+    configs = {}
+    for name in ("tiny_f32", "decode_bf16", "int8_kv"):
+        configs[name] = compact(run_decode(args, device, name, False, cpu_cfg))
+    configs["shared_prefix"] = compact(run_shared_prefix(args, device, cpu_cfg))
+    line["configs"] = configs
     print(json.dumps(line), flush=True)
 
 

@@ -267,7 +267,8 @@ int pkv_decode_step(pkv_cache* cache, int32_t layer, const int32_t* table, int32
  * tables, computed so that the shared pages are read once for all sequences:
  * a prefix pass attends over them with (sequence, query head) pairs as the
  * columns of its matrix-core tiles, the split pass covers only each
- * sequence's tokens past prefix_len, and the combine merges both.
+ * sequence's tokens past prefix_len (both in one launch, the prefix waves
+ * beside the split pass's), and the combine merges them.
  *   prefix_pages  device int32 [prefix_len / page_size]; prefix_len a
  *                 positive multiple of page_size within the table row.
  *                 Sequence b sees t < min(lens[b], prefix_len) of the shared
@@ -375,8 +376,7 @@ const char* pkv_last_error(void);
 #define PKV_T_GATHER 3
 #define PKV_T_ATTEND_MULTI 4
 #define PKV_T_COPY_PAGES 5
-#define PKV_T_ATTEND_PREFIX 6  /* the shared-prefix pass */
-#define PKV_T_COUNT 7
+#define PKV_T_COUNT 6
 int pkv_timing_enable(pkv_cache* cache, int32_t on);
 int pkv_timing_read(pkv_cache* cache, double* ms, int32_t* counts);
 

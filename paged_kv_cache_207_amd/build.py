@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libpkv.so")
 ARCH = "gfx950"
 
 SOURCES = ["pkv_host.hip", "write.hip", "gather.hip", "attend_valu.hip", "attend_mfma.hip",
-           "attend_multi.hip", "attend_prefix.hip", "reduce.hip", "pages.hip", "probe.hip"]
+           "attend_multi.hip", "reduce.hip", "pages.hip", "probe.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

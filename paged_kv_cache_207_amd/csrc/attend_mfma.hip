@@ -37,6 +37,7 @@
 #include <climits>
 
 #include "mfma_step.h"
+#include "prefix_wave.h"
 
 namespace pkv {
 namespace {
@@ -121,7 +122,8 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
 
   // sequences with no tokens have no work item: their output is zero (with a
   // shared prefix the combine writes every output)
-  for (int b = blockIdx.x; b < (a.prefix_len > 0 ? 0 : B); b += gridDim.x) {
+  const int nblk = a.prefix_len > 0 ? a.split_blocks : (int)gridDim.x;  // split-pass workgroups
+  for (int b = blockIdx.x; b < (a.prefix_len > 0 ? 0 : B); b += nblk) {
     if (lens[b] != 0) continue;
     for (int i = lane; i < a.n_q_heads * D / 4; i += 64)
       store_out4(a.out, a.q_bf16, (int64_t)b * a.n_q_heads * D + 4 * i, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -133,7 +135,7 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
   if constexpr (SB) {
     T = __builtin_amdgcn_readfirstlane(fpre[B]);
     const int64_t want = std::max<int64_t>(1, (T + kMinWaveSteps - 1) / kMinWaveSteps);
-    n_waves = (int)std::min<int64_t>(gridDim.x, want);
+    n_waves = (int)std::min<int64_t>(nblk, want);
     if ((int)blockIdx.x < n_waves) {
       F = (int64_t)blockIdx.x * T / n_waves;
       F1 = ((int64_t)blockIdx.x + 1) * T / n_waves;
@@ -187,7 +189,7 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
     if (item >= n_items) break;
     const int pair = item / a.n_kv_heads;
     g = item - pair * a.n_kv_heads;
-    item += gridDim.x;
+    item += nblk;
     // largest b whose prefix is <= the index: that sequence owns it
     const int32_t* pre = pair < n_full ? fpre : qpre;
     const int idx = pair < n_full ? pair : pair - n_full;
@@ -512,7 +514,7 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
   }  // pieces
 }
 
-template <int FMT, int D, int BS, bool BAL>
+template <int FMT, int D, int BS, bool BAL, bool PRE>
 __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
   using S = Step<FMT, D>;
   using KT = typename S::KT;
@@ -527,6 +529,16 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
   const int bs = BS ? BS : a.page_size;
   const int C = a.split_tokens;
   const int B = a.batch;
+
+  // shared-prefix mode: the workgroups past the split pass's are the prefix
+  // pass's waves (two column tiles per wave at head_dim 64; one at 128,
+  // within this kernel's registers)
+  if constexpr (PRE) {
+    if ((int)blockIdx.x >= a.split_blocks) {
+      prefix_wave<FMT, D, BS, D == 64 ? 2 : 1>(a, (int)blockIdx.x - a.split_blocks);
+      return;
+    }
+  }
 
   // ---- work list (LDS), one of two schedules.
   // Fixed splits: exclusive prefix sums over the sequences of their full
@@ -658,19 +670,35 @@ int resident_workgroups(K kernel, size_t lds) {
   return per_cu * cus;
 }
 
-template <int FMT, int D, int BS, bool BAL>
+template <int FMT, int D, int BS, bool BAL, bool PRE>
 hipError_t launch_sched(const AttendArgs& a, const Launch& l) {
-  auto kernel = attend_mfma_kernel<FMT, D, BS, BAL>;
+  auto kernel = attend_mfma_kernel<FMT, D, BS, BAL, PRE>;
   const size_t lds = (size_t)(3 * a.batch + 2) * sizeof(int32_t);
   const int64_t bound = BAL ? a.bal_waves : (int64_t)a.n_kv_heads * a.batch * a.n_split;
-  const int64_t grid = std::min<int64_t>(bound, resident_workgroups(kernel, lds));
-  return launch1(kernel, dim3((unsigned)std::max<int64_t>(grid, 1)), dim3(64), lds, l, a);
+  const int64_t resident = resident_workgroups(kernel, lds);
+  if (a.prefix_len <= 0) {
+    const int64_t grid = std::min<int64_t>(bound, resident);
+    return launch1(kernel, dim3((unsigned)std::max<int64_t>(grid, 1)), dim3(64), lds, l, a);
+  }
+  // shared-prefix mode: split workgroups first, then the prefix waves, all
+  // resident together when they fit (the split grid leaves room for them)
+  const int64_t pre = prefix_col_blocks<D == 64 ? 2 : 1>(a.batch, a.group) * a.n_kv_heads *
+                      a.n_pchunks;
+  int64_t split = a.split_wanted ? std::min<int64_t>(bound, resident) : 0;
+  if (split > 0) split = std::max<int64_t>(1, std::min(split, std::max(resident - pre, resident / 2)));
+  if (split + pre > 0x7fffffff) return hipErrorInvalidValue;
+  AttendArgs b = a;
+  b.split_blocks = (int32_t)split;
+  return launch1(kernel, dim3((unsigned)(split + pre)), dim3(64), lds, l, b);
 }
 
 template <int FMT, int D, int BS>
 hipError_t launch_bs(const AttendArgs& a, const Launch& l) {
-  return a.bal_waves > 0 ? launch_sched<FMT, D, BS, true>(a, l)
-                         : launch_sched<FMT, D, BS, false>(a, l);
+  if (a.prefix_len > 0)
+    return a.bal_waves > 0 ? launch_sched<FMT, D, BS, true, true>(a, l)
+                           : launch_sched<FMT, D, BS, false, true>(a, l);
+  return a.bal_waves > 0 ? launch_sched<FMT, D, BS, true, false>(a, l)
+                         : launch_sched<FMT, D, BS, false, false>(a, l);
 }
 
 template <int FMT, int D>

@@ -510,17 +510,11 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
       (int64_t)batch * c->L.n_kv_heads * ((sfx_max + 31) / 32 + kUnitCost) < (int64_t)INT32_MAX) {
     a.bal_waves = wpc * device_cus();
   }
-  if (pre && max_len > 0) {
-    // the shared prefix, once for every sequence
-    Timer tp(c, PKV_T_ATTEND_PREFIX, s, timed);
-    e = pkv::launch_attend_prefix(a, c->L.format, tp.l);
-    tp.stop(e);
-    if (e != hipSuccess)
-      return fail(PKV_EHIP, "prefix pass launch failed: %s", hipGetErrorString(e));
-  }
-  // (a shared-prefix decode step runs the split pass even without suffix
-  // tokens: it reports rows that would land inside the prefix)
-  if (sfx_max > 0 || (pre && a.k_new)) {
+  // With a shared prefix the split pass's launch also runs the prefix pass
+  // (its extra workgroups); a decode step runs the split work even without
+  // suffix tokens, which reports rows that would land inside the prefix.
+  a.split_wanted = sfx_max > 0 || a.k_new ? 1 : 0;
+  if (sfx_max > 0 || (pre && (a.k_new || max_len > 0))) {
     Timer tm(c, PKV_T_ATTEND_SPLIT, s, timed);
     e = mfma ? pkv::launch_attend_mfma(a, c->L.format, tm.l)
              : pkv::launch_attend_valu(a, c->L.format, tm.l);

@@ -90,6 +90,11 @@ struct AttendArgs {
   float* ws_pre_ml = nullptr;
   int32_t prefix_len = 0;
   int32_t n_pchunks = 0;
+  // shared-prefix mode: the split pass's launch holds split_blocks workgroups
+  // of split work (none when split_wanted is 0: no suffix tokens, no new
+  // rows), then the prefix pass's waves
+  int32_t split_blocks = 0;
+  int32_t split_wanted = 1;
 };
 
 // Tokens of the shared prefix per prefix-pass partial.
@@ -170,15 +175,14 @@ inline hipError_t launch1(K kernel, dim3 grid, dim3 block, size_t shm, const Lau
 hipError_t launch_write(const WriteArgs& a, int fmt, int in_dtype, const Launch& l);
 hipError_t launch_gather(const GatherArgs& a, int fmt, const Launch& l);
 hipError_t launch_attend_valu(const AttendArgs& a, int fmt, const Launch& l);
-// Returns hipErrorNotSupported when the shape has no matrix-core variant.
+// Returns hipErrorNotSupported when the shape has no matrix-core variant.  In
+// shared-prefix mode (prefix_len > 0) the launch also runs the prefix pass.
 hipError_t launch_attend_mfma(const AttendArgs& a, int fmt, const Launch& l);
 constexpr int kMaxMfmaBatch = 4096;   // the work list lives in LDS: 12 bytes per sequence
 constexpr int kMaxMfmaKvHeads = 64;  // split counters: a fixed region of the workspace
 bool mfma_supported(int fmt, int q_bf16, int head_dim, int page_size, int group, int batch,
                     int n_kv_heads);
 hipError_t launch_reduce(const AttendArgs& a, const Launch& l);
-// The shared-prefix pass (matrix-core shapes only; hipErrorNotSupported otherwise).
-hipError_t launch_attend_prefix(const AttendArgs& a, int fmt, const Launch& l);
 // Returns hipErrorNotSupported when the shape has no matrix-core variant.
 hipError_t launch_attend_multi(const MultiArgs& a, int fmt, const Launch& l);
 int64_t multi_grid(int batch, int n_kv_heads, int n_qgroups);

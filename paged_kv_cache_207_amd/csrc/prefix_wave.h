@@ -1,18 +1,18 @@
-// Shared-prefix pass: attention of every sequence's decode queries over the
-// tokens its block table shares with all the others, reading those pages
-// once for many sequences instead of once per sequence.
+// The shared-prefix pass: attention of every sequence's decode queries over
+// the tokens its block table shares with all the others, reading those
+// pages once for many sequences instead of once per sequence.
 //
 // Pages shared by reference count (libmir-metal src/engine/kv/paged/mod.rs,
 // PagedStore::snapshot; tiny-llm paged_kv.py: one block serves every reader
 // of it) hold the same K/V for every sequence that lists them, so the scores
 // of all those sequences' queries against one shared token can come from one
 // read of it.  Here the columns of the matrix-core tiles are (sequence, query
-// head) pairs of one KV head: a wave holds two tiles of 16 columns (the G
-// heads of consecutive sequences), walks one chunk of the shared tokens in
-// 32-token steps (the step machinery of mfma_step.h, with cached loads, since
-// every wave of the launch reads the same pages), and leaves per column the
-// running maximum m (log2 units), the sum l and the unnormalised weighted V
-// sum of that chunk: the tile accumulation of metrale_storage
+// head) pairs of one KV head: a wave holds one or two tiles of 16 columns
+// (the G heads of consecutive sequences), walks one chunk of the shared
+// tokens in 32-token steps (the step machinery of mfma_step.h, with cached
+// loads, since every such wave reads the same pages), and leaves per column
+// the running maximum m (log2 units), the sum l and the unnormalised weighted
+// V sum of that chunk: the tile accumulation of metrale_storage
 // high_speed_swap/impl_more.rs attend_layer, finalised by the combine kernel
 // together with the pieces of the private suffix.
 //
@@ -20,14 +20,18 @@
 // decode length rule of tiny-llm paged_kv.py begin_step.  Each wave also
 // checks that its sequences' table rows list the shared pages it read, and
 // reports PKV_DEV_PREFIX otherwise.
-#include <algorithm>
+//
+// These waves are extra workgroups of the split pass's launch (see
+// attend_mfma.hip): they run beside its memory-bound waves on the same
+// SIMDs, so their vector work hides under the streaming of the private
+// suffixes instead of taking a launch of its own.
+#pragma once
 
 #include "mfma_step.h"
 
 namespace pkv {
-namespace {
 
-// One step of cached (not streamed) loads: the same pages serve every wave.
+// One step of cached (not streamed) loads: the same pages serve every prefix wave.
 template <int FMT, int D, int BS>
 __device__ __forceinline__ void load_step_cached(Step<FMT, D>& r, const PageSrc& s, int page_a,
                                                  int page_b, int slot0, int g, int lane) {
@@ -73,24 +77,37 @@ struct Tile {
   f32x4 o[ND];
 };
 
-template <int FMT, int D, int BS>
-__global__ __launch_bounds__(64) void attend_prefix_kernel(AttendArgs a) {
+// Prefix work items: (column block of 16 TT columns, KV head, chunk), column
+// blocks fastest.
+template <int TT>
+__host__ __device__ inline int64_t prefix_col_blocks(int batch, int group) {
+  return ((int64_t)batch * group + 16 * TT - 1) / (16 * TT);
+}
+
+// One prefix work item, done by one wave: TT tiles of 16 columns (TT = 2
+// shares every K/V operand between two tiles; TT = 1 keeps the registers of
+// the head_dim 128 decode path).
+template <int FMT, int D, int BS, int TT>
+__device__ __forceinline__ void prefix_wave(const AttendArgs& a, int wid) {
   using S = Step<FMT, D>;
   constexpr int NC = S::NC, ND = S::ND;
   const int lane = threadIdx.x;
   const int n = lane & 15, j = lane >> 4;
-  const int G = a.group, g = blockIdx.y, chunk = blockIdx.z;
+  const int G = a.group;
+  const int nb = (int)prefix_col_blocks<TT>(a.batch, G);
+  const int cb = wid % nb, rest = wid / nb;
+  const int g = rest % a.n_kv_heads, chunk = rest / a.n_kv_heads;
   const int bs = BS ? BS : a.page_size;
   const int ncols = a.batch * G;
-  const int c0 = blockIdx.x * 32;
+  const int c0 = cb * 16 * TT;
   const int P0 = a.prefix_len;
 
   // the two tiles' columns: (sequence, head in group) of column c0 + 16 t + n,
   // and how many shared tokens each may see
-  int bcol[2], hcol[2], bound[2];
-  bf16x8 qf[2][NC];
+  int bcol[TT], hcol[TT], bound[TT];
+  bf16x8 qf[TT][NC];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < TT; ++t) {
     const int c = c0 + 16 * t + n;
     const bool used = c < ncols;
     const int b = used ? c / G : 0;
@@ -107,15 +124,17 @@ __global__ __launch_bounds__(64) void attend_prefix_kernel(AttendArgs a) {
   const int t_end = min(t_begin + kPrefixChunk, P0);
   // steps past every column's bound are skipped; slots at or past the wave's
   // largest bound may never have been written (NaN), so their V is zeroed
-  int bmax = max(bound[0], bound[1]);
+  int bmax = bound[0];
+#pragma unroll
+  for (int t = 1; t < TT; ++t) bmax = max(bmax, bound[t]);
 #pragma unroll
   for (int o1 = 1; o1 < 64; o1 <<= 1) bmax = max(bmax, __shfl_xor(bmax, o1, 64));
   bmax = __builtin_amdgcn_readfirstlane(bmax);
   const int t_stop = min(t_end, bmax);
 
-  Tile<ND> st[2];
+  Tile<ND> st[TT];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < TT; ++t) {
     st[t].m = -INFINITY;
     st[t].l = 0.f;
 #pragma unroll
@@ -126,19 +145,22 @@ __global__ __launch_bounds__(64) void attend_prefix_kernel(AttendArgs a) {
   const PageSrc src{static_cast<const char*>(a.k_pages), static_cast<const char*>(a.v_pages),
                     a.k_scales, a.v_scales, a.layer_page0, slab_bytes, a.n_kv_heads, bs};
 
-  auto page_at = [&](int lp) -> int {
-    const int pg = a.prefix_pages[lp];
-    if (pg < 0 || pg >= a.n_pages) {
-      if (lane == 0) report(a.status, PKV_DEV_READ_PAGE);
-      return -1;
-    }
-    return pg;
-  };
+  // the chunk's page ids, one per lane (a chunk spans at most 16 pages of 16
+  // tokens), read once: a step picks its pages with a lane read, so no step
+  // waits on a table load
+  const int pg0 = t_begin / bs;
+  const int pg_end = (t_end + bs - 1) / bs;  // this chunk's pages: [pg0, pg_end)
+  int vpage = -1;
+  if (pg0 + lane < pg_end) {
+    const int pg = a.prefix_pages[pg0 + lane];
+    if (pg < 0 || pg >= a.n_pages) report(a.status, PKV_DEV_READ_PAGE);
+    else vpage = pg;
+  }
   auto load_at = [&](int ts, S& r) {
     const int lp = ts / bs;
-    const int pa = page_at(lp);
+    const int pa = __builtin_amdgcn_readlane(vpage, lp - pg0);
     int pb = pa;
-    if (BS == 16) pb = ts + 16 < t_stop ? page_at(lp + 1) : -1;
+    if (BS == 16) pb = ts + 16 < t_stop ? __builtin_amdgcn_readlane(vpage, lp + 1 - pg0) : -1;
     load_step_cached<FMT, D, BS>(r, src, pa, pb, ts - lp * bs, g, lane);
   };
   auto compute = [&](int ts, S& r) {
@@ -152,7 +174,7 @@ __global__ __launch_bounds__(64) void attend_prefix_kernel(AttendArgs a) {
     uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
     if (FMT == PKV_FMT_BF16 && (ts + 32 > t_stop || !r.live_a || !r.live_b)) v_keep_masks(vok, keep);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < TT; ++t) {
       f32x4 sacc[2];
       step_scores<FMT, D>(r, qf[t], sacc);
       float sv[8];
@@ -190,32 +212,40 @@ __global__ __launch_bounds__(64) void attend_prefix_kernel(AttendArgs a) {
     }
   };
 
-  // two register sets, loads one step ahead; the last steps are peeled so no
-  // load sits under a condition
+  // NS register sets, loads NS steps ahead (all of a chunk's steps are in
+  // flight from the start when NS covers them).  Every wave of the launch
+  // asks the caches for the same shared lines at about the same time, so a
+  // step costs a full memory round trip: depth, not bandwidth, sets the pace
+  // here.  Loads are unconditional (a step past the chunk reloads the last
+  // one and is not computed), so no load sits under a condition and the
+  // compiler counts outstanding loads exactly.
+  // The waves of one (KV head, chunk) read the same lines; each starts at a
+  // different step of the chunk (the softmax merge does not depend on the
+  // order), so at any moment their requests spread over the chunk's pages
+  // instead of all queueing on the same few cache channels.
+  constexpr int NS = 2;
+  constexpr int MAXS = kPrefixChunk / 32;
   const int n_steps = t_stop > t_begin ? (t_stop - t_begin + 31) / 32 : 0;
   if (n_steps > 0) {
-    auto T = [&](int i) { return t_begin + 32 * i; };
-    S r0, r1;
-    load_at(T(0), r0);
-    int s = 0;
-    for (; s + 2 < n_steps; s += 2) {
-      load_at(T(s + 1), r1);
-      compute(T(s), r0);
-      load_at(T(s + 2), r0);
-      compute(T(s + 1), r1);
-    }
-    if (s + 1 < n_steps) {
-      load_at(T(s + 1), r1);
-      compute(T(s), r0);
-      compute(T(s + 1), r1);
-    } else {
-      compute(T(s), r0);
+    const int rot = cb % n_steps;
+    auto T = [&](int i) {
+      int k = min(i, n_steps - 1) + rot;
+      k -= k >= n_steps ? n_steps : 0;
+      return t_begin + 32 * k;
+    };
+    S r[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) load_at(T(i), r[i]);
+#pragma unroll
+    for (int i = 0; i < MAXS; ++i) {
+      if (i < n_steps) compute(T(i), r[i % NS]);
+      if (i + NS < MAXS) load_at(T(i + NS), r[i % NS]);
     }
   }
 
   // ---- partials of this chunk: O^T lane layout = dims 16 dt + 4 j + i of column n ----
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < TT; ++t) {
     const float l = rows_sum(st[t].l);
     if (c0 + 16 * t + n < ncols) {
       const int64_t row =
@@ -227,49 +257,33 @@ __global__ __launch_bounds__(64) void attend_prefix_kernel(AttendArgs a) {
     }
   }
 
-  // ---- the promise behind this pass: every sequence read here lists the
-  // shared pages of this chunk in its own table row (one check per column
-  // lane with j = 0; heads of one sequence repeat it) ----
-  if (j == 0) {
+  // ---- the promise behind this pass: every sequence read here lists this
+  // chunk's shared pages in its own table row, for the tokens it sees.  One
+  // (sequence, page) pair per lane, the table entry, the length and the
+  // shared id loaded together ----
+  const int b_first = c0 / G;
+  const int b_last = min(c0 + 16 * TT - 1, ncols - 1) / G;
+  const int per = pg_end - pg0;  // at most 16 pages
+  const int pairs = (b_last - b_first + 1) * per;
+  bool bad = false;
+  for (int p0 = 0; p0 < pairs; p0 += 256) {
+    int ent[4], len4[4], want[4], lpv[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int lp_end = (min(t_end, bound[t]) + bs - 1) / bs;
-      const int32_t* row = a.table_full + (int64_t)bcol[t] * a.table_stride;
-      bool bad = false;
-      for (int lp = t_begin / bs; lp < lp_end; ++lp) bad |= row[lp] != a.prefix_pages[lp];
-      if (bad) report(a.status, PKV_DEV_PREFIX);
+    for (int u = 0; u < 4; ++u) {
+      const int p = min(p0 + 64 * u + lane, pairs - 1);  // in bounds; repeats are harmless
+      const int bb = b_first + p / per, lp = pg0 + p % per;
+      lpv[u] = lp;
+      ent[u] = a.table_full[(int64_t)bb * a.table_stride + lp];
+      len4[u] = a.lens[bb];
+      want[u] = __shfl(vpage, lp - pg0, 64);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int L = len4[u] < 0 ? 0 : (len4[u] > a.max_len ? a.max_len : len4[u]);
+      bad |= (int64_t)lpv[u] * bs < min(L, P0) && ent[u] != want[u];
     }
   }
-}
-
-template <int FMT, int D, int BS>
-hipError_t launch_bs(const AttendArgs& a, const Launch& l) {
-  const int64_t blocks = ((int64_t)a.batch * a.group + 31) / 32;
-  if (blocks > 0x7fffffff || a.n_pchunks > 65535 || a.n_kv_heads > 65535)
-    return hipErrorInvalidValue;
-  return launch1(attend_prefix_kernel<FMT, D, BS>,
-                 dim3((unsigned)blocks, a.n_kv_heads, a.n_pchunks), dim3(64), 0, l, a);
-}
-
-template <int FMT, int D>
-hipError_t launch_d(const AttendArgs& a, const Launch& l) {
-  if (a.page_size == 16) return launch_bs<FMT, D, 16>(a, l);
-  if (a.page_size == 32) return launch_bs<FMT, D, 32>(a, l);
-  return launch_bs<FMT, D, 0>(a, l);
-}
-
-template <int FMT>
-hipError_t launch_fmt(const AttendArgs& a, const Launch& l) {
-  return a.head_dim == 128 ? launch_d<FMT, 128>(a, l) : launch_d<FMT, 64>(a, l);
-}
-
-}  // namespace
-
-hipError_t launch_attend_prefix(const AttendArgs& a, int fmt, const Launch& l) {
-  if (!mfma_supported(fmt, a.q_bf16, a.head_dim, a.page_size, a.group, a.batch, a.n_kv_heads))
-    return hipErrorNotSupported;
-  if (a.batch <= 0 || a.prefix_len <= 0 || a.n_pchunks <= 0) return hipSuccess;
-  return fmt == PKV_FMT_BF16 ? launch_fmt<PKV_FMT_BF16>(a, l) : launch_fmt<PKV_FMT_INT8>(a, l);
+  if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) report(a.status, PKV_DEV_PREFIX);
 }
 
 }  // namespace pkv

@@ -22,8 +22,7 @@ DEV_WRITE_PAGE, DEV_WRITE_TABLE, DEV_READ_PAGE, DEV_LEN, DEV_QROWS, DEV_WRITE_RO
 DEV_PREFIX = 64
 ATTEND_VALU, ATTEND_COMBINE_KERNEL, ATTEND_COMBINE_FUSED = 1, 2, 4
 T_WRITE, T_ATTEND_SPLIT, T_ATTEND_COMBINE, T_GATHER, T_ATTEND_MULTI, T_COPY_PAGES = 0, 1, 2, 3, 4, 5
-T_ATTEND_PREFIX = 6
-T_COUNT = 7
+T_COUNT = 6
 
 FORMAT_CODE = {"f32": FMT_F32, "bf16": FMT_BF16, "int8": FMT_INT8}
 DTYPE_CODE = {torch.float32: DT_F32, torch.bfloat16: DT_BF16}
@@ -402,7 +401,7 @@ class PagedKVCache:
         n = (C.c_int32 * T_COUNT)()
         _check(lib().pkv_timing_read(self._h, ms, n))
         names = ["write", "attend_split", "attend_combine", "gather", "attend_multi",
-                 "copy_pages", "attend_prefix"]
+                 "copy_pages"]
         return {k: (ms[i], n[i]) for i, k in enumerate(names)}
 
     # -- gather ------------------------------------------------------------------

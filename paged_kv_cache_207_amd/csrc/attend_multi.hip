@@ -51,6 +51,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTiles = 2;  // 16-column tiles per wave: both use the same K/V operands
 constexpr int kPageWin = 512;  // page ids staged in LDS at a time
 constexpr int kHalves = 4;     // 32-token steps per staged block (one barrier each)
+constexpr float kRescaleSlack = 8.f;  // log2 units a maximum may pass the reference by
 
 template <int D>
 struct MultiLds {
@@ -90,7 +91,9 @@ __device__ __forceinline__ uint4 zero_dead(uint4 v, uint32_t dead_bits) {
   return uint4{w[0], w[1], w[2], w[3]};
 }
 
-template <int FMT, int D, int BS>
+// RAW (bf16 pages, a positive scale): the running maximum is taken over the
+// raw score sums and the scale goes into one fma inside the exponential.
+template <int FMT, int D, int BS, bool RAW>
 __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) {
   using L = MultiLds<D>;
   constexpr int NC = D / 32, ND = D / 16;
@@ -181,9 +184,6 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
     }
     __syncthreads();
   };
-  auto page_of = [&](int lp) {  // uniform; -1 past the range or on a bad entry
-    return lp > pg_last ? -1 : __builtin_amdgcn_readfirstlane(pids[lp - win0]);
-  };
   // whether the window must move before the pages of a staged block
   // (logical pages lp .. lp + 2 kHalves at most) can be looked up
   auto window_misses = [&](int lp) {
@@ -195,6 +195,9 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
     uint4 kc[KL], vc[VL];
     float sc;
     int page_a, page_b, slot0;
+  };
+  auto page_of = [&](int lp) {  // uniform; -1 past the range or on a bad entry
+    return lp > pg_last ? -1 : __builtin_amdgcn_readfirstlane(pids[lp - win0]);
   };
   auto load_stage = [&](int ts, Stage& st) {
     const int lp = ts / bs;
@@ -292,17 +295,25 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
     }
   };
 
-  f32x4 o[kTiles][ND];
-  float m[kTiles], l[kTiles];
+  // o: the unnormalised outputs; ls: the softmax sums, taken by one more
+  // matrix-core product per tile and step with an all-ones A operand (every
+  // row of the result is the column's sum over the step's 32 weights, in
+  // every lane of the column), which replaces per-lane adds and the final
+  // cross-lane reduction; m: the reference maximum the weights are taken
+  // against.
+  f32x4 o[kTiles][ND], ls[kTiles];
+  float m[kTiles];
 #pragma unroll
   for (int u = 0; u < kTiles; ++u) {
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ls[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[u] = -INFINITY;
-    l[u] = 0.f;
   }
+  const bf16x8 ones = as_bf16x8(uint4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
   const float qs = a.qk_scale_log2;
-  const bool raw_max = qs > 0.f;  // the maximum of raw sums scales to the maximum of scores
+  constexpr bool raw_max = RAW && FMT == PKV_FMT_BF16;  // the maximum of raw sums scales to
+                                                        // the maximum of scores (qs > 0)
 
   // The wave's smallest position: every column of the wave sees a step whole
   // when the step lies below it (and inside the block's range, on live pages).
@@ -343,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
     // wave-uniform: every token of the step is seen by every column
     const bool open = live_a && live_b && ts + 31 <= pos_min && ts + 32 <= t_end;
     const bool lane_live = BS == 16 && j >= 2 ? live_b : live_a;
-    bf16x8 pb[kTiles];
+    bf16x8 pb[kTiles], ps[kTiles];
 #pragma unroll
     for (int u = 0; u < kTiles; ++u) {
       // scores in log2 units: sacc * qs (int8: times the token's K scale).
@@ -374,36 +385,44 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
       }
       mx = rows_max(mx);
       const float m_new = fmaxf(m[u], mx);
-      // lazy rescale: the output only moves when some column's maximum grew
-      const bool grow = __any(m_new > m[u]);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m[u] - m_use) : 1.f;
-      float psum = 0.f;
+      // Lazy rescale: the weights are taken against a reference maximum that
+      // moves only when some column's maximum passed it by more than
+      // kRescaleSlack (log2 units), so weights stay below 2^kRescaleSlack and
+      // the outputs and sums are rescaled on few steps.
+      const bool grow = __any(m_new > m[u] + kRescaleSlack);  // -inf + slack: any finite max
+      const float m_ref = grow ? m_new : m[u];
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
       float pw[8];
+      float pv[8];  // the weights of the sums (int8: before the V scale)
       if (open) {
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           const float pr = FMT == PKV_FMT_BF16 && raw_max
                                ? __builtin_amdgcn_exp2f(fmaf(sv[x], qs, -m_use))
                                : __builtin_amdgcn_exp2f(sv[x] - m_use);
-          psum += pr;
+          pv[x] = pr;
           pw[x] = FMT == PKV_FMT_INT8 ? pr * vsc[x] : pr;
         }
       } else {
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           const float pr = ok[x] ? __builtin_amdgcn_exp2f(sv[x] - m_use) : 0.f;
-          psum += pr;
+          pv[x] = pr;
           pw[x] = FMT == PKV_FMT_INT8 ? pr * vsc[x] : pr;
         }
       }
       pb[u] = as_bf16x8(uint4{pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3]),
                               pack_bf16x2(pw[4], pw[5]), pack_bf16x2(pw[6], pw[7])});
-      l[u] = l[u] * alpha + psum;
-      m[u] = m_new;
+      ps[u] = FMT == PKV_FMT_INT8
+                  ? as_bf16x8(uint4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                    pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])})
+                  : pb[u];
       if (grow) {
+        const float alpha = __builtin_amdgcn_exp2f(m[u] - m_use);
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) o[u][dt] *= alpha;
+        ls[u] *= alpha;
+        m[u] = m_ref;
       }
     }
     uint4 vw[ND];
@@ -415,6 +434,9 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
 #pragma unroll
       for (int u = 0; u < kTiles; ++u)
         o[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vw[dt]), pb[u], o[u][dt], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u)
+      ls[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, ps[u], ls[u], 0, 0, 0);
   };
 
   // ---- the step loop: the loads of step i+1 are in flight while step i is
@@ -468,9 +490,7 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
   // ---- results: O^T lane layout = dims 16 dt + 4j + i of column n
 #pragma unroll
   for (int u = 0; u < kTiles; ++u) {
-    float lu = l[u];
-    lu += __shfl_xor(lu, 16, 64);
-    lu += __shfl_xor(lu, 32, 64);
+    const float lu = ls[u][0];  // the column's whole sum, in every lane of the column
     if (col[u]) {
       const float inv = lu > 0.f ? 1.f / lu : 0.f;
 #pragma unroll
@@ -483,7 +503,13 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
 template <int FMT, int D, int BS>
 hipError_t launch_bs(const MultiArgs& a, const Launch& l) {
   const int64_t grid = multi_grid(a.batch, a.n_kv_heads, a.n_qgroups);
-  return launch1(attend_multi_kernel<FMT, D, BS>, dim3((unsigned)grid), dim3(kThreads), 0, l, a);
+  if constexpr (FMT == PKV_FMT_BF16) {
+    if (a.qk_scale_log2 > 0.f)
+      return launch1(attend_multi_kernel<FMT, D, BS, true>, dim3((unsigned)grid), dim3(kThreads),
+                     0, l, a);
+  }
+  return launch1(attend_multi_kernel<FMT, D, BS, false>, dim3((unsigned)grid), dim3(kThreads), 0,
+                 l, a);
 }
 
 template <int FMT, int D>

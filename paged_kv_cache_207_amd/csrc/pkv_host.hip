@@ -109,6 +109,11 @@ constexpr int kMaxBalWavesPerCu = 4;
 int bal_waves_per_cu(int fmt) { return fmt == PKV_FMT_BF16 ? kMaxBalWavesPerCu : 0; }
 constexpr int kUnitCost = 3;
 
+// Shared-prefix chunks: the target length, and the most one wave's page-id
+// vector covers.
+constexpr int kPrefixChunkTarget = 512;
+constexpr int kPrefixChunkMax = 1024;
+
 struct WsLayout {
   uint64_t o_off, ml_off, sched_off, desc_off, total;
   uint64_t pre_o_off = 0, pre_ml_off = 0;  // shared-prefix partials (after the rest)
@@ -132,14 +137,27 @@ WsLayout ws_layout(const pkv_cache* c, int batch, int n_q_heads, int n_split) {
   return w;
 }
 
-// Prefix chunks of a shared prefix of prefix_len tokens (one partial each).
-int prefix_chunks(int prefix_len) { return (prefix_len + pkv::kPrefixChunk - 1) / pkv::kPrefixChunk; }
+// Tokens per prefix-pass partial: the prefix waves take one chunk each.
+// Longer chunks mean fewer partials for the combine but longer prefix waves,
+// which must finish beside the split pass's.  Measured on the 256-sequence,
+// 1024-token-prefix workload (one MI355X, split launch + combine per step):
+// 256 tokens 75.8-76.6 us, 512 74.8-74.9, 1024 75.3.  A chunk spans at most
+// 64 pages (one page id per lane) and is a multiple of 32 tokens.
+int prefix_chunk_tokens(int page_size) {
+  const int cap = std::min(kPrefixChunkMax, 64 * page_size / 32 * 32);
+  return std::max(32, std::min(cap, kPrefixChunkTarget));
+}
+int prefix_chunks(int prefix_len, int page_size) {
+  const int c = prefix_chunk_tokens(page_size);
+  return (prefix_len + c - 1) / c;
+}
 
 // ws_layout plus the shared-prefix partials: [batch][n_q_heads][chunks] rows.
 WsLayout ws_layout_prefix(const pkv_cache* c, int batch, int n_q_heads, int n_split,
                           int prefix_len) {
   WsLayout w = ws_layout(c, batch, n_q_heads, n_split);
-  const uint64_t rows = (uint64_t)batch * n_q_heads * prefix_chunks(prefix_len);
+  const uint64_t rows =
+      (uint64_t)batch * n_q_heads * prefix_chunks(prefix_len, c->L.page_size);
   w.pre_o_off = (w.total + 255) / 256 * 256;
   w.pre_ml_off = (w.pre_o_off + rows * c->L.head_dim * sizeof(float) + 255) / 256 * 256;
   w.total = w.pre_ml_off + rows * 2 * sizeof(float);
@@ -452,7 +470,8 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
     a.table_full = table;
     a.prefix_pages = pre->pages;
     a.prefix_len = P0;
-    a.n_pchunks = prefix_chunks(P0);
+    a.pchunk = prefix_chunk_tokens(c->L.page_size);
+    a.n_pchunks = prefix_chunks(P0, c->L.page_size);
     a.ws_pre_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.pre_o_off);
     a.ws_pre_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.pre_ml_off);
   }

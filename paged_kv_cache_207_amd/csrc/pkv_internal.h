@@ -89,6 +89,7 @@ struct AttendArgs {
   float* ws_pre_o = nullptr;
   float* ws_pre_ml = nullptr;
   int32_t prefix_len = 0;
+  int32_t pchunk = 0;  // tokens per prefix chunk (a multiple of 32, at most 64 pages)
   int32_t n_pchunks = 0;
   // shared-prefix mode: the split pass's launch holds split_blocks workgroups
   // of split work (none when split_wanted is 0: no suffix tokens, no new
@@ -96,9 +97,6 @@ struct AttendArgs {
   int32_t split_blocks = 0;
   int32_t split_wanted = 1;
 };
-
-// Tokens of the shared prefix per prefix-pass partial.
-constexpr int kPrefixChunk = 256;
 
 // Arguments of the several-queries-per-sequence kernel (one launch = one
 // pkv_paged_attend_multi call).

@@ -120,8 +120,8 @@ __device__ __forceinline__ void prefix_wave(const AttendArgs& a, int wid) {
                              ((int64_t)b * a.n_q_heads + (int64_t)g * G + hcol[t]) * D,
                    used, j);
   }
-  const int t_begin = chunk * kPrefixChunk;
-  const int t_end = min(t_begin + kPrefixChunk, P0);
+  const int t_begin = chunk * a.pchunk;
+  const int t_end = min(t_begin + a.pchunk, P0);
   // steps past every column's bound are skipped; slots at or past the wave's
   // largest bound may never have been written (NaN), so their V is zeroed
   int bmax = bound[0];
@@ -145,9 +145,9 @@ __device__ __forceinline__ void prefix_wave(const AttendArgs& a, int wid) {
   const PageSrc src{static_cast<const char*>(a.k_pages), static_cast<const char*>(a.v_pages),
                     a.k_scales, a.v_scales, a.layer_page0, slab_bytes, a.n_kv_heads, bs};
 
-  // the chunk's page ids, one per lane (a chunk spans at most 16 pages of 16
-  // tokens), read once: a step picks its pages with a lane read, so no step
-  // waits on a table load
+  // the chunk's page ids, one per lane (a chunk spans at most 64 pages), read
+  // once: a step picks its pages with a lane read, so no step waits on a
+  // table load
   const int pg0 = t_begin / bs;
   const int pg_end = (t_end + bs - 1) / bs;  // this chunk's pages: [pg0, pg_end)
   int vpage = -1;
@@ -221,25 +221,32 @@ __device__ __forceinline__ void prefix_wave(const AttendArgs& a, int wid) {
   // compiler counts outstanding loads exactly.
   // The waves of one (KV head, chunk) read the same lines; each starts at a
   // different step of the chunk (the softmax merge does not depend on the
-  // order), so at any moment their requests spread over the chunk's pages
-  // instead of all queueing on the same few cache channels.
-  constexpr int NS = 2;
-  constexpr int MAXS = kPrefixChunk / 32;
+  // order), so at any moment their requests spread over the chunk's pages.
+  // Two register sets, loads one step ahead; the last steps are peeled so no
+  // load sits under a condition.
   const int n_steps = t_stop > t_begin ? (t_stop - t_begin + 31) / 32 : 0;
   if (n_steps > 0) {
     const int rot = cb % n_steps;
     auto T = [&](int i) {
-      int k = min(i, n_steps - 1) + rot;
+      int k = i + rot;
       k -= k >= n_steps ? n_steps : 0;
       return t_begin + 32 * k;
     };
-    S r[NS];
-#pragma unroll
-    for (int i = 0; i < NS; ++i) load_at(T(i), r[i]);
-#pragma unroll
-    for (int i = 0; i < MAXS; ++i) {
-      if (i < n_steps) compute(T(i), r[i % NS]);
-      if (i + NS < MAXS) load_at(T(i + NS), r[i % NS]);
+    S r0, r1;
+    load_at(T(0), r0);
+    int s = 0;
+    for (; s + 2 < n_steps; s += 2) {
+      load_at(T(s + 1), r1);
+      compute(T(s), r0);
+      load_at(T(s + 2), r0);
+      compute(T(s + 1), r1);
+    }
+    if (s + 1 < n_steps) {
+      load_at(T(s + 1), r1);
+      compute(T(s), r0);
+      compute(T(s + 1), r1);
+    } else {
+      compute(T(s), r0);
     }
   }
 
@@ -263,7 +270,7 @@ __device__ __forceinline__ void prefix_wave(const AttendArgs& a, int wid) {
   // shared id loaded together ----
   const int b_first = c0 / G;
   const int b_last = min(c0 + 16 * TT - 1, ncols - 1) / G;
-  const int per = pg_end - pg0;  // at most 16 pages
+  const int per = pg_end - pg0;  // at most 64 pages
   const int pairs = (b_last - b_first + 1) * per;
   bool bad = false;
   for (int p0 = 0; p0 < pairs; p0 += 256) {

@@ -57,11 +57,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_split_{}_traffic.json")
 # these are unchanged)
 KERNEL_SOURCES = ["paged_kv_cache_207_amd/csrc/attend_mfma.hip",
                   "paged_kv_cache_207_amd/csrc/mfma_step.h",
+                  "paged_kv_cache_207_amd/csrc/prefix_wave.h",
                   "paged_kv_cache_207_amd/csrc/pkv_device.h"]
 KERNEL_PARTS = [("paged_kv_cache_207_amd/csrc/pkv_internal.h", "struct AttendArgs {", "};"),
                 ("paged_kv_cache_207_amd/csrc/pkv_host.hip", "int plan_split(", "\n}\n"),
                 ("paged_kv_cache_207_amd/csrc/pkv_host.hip", "constexpr int kMaxBalWavesPerCu",
-                 "\n\n")]
+                 "\n\n"),
+                ("paged_kv_cache_207_amd/csrc/pkv_host.hip", "constexpr int kPrefixChunkTarget",
+                 "\n")]
 
 
 def log(msg: str) -> None:
@@ -290,6 +293,28 @@ def gather_compare(w, cache, table, device, reps=5):
             "gather_GBps_read_plus_write": round(moved / (per_batch_ms / 1e3) / 1e9, 1)}
 
 
+def shared_prefix_bytes(sp) -> dict:
+    """Byte counts of the shared-prefix job, per step on average: logical KV
+    bytes (the prefix counted once per sequence), unique KV bytes (the prefix
+    once), and the split launch's algorithmic bytes (the private K/V and their
+    table entries, the shared pages once with their table entries, the
+    queries, and the new rows it reads and stores)."""
+    w = sp.base
+    B, bs, P0 = w.batch, w.page_size, sp.prefix_tokens
+    lens_steps = [sp.step_lens(s).astype(np.int64) for s in range(sp.n_steps)]
+    per_tok = w.n_kv_heads * w.head_dim * 2 * 2
+    logical = sum(int(l.sum()) for l in lens_steps) * per_tok
+    private = sum(int((l - P0).sum()) for l in lens_steps) * per_tok
+    unique = private + sp.n_steps * P0 * per_tok
+    priv_pages = sum(int((-(-(l) // bs)).sum()) - B * sp.prefix_pages for l in lens_steps)
+    qb = B * w.n_q_heads * w.head_dim * 2
+    rows = B * w.n_kv_heads * w.head_dim * 2 * (2 + 2)
+    split = ((private + 4 * priv_pages) / sp.n_steps + P0 * per_tok + 4 * sp.prefix_pages
+             + qb + rows)
+    n = sp.n_steps
+    return {"logical": logical / n, "unique": unique / n, "split_launch": int(split)}
+
+
 def run_shared_prefix(args, device, cpu_seconds: float = 0.0):
     """The shared-prefix workload as one job of n_steps decode steps after the
     fill.  Each step = host table growth (pool-backed block tables: a sequence
@@ -306,6 +331,7 @@ def run_shared_prefix(args, device, cpu_seconds: float = 0.0):
     w = sp.base
     B, bs = w.batch, w.page_size
     P0 = sp.prefix_tokens
+    calibration_copy(device)  # the reference dispatch for scaling HBM counters
 
     def build_tables():
         pool = pkv.PagePool(w.n_pages)
@@ -438,22 +464,12 @@ def run_shared_prefix(args, device, cpu_seconds: float = 0.0):
         pool.close()
     assert cache.status() == 0
     graph_job_s = float(np.mean(g_times))
-    lens_steps = [sp.step_lens(s).astype(np.int64) for s in range(sp.n_steps)]
-    per_tok = w.n_kv_heads * w.head_dim * 2 * 2
-    logical = sum(int(l.sum()) for l in lens_steps) * per_tok
-    private = sum(int((l - P0).sum()) for l in lens_steps) * per_tok
-    unique = private + sp.n_steps * P0 * per_tok
+    nb = shared_prefix_bytes(sp)
+    logical, unique = nb["logical"] * sp.n_steps, nb["unique"] * sp.n_steps
+    split_bytes = nb["split_launch"]
     kp, ks_ = res[True]["kern"], res[False]["kern"]
     split_s, comb_s = kp["attend_split"] / 1e3, kp["attend_combine"] / 1e3
     attn_s = split_s + comb_s
-    # the split launch's algorithmic bytes: the private K/V and their table
-    # entries, the shared pages once (read by its prefix waves) and their
-    # table entries, the queries and the new rows it reads and stores
-    priv_pages = sum(int((-(-(l) // bs)).sum()) - B * sp.prefix_pages for l in lens_steps)
-    qb = B * w.n_q_heads * w.head_dim * 2
-    rows = B * w.n_kv_heads * w.head_dim * 2 * (2 + 2)
-    split_bytes = ((private + 4 * priv_pages) / sp.n_steps + P0 * per_tok + 4 * sp.prefix_pages
-                   + qb + rows)
     log(f"shared_prefix: job {graph_job_s * 1e3:.3f} ms (graphs), eager "
         f"{res[True]['job_s'] * 1e3:.3f} ms; per step: split pass with prefix waves "
         f"{split_s * 1e6:.1f} us, combine {comb_s * 1e6:.1f} us; per-sequence path: split "

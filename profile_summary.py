@@ -131,7 +131,10 @@ def main():
     fa = mean(F[att]) * 1024 / ff
     wa = mean(Wr[att]) * 1024 / fw
     w = bench.W.by_name(a.tag)
-    alg = bench.split_kernel_bytes(w)
+    if a.tag == "shared_prefix":  # the split launch with its prefix waves
+        alg = bench.shared_prefix_bytes(w)["split_launch"]
+    else:
+        alg = bench.split_kernel_bytes(w)
     lines = [f"# HBM traffic of the split-K attention pass: {a.tag}", "",
              "Commands (from the repository root, on one MI355X):", "", "```", *cmds[:2], "```",
              "",

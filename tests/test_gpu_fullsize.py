@@ -101,3 +101,48 @@ def test_full_size_shared_prefix_steps():
     assert c.status() == 0
     say(f"  sampled max err {worst:.3e}")
     assert worst <= TOL["bf16"]
+
+
+def test_full_size_shared_prefix_read_once():
+    """The same 32-step job through pkv_decode_step_prefix (the shared pages
+    read once for all 256 sequences, the step's rows written by the split
+    pass) beside pkv_decode_step: sampled sequences against the oracle at
+    the first, a middle and the last step, the two paths within the bf16
+    tolerance of each other at every step, and the same pages bit for bit
+    at the end."""
+    require_gpu()
+    sp = W.shared_prefix()
+    w = sp.base
+    say(f"full-size shared_prefix, prefix read once: B={w.batch} steps={sp.n_steps}")
+    c1, c2 = make_cache(w), make_cache(w)
+    tdev = dev(w.tables)
+    for c in (c1, c2):
+        gpu_write(c, tdev, sp.fill_rounds())
+    ks, vs = sp.step_rows_all()
+    pk, pv = sp.prefix_kv()
+    pre = dev(w.tables[0, :sp.prefix_pages])
+    max_len = int(sp.step_lens(sp.n_steps - 1).max())
+    check_at = {0, sp.n_steps // 2, sp.n_steps - 1}
+    ws1 = c1.prefix_workspace(w.batch, w.n_q_heads, max_len, sp.prefix_tokens)
+    ws2 = c2.workspace(w.batch, w.n_q_heads, max_len)
+    worst, worst_pair = 0.0, 0.0
+    for s in range(sp.n_steps):
+        lens = dev(sp.step_lens(s))
+        q = w.query(step=s)
+        kn, vn = ks[s].cuda(), vs[s].cuda()
+        out1 = c1.decode_step_prefix(tdev, lens, max_len, pre, sp.prefix_tokens, q.cuda(),
+                                     w.scale, k_new=kn, v_new=vn, workspace=ws1)
+        out2 = c2.decode_step(tdev, lens, max_len, kn, vn, q.cuda(), w.scale, workspace=ws2)
+        worst_pair = max(worst_pair, float((out1.float() - out2.float()).abs().max()))
+        if s in check_at:
+            for b in samples(w, 2):
+                kp, vp = sp.private_kv(b)
+                n = int(sp.suffix[b]) + s + 1
+                k = torch.cat([pk, kp[:n]])
+                v = torch.cat([pv, vp[:n]])
+                worst = max(worst, check_seq(c1, w, tdev, b, out1, k, v, q[b]))
+    torch.cuda.synchronize()
+    assert c1.status() == 0 and c2.status() == 0
+    assert torch.equal(c1.k_pages, c2.k_pages) and torch.equal(c1.v_pages, c2.v_pages)
+    say(f"  sampled max err {worst:.3e}; max difference between the paths {worst_pair:.3e}")
+    assert worst <= TOL["bf16"] and worst_pair <= TOL["bf16"]

@@ -148,13 +148,15 @@ def test_multi_query_bad_rows_flagged_without_fault():
     assert c.status() & pkv.DEV_QROWS
 
 
-def test_full_size_chunked_prefill_sampled():
-    """The benchmark's chunked-prefill workload at full size; sampled rows
-    (first, last and seeded ones of every sequence) against the oracle."""
+@pytest.mark.parametrize("fmt", ["bf16", "int8"])
+def test_full_size_chunked_prefill_sampled(fmt):
+    """The benchmark's chunked-prefill workloads (bf16 and int8 pages) at full
+    size; sampled rows (first, last and seeded ones of every sequence)
+    against the oracle."""
     require_gpu()
-    cp = W.chunked_prefill()
+    cp = W.chunked_prefill(kv_format=fmt)
     w = cp.base
-    say(f"full-size chunked prefill: B={w.batch} ctx={cp.context} chunk={cp.chunk}")
+    say(f"full-size chunked prefill ({fmt}): B={w.batch} ctx={cp.context} chunk={cp.chunk}")
     c, q, out = run(cp)
     rng = np.random.default_rng(3)
     rows = []
@@ -165,5 +167,5 @@ def test_full_size_chunked_prefill_sampled():
     ref = oracle_out(cp, q, rows=rows)
     e = err(out, ref, rows)
     say(f"  sampled max err {e:.3e}")
-    assert e <= TOL["bf16"]
+    assert e <= TOL[fmt]
     assert c.status() == 0

@@ -46,6 +46,7 @@ namespace {
 // small calls, so their partials stay few).
 constexpr int kMinWaveSteps = 8;
 
+
 // Partials are exchanged between workgroups, which may sit on different XCDs
 // with separate L2 caches.  Writers store them as agent-scope relaxed atomics
 // (sc1 stores, written through to the coherence point) and wait for those
@@ -227,6 +228,35 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
 
   const int t_new = len - 1;  // decode step: the position of the new row
 
+  // A decode step's new row (its K chunks as the A operand lays them out, one
+  // V value per dim lane), the page it goes to, and whether the length was
+  // in range (a clamped length writes nothing).  At head_dim 64 the row is
+  // fetched when the piece starts, so the loads are long done when its last
+  // step needs them; at 128 the registers are not there, and the row is
+  // fetched in the last step.
+  constexpr bool kEarlyRow = D == 64;
+  struct NewRow {
+    uint4 kb4[NC];
+    uint32_t vnew[ND];
+    int page;
+    bool ok;
+  };
+  auto fetch_new = [&](NewRow& nr) {
+    nr.ok = a.lens[b] - a.prefix_len == len;
+    const int64_t row = ((int64_t)b * a.n_kv_heads + g) * D;
+    const uint16_t* kr = static_cast<const uint16_t*>(a.k_new) + row;
+    const uint16_t* vr = static_cast<const uint16_t*>(a.v_new) + row;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) nr.kb4[c] = *reinterpret_cast<const uint4*>(kr + kdim(c, j));
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) nr.vnew[dt] = vr[16 * dt + n];
+    nr.page = trow[t_new / bs];
+  };
+  NewRow early;
+  if constexpr (kEarlyRow) {
+    if (owns_new) fetch_new(early);
+  }
+
   f32x4 o[ND];
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -286,6 +316,8 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
         const float p = ok[x] ? __builtin_amdgcn_exp2f(sv[x] - m_use) : 0.f;
         psum += p;
         pw[x] = p;
+        // int8: a dead token's scale may be any bits (NaN too), so its
+        // weight is zeroed rather than multiplied
         if (FMT == PKV_FMT_INT8) pw[x] = ok[x] ? p * vsc[x] : 0.f;
       }
       const bf16x8 pb = as_bf16x8(uint4{pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3]),
@@ -311,20 +343,20 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
     // flight behind it, so the row costs no registers during the loop.
     auto substitute_new = [&](int ts, S& r) {
       if (!owns_new || t_new < ts || t_new >= ts + 32) return;
-      // an out-of-range length (reported, clamped): no write
-      if (a.lens[b] - a.prefix_len != len) return;
+      NewRow late;
+      if constexpr (!kEarlyRow) fetch_new(late);
+      const NewRow& nr = kEarlyRow ? early : late;
+      if (!nr.ok) return;  // an out-of-range length (reported, clamped): no write
       const int x_new = t_new - ts;                          // slot of the token in the step
       const int tau_new = (x_new >> 2) & 1;                  // score tile holding it
       const int n_new = ((x_new >> 3) << 2) | (x_new & 3);  // its K row lane
       const int j_new = x_new >> 3;                          // its V k-group
-      const uint16_t* kr = static_cast<const uint16_t*>(a.k_new) + ((int64_t)b * a.n_kv_heads + g) * D;
-      const uint16_t* vr = static_cast<const uint16_t*>(a.v_new) + ((int64_t)b * a.n_kv_heads + g) * D;
       uint4 kb4[NC];
       uint32_t vnew[ND];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kb4[c] = *reinterpret_cast<const uint4*>(kr + kdim(c, j));
+      for (int c = 0; c < NC; ++c) kb4[c] = nr.kb4[c];
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) vnew[dt] = vr[16 * dt + n];
+      for (int dt = 0; dt < ND; ++dt) vnew[dt] = nr.vnew[dt];
       KT knew[S::NK];
       float ks_new = 0.f, vs_new = 0.f;
       if constexpr (FMT == PKV_FMT_BF16) {
@@ -375,7 +407,7 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
       }
       // the page write
       const int jp = t_new / bs;
-      const int page = trow[jp];
+      const int page = nr.page;
       if (page < 0 || page >= a.n_pages) {
         report(a.status, PKV_DEV_WRITE_PAGE);
       } else {

@@ -51,7 +51,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTiles = 2;  // 16-column tiles per wave: both use the same K/V operands
 constexpr int kPageWin = 512;  // page ids staged in LDS at a time
 constexpr int kHalves = 4;     // 32-token steps per staged block (one barrier each)
-constexpr float kRescaleSlack = 8.f;  // log2 units a maximum may pass the reference by
 
 template <int D>
 struct MultiLds {

@@ -35,6 +35,11 @@ namespace pkv {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// log2 units a column's maximum may pass its reference maximum by before the
+// reference moves and the running outputs are rescaled: weights taken against
+// the reference stay below 2^8, and most steps skip the rescale.
+constexpr float kRescaleSlack = 8.f;
+
 template <int FMT, int D>
 struct Step {
   static constexpr int NC = D / 32;  // 32-wide k chunks of the Q.K product

@@ -173,6 +173,12 @@ __device__ __forceinline__ void prefix_wave(const AttendArgs& a, int wid) {
     for (int x = 0; x < 8; ++x) vok[x] = lane_live && ts + 8 * j + x < t_stop;
     uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
     if (FMT == PKV_FMT_BF16 && (ts + 32 > t_stop || !r.live_a || !r.live_b)) v_keep_masks(vok, keep);
+    // int8: a dead slot's V scale may be any bits (NaN too): zero it, so its
+    // zero weight stays zero
+    if constexpr (FMT == PKV_FMT_INT8) {
+#pragma unroll
+      for (int x = 0; x < 8; ++x) vsc[x] = vok[x] ? vsc[x] : 0.f;
+    }
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       f32x4 sacc[2];

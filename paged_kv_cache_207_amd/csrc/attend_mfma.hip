@@ -567,7 +567,11 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
   // within this kernel's registers)
   if constexpr (PRE) {
     if ((int)blockIdx.x >= a.split_blocks) {
-      prefix_wave<FMT, D, BS, D == 64 ? 2 : 1>(a, (int)blockIdx.x - a.split_blocks);
+      constexpr int TT = prefix_tiles<D>();
+      if (a.qk_scale_log2 > 0.f)
+        prefix_wave<FMT, D, BS, TT, true>(a, (int)blockIdx.x - a.split_blocks);
+      else
+        prefix_wave<FMT, D, BS, TT, false>(a, (int)blockIdx.x - a.split_blocks);
       return;
     }
   }
@@ -714,7 +718,7 @@ hipError_t launch_sched(const AttendArgs& a, const Launch& l) {
   }
   // shared-prefix mode: split workgroups first, then the prefix waves, all
   // resident together when they fit (the split grid leaves room for them)
-  const int64_t pre = prefix_col_blocks<D == 64 ? 2 : 1>(a.batch, a.group) * a.n_kv_heads *
+  const int64_t pre = prefix_col_blocks<prefix_tiles<D>()>(a.batch, a.group) * a.n_kv_heads *
                       a.n_pchunks;
   int64_t split = a.split_wanted ? std::min<int64_t>(bound, resident) : 0;
   if (split > 0) split = std::max<int64_t>(1, std::min(split, std::max(resident - pre, resident / 2)));

@@ -90,8 +90,9 @@ __device__ __forceinline__ uint4 zero_dead(uint4 v, uint32_t dead_bits) {
   return uint4{w[0], w[1], w[2], w[3]};
 }
 
-// RAW (bf16 pages, a positive scale): the running maximum is taken over the
-// raw score sums and the scale goes into one fma inside the exponential.
+// RAW (a positive scale): scores stay in raw units (int8: times the token's
+// K scale) until the exponential, whose one fma applies the scale; the
+// running maximum is taken over raw scores and scaled once.
 template <int FMT, int D, int BS, bool RAW>
 __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) {
   using L = MultiLds<D>;
@@ -311,8 +312,6 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
   }
   const bf16x8 ones = as_bf16x8(uint4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
   const float qs = a.qk_scale_log2;
-  constexpr bool raw_max = RAW && FMT == PKV_FMT_BF16;  // the maximum of raw sums scales to
-                                                        // the maximum of scores (qs > 0)
 
   // The wave's smallest position: every column of the wave sees a step whole
   // when the step lies below it (and inside the block's range, on live pages).
@@ -356,33 +355,27 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
     bf16x8 pb[kTiles], ps[kTiles];
 #pragma unroll
     for (int u = 0; u < kTiles; ++u) {
-      // scores in log2 units: sacc * qs (int8: times the token's K scale).
-      // With bf16 pages and qs > 0 the maximum is taken over the raw sums and
-      // the scale goes into one fma inside the exponential.
-      float mx = -INFINITY;
+      // scores: raw sums (int8: times the token's K scale), in log2 units
+      // unless RAW.  A token the column may not see gets -inf, in place, and
+      // so a weight of exactly 0 (exp2(-inf) = 0): both paths share the
+      // exponentials below.
       float sv[8];
-      bool ok[8];  // token 8j + x of the step: on a valid page and seen by the column
-      if (open) {
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          sv[x] = sacc[u][x >> 2][x & 3];
-          if (FMT == PKV_FMT_INT8 || !raw_max) sv[x] *= qs * (FMT == PKV_FMT_INT8 ? ksc[x] : 1.f);
-          mx = fmaxf(mx, sv[x]);
-          ok[x] = true;
-        }
-        if (FMT == PKV_FMT_BF16 && raw_max) mx *= qs;
-      } else {
+      for (int x = 0; x < 8; ++x) {
+        sv[x] = sacc[u][x >> 2][x & 3];
+        if (FMT == PKV_FMT_INT8) sv[x] *= ksc[x];
+        if (!RAW) sv[x] *= qs;
+      }
+      if (!open) {
         const int lim = min(pos[u], t_end - 1) - ts - 8 * j;  // token 8j + x seen iff x <= lim
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          ok[x] = lane_live && x <= lim;
-          float y = sacc[u][x >> 2][x & 3] * qs;
-          if (FMT == PKV_FMT_INT8) y *= ksc[x];
-          sv[x] = ok[x] ? y : -INFINITY;
-          mx = fmaxf(mx, sv[x]);
-        }
+        for (int x = 0; x < 8; ++x) sv[x] = lane_live && x <= lim ? sv[x] : -INFINITY;
       }
+      float mx = sv[0];
+#pragma unroll
+      for (int x = 1; x < 8; ++x) mx = fmaxf(mx, sv[x]);
       mx = rows_max(mx);
+      if (RAW) mx *= qs;  // a positive scale keeps the maximum where it is
       const float m_new = fmaxf(m[u], mx);
       // Lazy rescale: the weights are taken against a reference maximum that
       // moves only when some column's maximum passed it by more than
@@ -393,22 +386,11 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
       const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
       float pw[8];
       float pv[8];  // the weights of the sums (int8: before the V scale)
-      if (open) {
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const float pr = FMT == PKV_FMT_BF16 && raw_max
-                               ? __builtin_amdgcn_exp2f(fmaf(sv[x], qs, -m_use))
-                               : __builtin_amdgcn_exp2f(sv[x] - m_use);
-          pv[x] = pr;
-          pw[x] = FMT == PKV_FMT_INT8 ? pr * vsc[x] : pr;
-        }
-      } else {
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const float pr = ok[x] ? __builtin_amdgcn_exp2f(sv[x] - m_use) : 0.f;
-          pv[x] = pr;
-          pw[x] = FMT == PKV_FMT_INT8 ? pr * vsc[x] : pr;
-        }
+      for (int x = 0; x < 8; ++x) {
+        const float pr = __builtin_amdgcn_exp2f(RAW ? fmaf(sv[x], qs, -m_use) : sv[x] - m_use);
+        pv[x] = pr;
+        pw[x] = FMT == PKV_FMT_INT8 ? pr * vsc[x] : pr;
       }
       pb[u] = as_bf16x8(uint4{pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3]),
                               pack_bf16x2(pw[4], pw[5]), pack_bf16x2(pw[6], pw[7])});
@@ -502,11 +484,9 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
 template <int FMT, int D, int BS>
 hipError_t launch_bs(const MultiArgs& a, const Launch& l) {
   const int64_t grid = multi_grid(a.batch, a.n_kv_heads, a.n_qgroups);
-  if constexpr (FMT == PKV_FMT_BF16) {
-    if (a.qk_scale_log2 > 0.f)
-      return launch1(attend_multi_kernel<FMT, D, BS, true>, dim3((unsigned)grid), dim3(kThreads),
-                     0, l, a);
-  }
+  if (a.qk_scale_log2 > 0.f)
+    return launch1(attend_multi_kernel<FMT, D, BS, true>, dim3((unsigned)grid), dim3(kThreads), 0,
+                   l, a);
   return launch1(attend_multi_kernel<FMT, D, BS, false>, dim3((unsigned)grid), dim3(kThreads), 0,
                  l, a);
 }

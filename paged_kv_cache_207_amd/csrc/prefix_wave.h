@@ -70,12 +70,22 @@ __device__ __forceinline__ void load_step_cached(Step<FMT, D>& r, const PageSrc&
   }
 }
 
-// Online-softmax state of one 16-column tile.
+// Online-softmax state of one 16-column tile: the reference maximum m (log2
+// units), the sums ls (taken by the matrix cores: every entry of a lane holds
+// its column's whole sum) and the unnormalised outputs o.
 template <int ND>
 struct Tile {
-  float m, l;
+  float m;
+  f32x4 ls;
   f32x4 o[ND];
 };
+
+// 16-column tiles per prefix wave: two at head_dim 64 (every K/V operand
+// serves both), one at 128 (within the registers of the decode path).
+template <int D>
+__host__ __device__ constexpr int prefix_tiles() {
+  return D == 64 ? 2 : 1;
+}
 
 // Prefix work items: (column block of 16 TT columns, KV head, chunk), column
 // blocks fastest.
@@ -86,8 +96,11 @@ __host__ __device__ inline int64_t prefix_col_blocks(int batch, int group) {
 
 // One prefix work item, done by one wave: TT tiles of 16 columns (TT = 2
 // shares every K/V operand between two tiles; TT = 1 keeps the registers of
-// the head_dim 128 decode path).
-template <int FMT, int D, int BS, int TT>
+// the head_dim 128 decode path).  RAW (a positive scale): scores stay in raw
+// units (int8: times the K scale) until the exponential, whose one fma
+// applies the scale, and the maximum is taken over raw scores and scaled
+// once.
+template <int FMT, int D, int BS, int TT, bool RAW>
 __device__ __forceinline__ void prefix_wave(const AttendArgs& a, int wid) {
   using S = Step<FMT, D>;
   constexpr int NC = S::NC, ND = S::ND;
@@ -131,12 +144,24 @@ __device__ __forceinline__ void prefix_wave(const AttendArgs& a, int wid) {
   for (int o1 = 1; o1 < 64; o1 <<= 1) bmax = max(bmax, __shfl_xor(bmax, o1, 64));
   bmax = __builtin_amdgcn_readfirstlane(bmax);
   const int t_stop = min(t_end, bmax);
+  // per tile, the smallest bound of its used columns (uniform): a step that
+  // ends by then is seen whole by every column of the tile; lim: this
+  // lane's column sees tokens t < lim
+  int bmin[TT], lim[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    int v = c0 + 16 * t + n < ncols ? bound[t] : 0x7fffffff;
+#pragma unroll
+    for (int o1 = 1; o1 < 64; o1 <<= 1) v = min(v, __shfl_xor(v, o1, 64));
+    bmin[t] = __builtin_amdgcn_readfirstlane(v);
+    lim[t] = min(bound[t], t_stop);
+  }
 
   Tile<ND> st[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
     st[t].m = -INFINITY;
-    st[t].l = 0.f;
+    st[t].ls = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) st[t].o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -163,58 +188,101 @@ __device__ __forceinline__ void prefix_wave(const AttendArgs& a, int wid) {
     if (BS == 16) pb = ts + 16 < t_stop ? __builtin_amdgcn_readlane(vpage, lp + 1 - pg0) : -1;
     load_step_cached<FMT, D, BS>(r, src, pa, pb, ts - lp * bs, g, lane);
   };
+  const bf16x8 ones = as_bf16x8(uint4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
   auto compute = [&](int ts, S& r) {
+    // uniform: every slot of the step is on a page and inside the range some
+    // column of the wave sees (the common case: nothing to mask)
+    const bool whole = ts + 32 <= t_stop && r.live_a && r.live_b;
     const bool lane_live = BS == 16 && j >= 2 ? r.live_b : r.live_a;
     float ksc[8], vsc[8];
     if constexpr (FMT == PKV_FMT_INT8) step_scales<FMT, D>(r, ksc, vsc);
-    // V slots no column may see are zeroed (they may hold NaN)
-    bool vok[8];
+    if (!whole) {
+      // V slots no column may see are zeroed (they may hold NaN); int8:
+      // their V scales, so that a zero weight stays zero
+      bool vok[8];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) vok[x] = lane_live && ts + 8 * j + x < t_stop;
-    uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
-    if (FMT == PKV_FMT_BF16 && (ts + 32 > t_stop || !r.live_a || !r.live_b)) v_keep_masks(vok, keep);
-    // int8: a dead slot's V scale may be any bits (NaN too): zero it, so its
-    // zero weight stays zero
-    if constexpr (FMT == PKV_FMT_INT8) {
+      for (int x = 0; x < 8; ++x) vok[x] = lane_live && ts + 8 * j + x < t_stop;
+      if constexpr (FMT == PKV_FMT_BF16) {
+        uint32_t keep[4];
+        v_keep_masks(vok, keep);
 #pragma unroll
-      for (int x = 0; x < 8; ++x) vsc[x] = vok[x] ? vsc[x] : 0.f;
+        for (int dt = 0; dt < ND; ++dt) {
+          r.v[dt].x &= keep[0];
+          r.v[dt].y &= keep[1];
+          r.v[dt].z &= keep[2];
+          r.v[dt].w &= keep[3];
+        }
+      } else {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) vsc[x] = vok[x] ? vsc[x] : 0.f;
+      }
+    }
+    // the P.V operand of every tile: V^T rows (int8 codes converted once)
+    bf16x8 va[ND];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      if constexpr (FMT == PKV_FMT_BF16) {
+        va[dt] = as_bf16x8(r.v[dt]);
+      } else {
+        const uint2 lo = codes_to_bf16(r.v[dt].x), hi = codes_to_bf16(r.v[dt].y);
+        va[dt] = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
+      }
     }
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       f32x4 sacc[2];
       step_scores<FMT, D>(r, qf[t], sacc);
+      // scores (RAW: unscaled; int8: times the K scale); a token the column
+      // may not see gets -inf, and so a weight of exactly 0 below
+      // (exp2(-inf) = 0: no select on the weights)
       float sv[8];
-      bool ok[8];
-      float mx = -INFINITY;
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        ok[x] = vok[x] && ts + 8 * j + x < bound[t];
-        float y = sacc[x >> 2][x & 3] * qs;
-        if (FMT == PKV_FMT_INT8) y *= ksc[x];
-        sv[x] = ok[x] ? y : -INFINITY;
-        mx = fmaxf(mx, sv[x]);
+        sv[x] = RAW ? sacc[x >> 2][x & 3] : sacc[x >> 2][x & 3] * qs;
+        if (FMT == PKV_FMT_INT8) sv[x] *= ksc[x];
       }
+      if (!(whole && ts + 32 <= bmin[t])) {  // uniform: some column sees part of the step
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+          sv[x] = lane_live && ts + 8 * j + x < lim[t] ? sv[x] : -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
       mx = rows_max(mx);
+      if (RAW) mx *= qs;  // a positive scale keeps the maximum where it is
       const float m_new = fmaxf(st[t].m, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(st[t].m - m_use);
-      float psum = 0.f;
-      float pw[8];
+      // the reference maximum moves only when some column's maximum passes
+      // it by more than kRescaleSlack (-inf + slack: any finite maximum), so
+      // weights stay below 2^kRescaleSlack and the outputs and sums are
+      // rescaled on few steps; the combine weighs each partial by its own
+      // reference
+      const bool grow = __builtin_amdgcn_ballot_w64(m_new > st[t].m + kRescaleSlack) != 0;
+      const float m_ref = grow ? m_new : st[t].m;
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      float p[8], pw[8];
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        const float p = ok[x] ? __builtin_amdgcn_exp2f(sv[x] - m_use) : 0.f;
-        psum += p;
-        pw[x] = FMT == PKV_FMT_INT8 ? p * vsc[x] : p;
+        p[x] = __builtin_amdgcn_exp2f(RAW ? __builtin_fmaf(sv[x], qs, -m_use) : sv[x] - m_use);
+        pw[x] = FMT == PKV_FMT_INT8 ? p[x] * vsc[x] : p[x];
       }
       const bf16x8 pb = as_bf16x8(uint4{pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3]),
                                         pack_bf16x2(pw[4], pw[5]), pack_bf16x2(pw[6], pw[7])});
-      st[t].l = st[t].l * alpha + psum;
-      st[t].m = m_new;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+      // the sums' operand: the weights themselves (int8: before the V scale)
+      const bf16x8 ps = FMT == PKV_FMT_INT8
+                            ? as_bf16x8(uint4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                              pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])})
+                            : pb;
+      if (grow) {
+        const float alpha = __builtin_amdgcn_exp2f(st[t].m - m_use);
+        st[t].ls *= alpha;
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) st[t].o[dt] *= alpha;
+        st[t].m = m_ref;
       }
-      step_pv<FMT, D>(r, pb, keep, st[t].o);
+      st[t].ls = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, ps, st[t].ls, 0, 0, 0);
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+        st[t].o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pb, st[t].o[dt], 0, 0, 0);
     }
   };
 
@@ -259,7 +327,7 @@ __device__ __forceinline__ void prefix_wave(const AttendArgs& a, int wid) {
   // ---- partials of this chunk: O^T lane layout = dims 16 dt + 4 j + i of column n ----
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
-    const float l = rows_sum(st[t].l);
+    const float l = st[t].ls[0];  // the column's whole sum, in every lane of the column
     if (c0 + 16 * t + n < ncols) {
       const int64_t row =
           (((int64_t)bcol[t] * a.n_q_heads + (int64_t)g * G + hcol[t]) * a.n_pchunks + chunk);

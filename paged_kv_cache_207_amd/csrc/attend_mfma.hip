@@ -303,10 +303,10 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
         float y = sacc[x >> 2][x & 3] * qs;
         if (FMT == PKV_FMT_INT8) y *= ksc[x];
         sv[x] = ok[x] ? y : -INFINITY;
-        mx = fmaxf(mx, sv[x]);
+        mx = fmax_fast(mx, sv[x]);
       }
       mx = rows_max(mx);
-      const float m_new = fmaxf(m, mx);
+      const float m_new = fmax_fast(m, mx);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m - m_use);
       float psum = 0.f;

@@ -373,10 +373,10 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
       }
       float mx = sv[0];
 #pragma unroll
-      for (int x = 1; x < 8; ++x) mx = fmaxf(mx, sv[x]);
+      for (int x = 1; x < 8; ++x) mx = fmax_fast(mx, sv[x]);
       mx = rows_max(mx);
       if (RAW) mx *= qs;  // a positive scale keeps the maximum where it is
-      const float m_new = fmaxf(m[u], mx);
+      const float m_new = fmax_fast(m[u], mx);
       // Lazy rescale: the weights are taken against a reference maximum that
       // moves only when some column's maximum passed it by more than
       // kRescaleSlack (log2 units), so weights stay below 2^kRescaleSlack and

@@ -30,6 +30,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
+// The larger of two floats as one v_maximum3_f32 (IEEE maximum: a NaN input
+// gives NaN).  fmaxf must quiet signalling NaNs first, an extra move per
+// operand that is not a known arithmetic result; the callers here never
+// pass NaN (a score the column may not see is -inf).
+__device__ __forceinline__ float fmax_fast(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 // Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one lane of each
 // 16-lane row), without LDS: v_permlane16_swap leaves rows (0, 0, 2, 2) in
 // one register and (1, 1, 3, 3) in the other, so combining the two pairs
@@ -37,10 +45,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float rows_max(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = fmax_fast(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return fmax_fast(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float rows_sum(float x) {
@@ -70,10 +78,10 @@ __device__ __forceinline__ float dpp_mov(float v) {
 // Max / sum over the whole wave, in every lane, without LDS: within rows by
 // DPP (pairs, quads, half-rows, rows), then across the four rows.
 __device__ __forceinline__ float wave_max(float x) {
-  x = fmaxf(x, dpp_mov<0xB1>(x));
-  x = fmaxf(x, dpp_mov<0x4E>(x));
-  x = fmaxf(x, dpp_mov<0x141>(x));
-  x = fmaxf(x, dpp_mov<0x140>(x));
+  x = fmax_fast(x, dpp_mov<0xB1>(x));
+  x = fmax_fast(x, dpp_mov<0x4E>(x));
+  x = fmax_fast(x, dpp_mov<0x141>(x));
+  x = fmax_fast(x, dpp_mov<0x140>(x));
   return rows_max(x);
 }
 

@@ -246,11 +246,12 @@ __device__ __forceinline__ void prefix_wave(const AttendArgs& a, int wid) {
         for (int x = 0; x < 8; ++x)
           sv[x] = lane_live && ts + 8 * j + x < lim[t] ? sv[x] : -INFINITY;
       }
-      float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      float mx = sv[0];
+#pragma unroll
+      for (int x = 1; x < 8; ++x) mx = fmax_fast(mx, sv[x]);
       mx = rows_max(mx);
       if (RAW) mx *= qs;  // a positive scale keeps the maximum where it is
-      const float m_new = fmaxf(st[t].m, mx);
+      const float m_new = fmax_fast(st[t].m, mx);
       // the reference maximum moves only when some column's maximum passes
       // it by more than kRescaleSlack (-inf + slack: any finite maximum), so
       // weights stay below 2^kRescaleSlack and the outputs and sums are

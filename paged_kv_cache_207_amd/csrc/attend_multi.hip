@@ -31,8 +31,13 @@
 // running maximum grew.
 //
 // LDS holds K as [32 tokens][head_dim] (tokens in score-tile order, see
-// k_row) and V as [head_dim][32 tokens], bf16, rows padded by 16 bytes so the
-// rows one read instruction touches fall on different banks.
+// k_row), rows padded by 32 bytes, and V as [head_dim][32 tokens], bf16, with
+// the four 16-byte token chunks of a row permuted (v_chunk), so the rows one
+// read instruction touches fall on different banks.  Measured on gfx950 for
+// 16-byte reads: rows padded by 16 bytes (or 48, 64) conflict 2-way, by 32
+// bytes not at all; unpadded V rows with the chunk index XOR-ed with bits 1-2
+// of the row do not conflict either (V padded by 32 bytes would not fit the
+// eight step buffers in LDS).
 //
 // Launch order is XCD-aware: workgroups are handed to the 8 XCDs in turn, so
 // block x runs on XCD x % 8; the blocks of one (sequence, KV head) are given
@@ -54,13 +59,16 @@ constexpr int kHalves = 4;     // 32-token steps per staged block (one barrier e
 
 template <int D>
 struct MultiLds {
-  static constexpr int KP = 2 * D + 16;       // K row pitch in bytes (one token)
-  static constexpr int VP = 2 * 32 + 16;      // V row pitch in bytes (one dim)
+  static constexpr int KP = 2 * D + 32;  // K row pitch in bytes (one token)
+  static constexpr int VP = 2 * 32;      // V row pitch in bytes (one dim), chunks permuted
   static constexpr int K_OFF = 0;
   static constexpr int V_OFF = 32 * KP;
   static constexpr int S_OFF = V_OFF + D * VP;  // int8: 32 K scales, then 32 V scales
   static constexpr int BUF = S_OFF + 64 * 4;
 };
+
+// Position of 16-byte chunk c (tokens 8c .. 8c+7) in the LDS row of dim d.
+__device__ __forceinline__ int v_chunk(int d, int c) { return c ^ ((d >> 1) & 3); }
 
 // LDS row of token r of a step: the 16 tokens of score tile t (token
 // 8 (n / 4) + 4t + n % 4 for row n) are stored in rows 16t .. 16t+15, so the
@@ -270,7 +278,7 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
       if (NVC % kThreads == 0 || q < NVC) {
         const int d = q / CV, kk = q - d * CV;
         const int t0 = kk * E;
-        char* dst = buf + L::V_OFF + d * L::VP + t0 * 2;
+        char* row = buf + L::V_OFF + d * L::VP;  // the chunks of tokens t0 ..
         // one bit per token of the chunk (its E tokens share one page half):
         // all on a missing page, else those at or past the range's end
         uint32_t dbits = 0;
@@ -278,13 +286,16 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
           const int keep = min(max(live_n - t0, 0), E);
           dbits = page_dead(t0) ? (1u << E) - 1u : ((1u << E) - 1u) & ~((1u << keep) - 1u);
         }
-        if constexpr (FMT == PKV_FMT_BF16) {
-          *reinterpret_cast<uint4*>(dst) = whole ? st.vc[i] : zero_dead(st.vc[i], dbits);
-        } else {
+        if constexpr (FMT == PKV_FMT_BF16) {  // one chunk of 8 tokens
+          *reinterpret_cast<uint4*>(row + 16 * v_chunk(d, kk)) =
+              whole ? st.vc[i] : zero_dead(st.vc[i], dbits);
+        } else {  // 16 codes: two chunks of bf16
           uint4 lo, hi;
           codes16_to_bf16(st.vc[i], lo, hi);
-          *reinterpret_cast<uint4*>(dst) = whole ? lo : zero_dead(lo, dbits & 0xffu);
-          *reinterpret_cast<uint4*>(dst + 16) = whole ? hi : zero_dead(hi, dbits >> 8);
+          *reinterpret_cast<uint4*>(row + 16 * v_chunk(d, 2 * kk)) =
+              whole ? lo : zero_dead(lo, dbits & 0xffu);
+          *reinterpret_cast<uint4*>(row + 16 * v_chunk(d, 2 * kk + 1)) =
+              whole ? hi : zero_dead(hi, dbits >> 8);
         }
       }
     }
@@ -409,7 +420,8 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
     uint4 vw[ND];
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
-      vw[dt] = *reinterpret_cast<const uint4*>(buf + L::V_OFF + (16 * dt + n) * L::VP + 16 * j);
+      vw[dt] = *reinterpret_cast<const uint4*>(buf + L::V_OFF + (16 * dt + n) * L::VP +
+                                               16 * v_chunk(16 * dt + n, j));
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll

@@ -360,31 +360,40 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
         vsc[x] = vv[x];
       }
     }
+    // the step's V operands, read now so the reads are in flight during the
+    // softmax
+    uint4 vw[ND];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+      vw[dt] = *reinterpret_cast<const uint4*>(buf + L::V_OFF + (16 * dt + n) * L::VP +
+                                               16 * v_chunk(16 * dt + n, j));
     // wave-uniform: every token of the step is seen by every column
     const bool open = live_a && live_b && ts + 31 <= pos_min && ts + 32 <= t_end;
     const bool lane_live = BS == 16 && j >= 2 ? live_b : live_a;
-    bf16x8 pb[kTiles], ps[kTiles];
+    // Phase 1, per tile: scores, maxima, the reference maximum and the rescale
+    // (rare); phase 2 then holds no branch, so the exponentials of one tile
+    // and the P.V products of the other can interleave.
+    float sv[kTiles][8], m_use[kTiles];
 #pragma unroll
     for (int u = 0; u < kTiles; ++u) {
       // scores: raw sums (int8: times the token's K scale), in log2 units
       // unless RAW.  A token the column may not see gets -inf, in place, and
       // so a weight of exactly 0 (exp2(-inf) = 0): both paths share the
       // exponentials below.
-      float sv[8];
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        sv[x] = sacc[u][x >> 2][x & 3];
-        if (FMT == PKV_FMT_INT8) sv[x] *= ksc[x];
-        if (!RAW) sv[x] *= qs;
+        sv[u][x] = sacc[u][x >> 2][x & 3];
+        if (FMT == PKV_FMT_INT8) sv[u][x] *= ksc[x];
+        if (!RAW) sv[u][x] *= qs;
       }
       if (!open) {
         const int lim = min(pos[u], t_end - 1) - ts - 8 * j;  // token 8j + x seen iff x <= lim
 #pragma unroll
-        for (int x = 0; x < 8; ++x) sv[x] = lane_live && x <= lim ? sv[x] : -INFINITY;
+        for (int x = 0; x < 8; ++x) sv[u][x] = lane_live && x <= lim ? sv[u][x] : -INFINITY;
       }
-      float mx = sv[0];
+      float mx = sv[u][0];
 #pragma unroll
-      for (int x = 1; x < 8; ++x) mx = fmax_fast(mx, sv[x]);
+      for (int x = 1; x < 8; ++x) mx = fmax_fast(mx, sv[u][x]);
       mx = rows_max(mx);
       if (RAW) mx *= qs;  // a positive scale keeps the maximum where it is
       const float m_new = fmax_fast(m[u], mx);
@@ -394,42 +403,38 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
       // the outputs and sums are rescaled on few steps.
       const bool grow = __any(m_new > m[u] + kRescaleSlack);  // -inf + slack: any finite max
       const float m_ref = grow ? m_new : m[u];
-      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-      float pw[8];
-      float pv[8];  // the weights of the sums (int8: before the V scale)
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const float pr = __builtin_amdgcn_exp2f(RAW ? fmaf(sv[x], qs, -m_use) : sv[x] - m_use);
-        pv[x] = pr;
-        pw[x] = FMT == PKV_FMT_INT8 ? pr * vsc[x] : pr;
-      }
-      pb[u] = as_bf16x8(uint4{pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3]),
-                              pack_bf16x2(pw[4], pw[5]), pack_bf16x2(pw[6], pw[7])});
-      ps[u] = FMT == PKV_FMT_INT8
-                  ? as_bf16x8(uint4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                                    pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])})
-                  : pb[u];
+      m_use[u] = m_ref == -INFINITY ? 0.f : m_ref;
       if (grow) {
-        const float alpha = __builtin_amdgcn_exp2f(m[u] - m_use);
+        const float alpha = __builtin_amdgcn_exp2f(m[u] - m_use[u]);
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) o[u][dt] *= alpha;
         ls[u] *= alpha;
         m[u] = m_ref;
       }
     }
-    uint4 vw[ND];
+    // Phase 2: weights, P.V and the sums
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-      vw[dt] = *reinterpret_cast<const uint4*>(buf + L::V_OFF + (16 * dt + n) * L::VP +
-                                               16 * v_chunk(16 * dt + n, j));
+    for (int u = 0; u < kTiles; ++u) {
+      float pw[8];
+      float pv[8];  // the weights of the sums (int8: before the V scale)
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
+      for (int x = 0; x < 8; ++x) {
+        const float pr = __builtin_amdgcn_exp2f(RAW ? fmaf(sv[u][x], qs, -m_use[u])
+                                                    : sv[u][x] - m_use[u]);
+        pv[x] = pr;
+        pw[x] = FMT == PKV_FMT_INT8 ? pr * vsc[x] : pr;
+      }
+      const bf16x8 pb = as_bf16x8(uint4{pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3]),
+                                        pack_bf16x2(pw[4], pw[5]), pack_bf16x2(pw[6], pw[7])});
+      const bf16x8 ps = FMT == PKV_FMT_INT8
+                            ? as_bf16x8(uint4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                              pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])})
+                            : pb;
 #pragma unroll
-      for (int u = 0; u < kTiles; ++u)
-        o[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vw[dt]), pb[u], o[u][dt], 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < kTiles; ++u)
-      ls[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, ps[u], ls[u], 0, 0, 0);
+      for (int dt = 0; dt < ND; ++dt)
+        o[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vw[dt]), pb, o[u][dt], 0, 0, 0);
+      ls[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, ps, ls[u], 0, 0, 0);
+    }
   };
 
   // ---- the step loop: the loads of step i+1 are in flight while step i is

@@ -323,9 +323,11 @@ def run_shared_prefix(args, device, cpu_seconds: float = 0.0):
     sequence at its length + paged_attend over length + 1 tokens.  The
     attention reads the 64 shared prefix pages once for all sequences
     (pkv_decode_step_prefix: a prefix pass over the shared pages, the split
-    pass over the private suffixes, the combine); the same job through
-    pkv_decode_step, which streams the prefix once per sequence, is timed
-    beside it.  Every timed job starts from the same rebuilt pool state
+    pass over the private suffixes, the combine), and the host grows its
+    tables one step ahead, so each step's launch also writes the next step's
+    table entries; the same job through pkv_decode_step, which streams the
+    prefix once per sequence and applies each step's entries with a table
+    update launch, is timed beside it.  Every timed job starts from the same rebuilt pool state
     (untimed)."""
     sp = W.shared_prefix()
     w = sp.base
@@ -368,11 +370,11 @@ def run_shared_prefix(args, device, cpu_seconds: float = 0.0):
     torch.cuda.synchronize()
     ones = np.ones(B, np.int32)
 
-    def step(s, shared):
+    def step(s, shared, next_updates=None):
         if shared:
             cache.decode_step_prefix(table, lens_all[s], max_len, prefix_pages, P0, qs[s],
                                      w.scale, k_new=ks[s], v_new=vs[s], out=out,
-                                     workspace=ws_pre)
+                                     workspace=ws_pre, next_updates=next_updates)
         else:
             cache.decode_step(table, lens_all[s], max_len, ks[s], vs[s], qs[s], w.scale,
                               out=out, workspace=ws_seq)
@@ -384,13 +386,26 @@ def run_shared_prefix(args, device, cpu_seconds: float = 0.0):
         torch.cuda.synchronize()
         return pool, seqs
 
+    def grow(seqs, s):  # every sequence grows by its new token: step s's new entries
+        seqs.append_all(ones)
+        n = seqs.take_updates(upd_host[s]).shape[0]
+        return upd_host[s][:n] if n else None
+
     def job(seqs, shared):
+        if not shared:
+            for s in range(sp.n_steps):
+                u = grow(seqs, s)
+                if u is not None:  # the kernel reads the step's pinned list in place
+                    pkv.table_apply(table, u)
+                step(s, False)
+            return
+        # the host grows its tables one step ahead: step s's launch writes the
+        # entries step s + 1 adds (no table-update launch inside the loop)
+        u = grow(seqs, 0)
+        if u is not None:
+            pkv.table_apply(table, u)
         for s in range(sp.n_steps):
-            seqs.append_all(ones)  # every sequence grows by its new token
-            n = seqs.take_updates(upd_host[s]).shape[0]
-            if n:  # the kernel reads the step's pinned list in place
-                pkv.table_apply(table, upd_host[s][:n])
-            step(s, shared)
+            step(s, True, grow(seqs, s + 1) if s + 1 < sp.n_steps else None)
 
     jobs = max(1, args.steps)
     res = {}
@@ -425,8 +440,10 @@ def run_shared_prefix(args, device, cpu_seconds: float = 0.0):
     assert diff <= 2e-2, diff
 
     # The shared-prefix job with each step's device work replayed from a HIP
-    # graph captured once (padded update list of fixed size: padding rows
-    # name no sequence and are skipped), the host table growth still per step.
+    # graph captured once (padded update lists of fixed size: padding rows
+    # name no sequence and are skipped), the host table growth still per step,
+    # one step ahead: step s's graph writes the entries of step s + 1 from
+    # its pinned list, which the host fills before replaying it.
     cap = B + 8
     g_upd_host = [torch.full((cap, 3), -1, dtype=torch.int32).pin_memory()
                   for _ in range(sp.n_steps)]
@@ -436,16 +453,20 @@ def run_shared_prefix(args, device, cpu_seconds: float = 0.0):
         for s in range(sp.n_steps):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=g_stream):
-                pkv.table_apply(table, g_upd_host[s])  # reads the pinned list in place
-                step(s, True)
+                step(s, True, g_upd_host[s + 1] if s + 1 < sp.n_steps else None)
             graphs.append(g)
     torch.cuda.synchronize()
 
     def graph_job(seqs):
-        for s in range(sp.n_steps):
+        def fill(s):
             seqs.append_all(ones)
             n = seqs.take_updates(g_upd_host[s]).shape[0]
             g_upd_host[s][n:].fill_(-1)
+        fill(0)
+        pkv.table_apply(table, g_upd_host[0])
+        for s in range(sp.n_steps):
+            if s + 1 < sp.n_steps:
+                fill(s + 1)
             graphs[s].replay()
 
     g_times = []
@@ -490,9 +511,10 @@ def run_shared_prefix(args, device, cpu_seconds: float = 0.0):
                    "value_bytes": "unique KV bytes (shared prefix once)"},
         "tokens_per_s": round(B * sp.n_steps / graph_job_s, 1),
         "logical_kv_GBps": round(logical / graph_job_s / 1e9, 2),
-        "job": "each step: host table growth (append_all, take_updates), then the step's "
-               "padded table update (table_apply reading the pinned list in place) and "
-               "decode_step_prefix replayed from a HIP graph captured once",
+        "job": "the host grows its tables one step ahead (append_all, take_updates into a "
+               "padded pinned list); each step's decode_step_prefix, replayed from a HIP "
+               "graph captured once, also writes the next step's table entries from that "
+               "list (one table_apply before the first step)",
         "eager": {"ms_per_job": round(res[True]["job_s"] * 1e3, 5),
                   "GBps_unique": round(unique / res[True]["job_s"] / 1e9, 2),
                   "note": "the same job with every library call launched from Python"},

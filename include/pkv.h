@@ -80,6 +80,8 @@ extern "C" {
                                    differ from the shared list (its result is wrong), or a
                                    decode-step row that would land inside the shared prefix
                                    (not written) */
+#define PKV_DEV_TABLE_NEXT 128u /* a next-step table update (pkv_decode_step_prefix) named an
+                                   entry the step itself reads (that update skipped) */
 
 typedef enum { PKV_FMT_F32 = 0, PKV_FMT_BF16 = 1, PKV_FMT_INT8 = 2 } pkv_format;
 typedef enum { PKV_DT_F32 = 0, PKV_DT_BF16 = 1 } pkv_dtype;
@@ -281,6 +283,19 @@ int pkv_decode_step(pkv_cache* cache, int32_t layer, const int32_t* table, int32
  *                 shared prefix is not written and sets PKV_DEV_PREFIX.
  *   workspace     at least pkv_prefix_workspace_size bytes, 256-byte aligned,
  *                 zeroed once (as for pkv_paged_attend).
+ *   next_upd      null, or n_next_upd block-table updates for the next step,
+ *                 in pkv_table_apply's form (int32 [n][3]: sequence, logical
+ *                 block, page; device memory or pinned host memory, read in
+ *                 place): the step's launch writes them into the table, so a
+ *                 decode loop needs no table-update launch of its own (the
+ *                 host grows its tables one step ahead: tiny-llm paged_kv.py
+ *                 begin_step, applied with the previous step).  Each must name
+ *                 an entry this step does not read, block * page_size >=
+ *                 lens[b]; one that does is skipped and sets
+ *                 PKV_DEV_TABLE_NEXT.  Rows outside the table are skipped, as
+ *                 by pkv_table_apply.  The host must neither change nor free
+ *                 the list until the stream has run the step.  The table is
+ *                 written only through these updates.
  *   flags         0 or PKV_ATTEND_COMBINE_KERNEL (EINVAL otherwise).
  * Matrix-core shapes only (bf16/int8 pages, bf16 q, head_dim 64/128, page
  * size 16 or a multiple of 32, groups of at most 16): EFORMAT otherwise.
@@ -288,13 +303,14 @@ int pkv_decode_step(pkv_cache* cache, int32_t layer, const int32_t* table, int32
 int pkv_prefix_workspace_size(const pkv_cache* cache, int32_t batch, int32_t n_q_heads,
                               int32_t max_len, int32_t prefix_len, int32_t split_tokens,
                               uint64_t* bytes);
-int pkv_decode_step_prefix(pkv_cache* cache, int32_t layer, const int32_t* table,
+int pkv_decode_step_prefix(pkv_cache* cache, int32_t layer, int32_t* table,
                            int32_t table_stride, const int32_t* lens, int32_t batch,
                            int32_t max_len, const int32_t* prefix_pages, int32_t prefix_len,
                            const void* k_new, const void* v_new, int32_t in_dtype, const void* q,
                            int32_t q_dtype, int32_t n_q_heads, float scale, void* out,
-                           void* workspace, uint64_t workspace_bytes, int32_t split_tokens,
-                           uint32_t flags, void* stream);
+                           void* workspace, uint64_t workspace_bytes, const int32_t* next_upd,
+                           int32_t n_next_upd, int32_t split_tokens, uint32_t flags,
+                           void* stream);
 
 /* Several queries per sequence (a chunk of new tokens, as in chunked
  * prefill).  Sequence b's T_b = cu_q[b+1] - cu_q[b] query rows stand for its

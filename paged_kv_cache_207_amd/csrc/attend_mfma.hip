@@ -566,6 +566,20 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
   // pass's waves (two column tiles per wave at head_dim 64; one at 128,
   // within this kernel's registers)
   if constexpr (PRE) {
+    // the next step's table updates, spread over the launch's workgroups;
+    // each names an entry no wave of this launch reads (checked: a row past
+    // the length), so writing it here races with nothing
+    for (int u = (int)blockIdx.x * 64 + lane; u < a.n_next_upd; u += (int)gridDim.x * 64) {
+      const int ub = a.next_upd[3 * u], blk = a.next_upd[3 * u + 1], pg = a.next_upd[3 * u + 2];
+      if (ub < 0 || ub >= B || blk < 0 || blk >= a.table_stride) continue;
+      int len = a.lens[ub];
+      len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
+      if ((int64_t)blk * bs < len) {
+        report(a.status, PKV_DEV_TABLE_NEXT);
+        continue;
+      }
+      a.upd_table[(int64_t)ub * a.table_stride + blk] = pg;
+    }
     if ((int)blockIdx.x >= a.split_blocks) {
       constexpr int TT = prefix_tiles<D>();
       if (a.qk_scale_log2 > 0.f)

@@ -164,11 +164,27 @@ WsLayout ws_layout_prefix(const pkv_cache* c, int batch, int n_q_heads, int n_sp
   return w;
 }
 
-// A shared prefix: the first `len` tokens of every sequence sit in `pages`.
+// A shared prefix: the first `len` tokens of every sequence sit in `pages`;
+// with `next_upd`, the launch also writes the next step's table updates.
 struct Prefix {
   const int32_t* pages;
   int32_t len;
+  const int32_t* next_upd = nullptr;
+  int32_t n_next_upd = 0;
+  int32_t* table = nullptr;
 };
+
+// The kernels read an update list in place: device memory or pinned host
+// memory (a pageable host list would fault the device).
+bool readable_in_place(const void* p) {
+  hipPointerAttribute_t at;
+  const hipError_t pe = hipPointerGetAttributes(&at, p);
+  if (pe != hipSuccess || at.type == hipMemoryTypeUnregistered || !at.devicePointer) {
+    (void)hipGetLastError();  // leave no sticky error for later launches
+    return false;
+  }
+  return true;
+}
 
 // Timing: while enabled, each kernel pass is launched with an event pair
 // that its dispatch stamps with the kernel's start and end; the pairs are
@@ -474,6 +490,9 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
     a.n_pchunks = prefix_chunks(P0, c->L.page_size);
     a.ws_pre_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.pre_o_off);
     a.ws_pre_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.pre_ml_off);
+    a.next_upd = pre->next_upd;
+    a.n_next_upd = pre->n_next_upd;
+    a.upd_table = pre->table;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
@@ -533,7 +552,7 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
   // (its extra workgroups); a decode step runs the split work even without
   // suffix tokens, which reports rows that would land inside the prefix.
   a.split_wanted = sfx_max > 0 || a.k_new ? 1 : 0;
-  if (sfx_max > 0 || (pre && (a.k_new || max_len > 0))) {
+  if (sfx_max > 0 || (pre && (a.k_new || max_len > 0 || a.n_next_upd > 0))) {
     Timer tm(c, PKV_T_ATTEND_SPLIT, s, timed);
     e = mfma ? pkv::launch_attend_mfma(a, c->L.format, tm.l)
              : pkv::launch_attend_valu(a, c->L.format, tm.l);
@@ -733,18 +752,28 @@ int pkv_prefix_workspace_size(const pkv_cache* c, int32_t batch, int32_t n_q_hea
   return PKV_OK;
 }
 
-int pkv_decode_step_prefix(pkv_cache* c, int32_t layer, const int32_t* table,
+int pkv_decode_step_prefix(pkv_cache* c, int32_t layer, int32_t* table,
                            int32_t table_stride, const int32_t* lens, int32_t batch,
                            int32_t max_len, const int32_t* prefix_pages, int32_t prefix_len,
                            const void* k_new, const void* v_new, int32_t in_dtype, const void* q,
                            int32_t q_dtype, int32_t n_q_heads, float scale, void* out,
-                           void* workspace, uint64_t workspace_bytes, int32_t split_tokens,
-                           uint32_t flags, void* stream) {
+                           void* workspace, uint64_t workspace_bytes, const int32_t* next_upd,
+                           int32_t n_next_upd, int32_t split_tokens, uint32_t flags,
+                           void* stream) {
   if (!c) return fail(PKV_EINVAL, "cache is null");
   if (!k_new != !v_new) return fail(PKV_EINVAL, "k_new and v_new must both be given or both null");
   if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
     return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
-  const Prefix pre{prefix_pages, prefix_len};
+  if (n_next_upd < 0) return fail(PKV_EINVAL, "negative update count");
+  if (n_next_upd > 0 && !next_upd) return fail(PKV_EINVAL, "null update list");
+  if (n_next_upd > 0 && !readable_in_place(next_upd))
+    return fail(PKV_EINVAL, "next_upd is neither device memory nor pinned host memory");
+  Prefix pre{prefix_pages, prefix_len};
+  if (batch > 0 && n_next_upd > 0) {
+    pre.next_upd = next_upd;
+    pre.n_next_upd = n_next_upd;
+    pre.table = table;
+  }
   return attend_impl(c, layer, q, q_dtype, n_q_heads, table, table_stride, lens, batch, max_len,
                      scale, out, workspace, workspace_bytes, split_tokens, flags, stream, k_new,
                      v_new, in_dtype, true, &pre);
@@ -791,14 +820,8 @@ int pkv_table_apply(int32_t* table, int32_t table_stride, int32_t batch, const i
   if (n < 0 || table_stride < 1 || batch < 0) return fail(PKV_EINVAL, "bad sizes");
   if (n == 0) return PKV_OK;
   if (!table || !upd) return fail(PKV_EINVAL, "null device pointer");
-  // the kernel reads upd in place: it must be device memory or pinned host
-  // memory (a pageable host list would fault the device)
-  hipPointerAttribute_t at;
-  const hipError_t pe = hipPointerGetAttributes(&at, upd);
-  if (pe != hipSuccess || at.type == hipMemoryTypeUnregistered || !at.devicePointer) {
-    (void)hipGetLastError();  // leave no sticky error for later launches
+  if (!readable_in_place(upd))
     return fail(PKV_EINVAL, "upd is neither device memory nor pinned host memory");
-  }
   hipError_t e = pkv::launch_table_apply(table, table_stride, batch, upd, n,
                                          static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_EHIP, "table update launch failed: %s", hipGetErrorString(e));

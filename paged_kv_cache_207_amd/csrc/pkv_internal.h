@@ -96,6 +96,12 @@ struct AttendArgs {
   // rows), then the prefix pass's waves
   int32_t split_blocks = 0;
   int32_t split_wanted = 1;
+  // shared-prefix mode: table updates for the next step (upd_table[b *
+  // table_stride + block] = page for each (b, block, page) row), each for an
+  // entry this launch does not read
+  const int32_t* next_upd = nullptr;
+  int32_t n_next_upd = 0;
+  int32_t* upd_table = nullptr;
 };
 
 // Arguments of the several-queries-per-sequence kernel (one launch = one

@@ -20,6 +20,7 @@ FMT_F32, FMT_BF16, FMT_INT8 = 0, 1, 2
 DT_F32, DT_BF16 = 0, 1
 DEV_WRITE_PAGE, DEV_WRITE_TABLE, DEV_READ_PAGE, DEV_LEN, DEV_QROWS, DEV_WRITE_ROWS = 1, 2, 4, 8, 16, 32
 DEV_PREFIX = 64
+DEV_TABLE_NEXT = 128
 ATTEND_VALU, ATTEND_COMBINE_KERNEL, ATTEND_COMBINE_FUSED = 1, 2, 4
 T_WRITE, T_ATTEND_SPLIT, T_ATTEND_COMBINE, T_GATHER, T_ATTEND_MULTI, T_COPY_PAGES = 0, 1, 2, 3, 4, 5
 T_COUNT = 6
@@ -51,7 +52,7 @@ SYMBOLS = [
      [_P, _I32, _I32, _I32, _I32, _I32, C.POINTER(C.c_uint64)]),
     ("pkv_decode_step_prefix", C.c_int,
      [_P, _I32, _P, _I32, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _I32, _F, _P, _P, _U64,
-      _I32, _U32, _P]),
+      _P, _I32, _I32, _U32, _P]),
     ("pkv_paged_attend_multi", C.c_int,
      [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _F, _P, _P]),
     ("pkv_gather", C.c_int, [_P, _I32, _P, _I32, _P, _P, _P, _P, _P]),
@@ -322,13 +323,16 @@ class PagedKVCache:
 
     def decode_step_prefix(self, table, lens, max_len: int, prefix_pages, prefix_len: int, q,
                            scale: float, k_new=None, v_new=None, out=None, workspace=None,
-                           split_tokens: int = 0, flags: int = 0,
-                           layer: int = 0) -> torch.Tensor:
+                           split_tokens: int = 0, flags: int = 0, layer: int = 0,
+                           next_updates=None) -> torch.Tensor:
         """Attention of one query per sequence whose first prefix_len tokens sit
         in the shared pages prefix_pages (device int32, prefix_len / page_size
         ids, the same first entries in every table row): the shared pages are
         read once for all sequences.  With k_new / v_new (bf16 [B, Hkv, D])
-        each sequence first gets its new row at lens[b] - 1, as decode_step."""
+        each sequence first gets its new row at lens[b] - 1, as decode_step.
+        next_updates: (sequence, block, page) rows [n, 3] for the next step
+        (GPU or pinned host int32, as table_apply takes), written into the
+        table by this step's launch; each must lie past its sequence's length."""
         self._check_decode_shapes(q, table, lens, out)
         B, Hq, D = q.shape
         if q.dtype not in DTYPE_CODE:
@@ -346,6 +350,7 @@ class PagedKVCache:
             out = torch.empty_like(q)
         if workspace is None:
             workspace = self.prefix_workspace(B, Hq, max_len, prefix_len, split_tokens)
+        up, n_up, host = _update_list(next_updates)
         _check(lib().pkv_decode_step_prefix(
             self._h, layer, _dev(table, torch.int32, "table"), table.shape[1],
             _dev(lens, torch.int32, "lens"), B, max_len,
@@ -353,7 +358,9 @@ class PagedKVCache:
             _dev(k_new, name="k_new"), _dev(v_new, name="v_new"), DT_BF16,
             _dev(q, name="q"), DTYPE_CODE[q.dtype], Hq, float(scale), _dev(out, q.dtype, "out"),
             _dev(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
-            split_tokens, flags, _stream(self.device)))
+            up, n_up, split_tokens, flags, _stream(self.device)))
+        if host and n_up > 0:
+            _hold_pinned(next_updates, self.device)
         return out
 
     # -- several queries per sequence (a chunk of new tokens) -------------------
@@ -438,33 +445,50 @@ def probe_stream(src: torch.Tensor, dst: torch.Tensor | None = None,
 _pinned_in_flight: list = []
 
 
+def _update_list(upd):
+    """(pointer, rows, is_host) of a [n, 3] int32 update list: a GPU tensor or
+    a pinned host tensor (read in place by the kernel); None gives no list."""
+    if upd is None:
+        return None, 0, False
+    if upd.dim() != 2 or upd.shape[1] != 3:
+        raise ValueError(f"an update list must be [n, 3], got {tuple(upd.shape)}")
+    if upd.shape[0] == 0:  # nothing to read (an empty tensor has no pinned storage)
+        return None, 0, False
+    if upd.is_cuda:
+        return _dev(upd, torch.int32, "upd"), upd.shape[0], False
+    if not upd.is_pinned():
+        raise ValueError("a host update list must be pinned")
+    if not upd.is_contiguous() or upd.dtype != torch.int32:
+        raise ValueError("an update list must be contiguous int32")
+    return C.c_void_p(upd.data_ptr()), upd.shape[0], True
+
+
+def _hold_pinned(upd, device) -> None:
+    """Keep a pinned list alive until the current stream has run its reader
+    (outside graph capture; under capture the caller keeps it alive for as
+    long as the graph may be replayed)."""
+    if torch.cuda.is_current_stream_capturing():
+        return
+    while _pinned_in_flight and _pinned_in_flight[0][0].query():
+        _pinned_in_flight.pop(0)
+    ev = torch.cuda.Event()
+    ev.record(torch.cuda.current_stream(device))
+    _pinned_in_flight.append((ev, upd))
+
+
 def table_apply(table: torch.Tensor, upd: torch.Tensor) -> None:
     """Apply (sequence, block, page) triples [n, 3] to a device block table.
     ``upd`` is a GPU tensor or a pinned host tensor, which the kernel reads
     in place (no copy launch).  Outside graph capture a pinned list is kept
     alive here until the stream has run the update; under capture the caller
     keeps it alive for as long as the graph may be replayed."""
-    if upd.dim() != 2 or upd.shape[1] != 3:
-        raise ValueError(f"upd must be [n, 3], got {tuple(upd.shape)}")
     if table.dim() != 2:
         raise ValueError("table must be [batch, stride]")
-    host = not upd.is_cuda
-    if host:
-        if not upd.is_pinned():
-            raise ValueError("a host update list must be pinned")
-        if not upd.is_contiguous() or upd.dtype != torch.int32:
-            raise ValueError("upd must be contiguous int32")
-        up = C.c_void_p(upd.data_ptr())
-    else:
-        up = _dev(upd, torch.int32, "upd")
+    up, n, host = _update_list(upd)
     _check(lib().pkv_table_apply(_dev(table, torch.int32, "table"), table.shape[1], table.shape[0],
-                                 up, upd.shape[0], _stream(table.device)))
-    if host and upd.shape[0] > 0 and not torch.cuda.is_current_stream_capturing():
-        while _pinned_in_flight and _pinned_in_flight[0][0].query():
-            _pinned_in_flight.pop(0)
-        ev = torch.cuda.Event()
-        ev.record(torch.cuda.current_stream(table.device))
-        _pinned_in_flight.append((ev, upd))
+                                 up, n, _stream(table.device)))
+    if host and n > 0:
+        _hold_pinned(upd, table.device)
 
 
 class PagePool:

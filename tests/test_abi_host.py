@@ -364,11 +364,11 @@ def test_prefix_validation():
     assert L.pkv_prefix_workspace_size(h, 2, 4, 50, 32, 0, C.byref(need)) == pkv.OK
 
     def s(prefix_len=32, flags=0, k=None, v=None, in_dt=pkv.DT_BF16, hq=4, pages=P,
-          ws_bytes=None, q_dt=pkv.DT_BF16, batch=2):
+          ws_bytes=None, q_dt=pkv.DT_BF16, batch=2, upd=None, n_upd=0):
         return L.pkv_decode_step_prefix(h, 0, P, 4, P, batch, 50, pages, prefix_len, k, v, in_dt,
                                         P, q_dt, hq, 0.125, P, P,
-                                        need.value if ws_bytes is None else ws_bytes, 0, flags,
-                                        None)
+                                        need.value if ws_bytes is None else ws_bytes, upd, n_upd,
+                                        0, flags, None)
 
     assert s(prefix_len=0) == pkv.EINVAL
     assert s(prefix_len=24) == pkv.EINVAL  # not a multiple of the page size
@@ -382,6 +382,11 @@ def test_prefix_validation():
     assert s(pages=None) == pkv.EINVAL
     assert s(ws_bytes=need.value - 1) == pkv.ENOMEM
     assert s(batch=0) == pkv.OK
+    # next-step table updates: a count, a list the kernel can read in place
+    assert s(n_upd=-1) == pkv.EINVAL
+    assert s(upd=None, n_upd=3) == pkv.EINVAL
+    host_list = (C.c_int32 * 9)()  # pageable host memory: refused before any launch
+    assert s(upd=C.cast(host_list, C.c_void_p), n_upd=3) == pkv.EINVAL
     L.pkv_cache_destroy(h)
     L, h = _cache(fmt=pkv.FMT_F32)
     assert s() == pkv.EFORMAT  # no matrix-core kernels for f32 pages

@@ -194,3 +194,98 @@ def test_prefix_reports_broken_promises():
     bk = before.view(torch.bfloat16).view(kv.shape)
     for p in cs.pre_pages.tolist():
         assert torch.equal(kv[p], bk[p])
+
+
+def test_prefix_step_applies_next_updates():
+    """A decode loop whose steps write the next step's table updates (the
+    host grows its tables one step ahead) leaves the same tables, pages and
+    outputs, bit for bit, as the loop with a table update launch before each
+    step; an update naming an entry the step reads is skipped and reported."""
+    require_gpu()
+    rng = np.random.default_rng(4100)
+    bs, Hkv, G, D, P0, B, S = 16, 2, 4, 64, 64, 7, 20
+    npre = P0 // bs
+    lens0 = rng.integers(P0 + 1, P0 + 40, size=B).astype(np.int32)
+    lens0[3] = 0  # an empty sequence stays empty (no row, no growth)
+    live = lens0 > 0
+    final = np.where(live, lens0 + S, 0)
+    priv = [max(-(-int(L) // bs) - npre, 0) for L in final]
+    P = npre + sum(priv) + 2
+    perm = rng.permutation(P).astype(np.int32)
+    stride = npre + max(priv) + 1
+    full = np.full((B, stride), -1, np.int32)
+    o = npre
+    for b in range(B):
+        if live[b]:
+            full[b, :npre] = perm[:npre]
+            full[b, npre:npre + priv[b]] = perm[o:o + priv[b]]
+        o += priv[b]
+
+    def upto(lens):  # the table a step with these lengths reads
+        t = np.full_like(full, -1)
+        for b in range(B):
+            n = -(-int(lens[b]) // bs)
+            t[b, :n] = full[b, :n]
+        return t
+
+    def updates(lens_from, lens_to):  # entries the longer lengths add
+        a, z = upto(lens_from), upto(lens_to)
+        rows = [(b, k, int(z[b, k])) for b in range(B) for k in range(stride) if a[b, k] != z[b, k]]
+        return torch.tensor(rows, dtype=torch.int32).reshape(-1, 3)
+
+    g = torch.Generator().manual_seed(4101)
+    pk = torch.randn(P0, Hkv, D, generator=g).to(torch.bfloat16)
+    pv = torch.randn(P0, Hkv, D, generator=g).to(torch.bfloat16)
+    n_sfx = np.maximum(lens0 - P0, 0).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(n_sfx)]).astype(np.int32)
+    sk = torch.randn(int(cu[-1]), Hkv, D, generator=g).to(torch.bfloat16)
+    sv = torch.randn(int(cu[-1]), Hkv, D, generator=g).to(torch.bfloat16)
+    qs = torch.randn(S, B, Hkv * G, D, generator=g).to(torch.bfloat16)
+    kn = torch.randn(S, B, Hkv, D, generator=g).to(torch.bfloat16)
+    vn = torch.randn(S, B, Hkv, D, generator=g).to(torch.bfloat16)
+    step_lens = [np.where(live, lens0 + s + 1, 0).astype(np.int32) for s in range(S)]
+
+    def setup():
+        c = pkv.PagedKVCache(P, bs, Hkv, D, "bf16")
+        c.k_pages.fill_(0xFF)
+        c.v_pages.fill_(0xFF)
+        t0 = dev(upto(lens0))
+        c.write(dev(perm[None, :npre]), dev([0]), dev([0, P0]), pk.cuda(), pv.cuda())
+        c.write(t0, dev(np.minimum(lens0, P0)), dev(cu), sk.cuda(), sv.cuda())
+        return c, t0
+
+    pre = dev(perm[:npre])
+    max_len = int(final.max())
+    scale = float(np.float32(D ** -0.5))
+    ca, ta = setup()
+    cb, tb = setup()
+    ws_a = ca.prefix_workspace(B, Hkv * G, max_len, P0)
+    ws_b = cb.prefix_workspace(B, Hkv * G, max_len, P0)
+    pkv.table_apply(tb, updates(lens0, step_lens[0]).cuda())
+    for s in range(S):
+        pkv.table_apply(ta, updates(lens0 if s == 0 else step_lens[s - 1], step_lens[s]).cuda())
+        L = dev(step_lens[s])
+        oa = ca.decode_step_prefix(ta, L, max_len, pre, P0, qs[s].cuda(), scale,
+                                   k_new=kn[s].cuda(), v_new=vn[s].cuda(), workspace=ws_a)
+        nxt = updates(step_lens[s], step_lens[s + 1]) if s + 1 < S else None
+        if nxt is not None and s % 2:
+            nxt = nxt.pin_memory()  # a pinned host list, read in place
+        elif nxt is not None:
+            nxt = nxt.cuda()
+        ob = cb.decode_step_prefix(tb, L, max_len, pre, P0, qs[s].cuda(), scale,
+                                   k_new=kn[s].cuda(), v_new=vn[s].cuda(), workspace=ws_b,
+                                   next_updates=nxt)
+        assert torch.equal(oa, ob), s
+    torch.cuda.synchronize()
+    assert torch.equal(ta, tb) and torch.equal(ta.cpu(), torch.from_numpy(upto(step_lens[-1])))
+    assert torch.equal(ca.k_pages, cb.k_pages) and torch.equal(ca.v_pages, cb.v_pages)
+    assert ca.status() == 0 and cb.status() == 0
+    # an update for an entry the step reads is skipped (the table keeps it)
+    b = int(np.flatnonzero(live)[0])
+    bad = torch.tensor([[b, npre, int(perm[-1])]], dtype=torch.int32).cuda()
+    L = dev(step_lens[-1])
+    cb.decode_step_prefix(tb, L, max_len, pre, P0, qs[0].cuda(), scale, workspace=ws_b,
+                          next_updates=bad)
+    torch.cuda.synchronize()
+    assert cb.status() == pkv.DEV_TABLE_NEXT
+    assert torch.equal(tb, ta)

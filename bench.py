@@ -150,17 +150,19 @@ def fill(w, cache, device):
     return table, [kv[b][0] for b in range(w.batch)], [kv[b][1] for b in range(w.batch)], info
 
 
-def read_probe(device, nbytes=4 << 30, reps=10) -> float:
+def read_probe(device, nbytes=4 << 30, reps=10, scrambled=False) -> float:
     """Achievable streaming-read rate: the probe kernel (16-byte non-temporal
-    loads, 32 768 workgroups) over 4 GiB, 10 launches back to back."""
+    loads, 4 KiB blocks, 16 blocks per wave) over 4 GiB, 10 launches back to
+    back; in order, or with the blocks in a scrambled order (the page slabs
+    of a fragmented pool)."""
     src = torch.empty(nbytes, dtype=torch.uint8, device=device)
     src.fill_(1)
     sink = torch.empty(pkv.lib().pkv_probe_blocks(nbytes), dtype=torch.float32, device=device)
-    pkv.probe_stream(src, sink=sink)
+    pkv.probe_stream(src, sink=sink, scrambled=scrambled)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
-        pkv.probe_stream(src, sink=sink)
+        pkv.probe_stream(src, sink=sink, scrambled=scrambled)
     e1.record()
     torch.cuda.synchronize()
     gbps = nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
@@ -755,8 +757,10 @@ def run_decode(args, device, name: str, headline: bool, cpu_seconds: float):
 
     if headline:
         read_gbps = read_probe(device)
+        read_pages_gbps = read_probe(device, scrambled=True)
         copy_gbps = calibration_copy(device)
-        log(f"probe: streaming read {read_gbps:.0f} GB/s, copy {copy_gbps:.0f} GB/s")
+        log(f"probe: streaming read {read_gbps:.0f} GB/s in order, {read_pages_gbps:.0f} GB/s "
+            f"as 4 KiB blocks in a scrambled order; copy {copy_gbps:.0f} GB/s")
 
     cache = pkv.PagedKVCache(w.n_pages, w.page_size, w.n_kv_heads, w.head_dim, w.kv_format,
                              device=device)
@@ -883,6 +887,9 @@ def run_decode(args, device, name: str, headline: bool, cpu_seconds: float):
     if headline:
         line["achievable_read_GBps"] = round(read_gbps, 1)
         line["split_pass_frac_of_achievable_read"] = round(achieved / read_gbps, 4)
+        # the pages of this workload are 4 KiB slabs in a shuffled order
+        line["achievable_read_4k_scrambled_GBps"] = round(read_pages_gbps, 1)
+        line["split_pass_frac_of_scrambled_read"] = round(achieved / read_pages_gbps, 4)
         line["cold_cache"] = {
             "split_pass_us": round(kt_cold["attend_split"] * 1e3, 2),
             "combine_us": round(kt_cold["attend_combine"] * 1e3, 2),

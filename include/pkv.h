@@ -397,10 +397,13 @@ int pkv_timing_enable(pkv_cache* cache, int32_t on);
 int pkv_timing_read(pkv_cache* cache, double* ms, int32_t* counts);
 
 /* Streaming probes, the denominators of a bandwidth figure: mode 0 reads
- * `bytes` from src (16-byte loads, every byte once; one float per workgroup
- * goes to sink[blocks]); mode 1 copies src to dst.  bytes must be a multiple
- * of 16 and both pointers 16-byte aligned.  pkv_probe_blocks gives the sink
- * length mode 0 needs. */
+ * `bytes` from src in order (16-byte loads, every byte once, 4 KiB blocks per
+ * wave; one float per workgroup goes to sink); mode 2 reads the same 4 KiB
+ * blocks in a scrambled order, as the pages of a fragmented pool are read
+ * (bytes must then be 4 KiB times a power of two, EINVAL otherwise); mode 1
+ * copies src to dst.  bytes must be a multiple of 16 and both pointers
+ * 16-byte aligned.  pkv_probe_blocks gives the sink length modes 0 and 2
+ * need. */
 int32_t pkv_probe_blocks(uint64_t bytes);
 int pkv_probe_stream(const void* src, void* dst, float* sink, uint64_t bytes, int32_t mode,
                      void* stream);

@@ -253,10 +253,16 @@ int32_t pkv_probe_blocks(uint64_t bytes) { return pkv::probe_blocks(bytes); }
 
 int pkv_probe_stream(const void* src, void* dst, float* sink, uint64_t bytes, int32_t mode,
                      void* stream) {
-  if (mode != 0 && mode != 1) return fail(PKV_EINVAL, "mode must be 0 or 1");
+  if (mode < 0 || mode > 2) return fail(PKV_EINVAL, "mode must be 0, 1 or 2");
   if (bytes == 0) return PKV_OK;
   if (bytes % 16) return fail(PKV_EINVAL, "bytes must be a multiple of 16");
-  if (!src || (mode == 1 && !dst) || (mode == 0 && !sink))
+  if (mode == 2) {
+    const uint64_t n_blk = bytes / 4096;
+    if (bytes % 4096 || (n_blk & (n_blk - 1)) || n_blk > (1ull << 31))
+      return fail(PKV_EINVAL, "a scrambled read needs 4 KiB times a power of two bytes");
+  }
+  if (bytes / 4096 > 0xffffffffull) return fail(PKV_EINVAL, "buffer too large for the probe");
+  if (!src || (mode == 1 && !dst) || (mode != 1 && !sink))
     return fail(PKV_EINVAL, "null device pointer");
   if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15)
     return fail(PKV_EINVAL, "pointers must be 16-byte aligned");

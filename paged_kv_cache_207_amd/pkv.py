@@ -426,14 +426,15 @@ class PagedKVCache:
 
 
 def probe_stream(src: torch.Tensor, dst: torch.Tensor | None = None,
-                 sink: torch.Tensor | None = None) -> None:
-    """Read every byte of src (dst None) or copy src to dst, on the current stream."""
+                 sink: torch.Tensor | None = None, scrambled: bool = False) -> None:
+    """Read every byte of src (dst None; in order, or as 4 KiB blocks in a
+    scrambled order) or copy src to dst, on the current stream."""
     nbytes = src.numel() * src.element_size()
     if dst is None:
         if sink is None or sink.numel() < lib().pkv_probe_blocks(nbytes):
             raise ValueError("sink must hold pkv_probe_blocks(bytes) floats")
-        _check(lib().pkv_probe_stream(_dev(src), None, _dev(sink, torch.float32), nbytes, 0,
-                                      _stream(src.device)))
+        _check(lib().pkv_probe_stream(_dev(src), None, _dev(sink, torch.float32), nbytes,
+                                      2 if scrambled else 0, _stream(src.device)))
     else:
         _check(lib().pkv_probe_stream(_dev(src), _dev(dst), None, nbytes, 1, _stream(src.device)))
 

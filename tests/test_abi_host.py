@@ -391,3 +391,17 @@ def test_prefix_validation():
     L, h = _cache(fmt=pkv.FMT_F32)
     assert s() == pkv.EFORMAT  # no matrix-core kernels for f32 pages
     L.pkv_cache_destroy(h)
+
+
+def test_probe_validation():
+    L = pkv.lib()
+    P = C.c_void_p(FAKE)
+    assert L.pkv_probe_stream(P, None, P, 4096, 3, None) == pkv.EINVAL  # no mode 3
+    assert L.pkv_probe_stream(P, None, P, 4095, 0, None) == pkv.EINVAL  # not 16-byte words
+    assert L.pkv_probe_stream(P, None, P, 3 * 4096, 2, None) == pkv.EINVAL  # not a power of two
+    assert L.pkv_probe_stream(P, None, P, 4096 + 16, 2, None) == pkv.EINVAL  # not whole blocks
+    assert L.pkv_probe_stream(P, None, None, 4096, 2, None) == pkv.EINVAL  # no sink
+    assert L.pkv_probe_stream(P, None, None, 4096, 1, None) == pkv.EINVAL  # copy without dst
+    assert L.pkv_probe_stream(P, None, P, 0, 2, None) == pkv.OK
+    assert L.pkv_probe_blocks(0) == 1 and L.pkv_probe_blocks(16 * 4096) == 1
+    assert L.pkv_probe_blocks(16 * 4096 + 4096) == 2

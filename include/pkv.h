@@ -30,8 +30,15 @@
  *     into the cache's device status word.
  *
  * Page layout in HBM (chosen for gfx950, see the pool layout note below):
- *   K pages  [n_layers][n_pages][n_kv_heads][page_size][head_dim]
- *            (per page and KV head one token-major slab: slot rows of head_dim)
+ *   K pages  [n_layers][n_pages][n_kv_heads][slab], one slab of page_size rows
+ *            of head_dim per page and KV head.  With row bytes R = head_dim *
+ *            element size: rows of 64 or 128 bytes are stored in 64-byte
+ *            pieces, piece-major (byte b of slot t's row at
+ *            ((b / 64) * page_size + m(t)) * 64 + b % 64, with m(t) =
+ *            ((t >> 2) & 1) * page_size / 2 + (t >> 3) * 4 + (t & 3) when
+ *            page_size is a multiple of 8, else m(t) = t: the rows one score
+ *            tile of a 32-token step reads lie together); other rows are
+ *            whole, in slot order (byte b of slot t at t * R + b)
  *   V pages  [n_layers][n_pages][n_kv_heads][head_dim][page_size]
  *            (per page and KV head one dim-major slab: for each dim, the
  *             page_size slots are contiguous)

@@ -418,7 +418,8 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
         if (n == 0) {  // lanes j = 0..3 of one row hold the whole K row
 #pragma unroll
           for (int c = 0; c < S::NK; ++c)
-            *reinterpret_cast<KT*>(kw + ((int64_t)slot * D + kdim(KPL * c, j)) * ESZ) = knew[c];
+            *reinterpret_cast<KT*>(kw + k_byte(slot, kdim(KPL * c, j) * ESZ, bs, D * ESZ)) =
+                knew[c];
         }
         if (j == 0) {  // lanes n = 0..15 hold every dim of the V row
 #pragma unroll

@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
         const bool on_b = BS == 16 && r >= 16;
         const int slot = BS == 16 ? (r & 15) : st.slot0 + r;
         st.kc[i] = stream_load<uint4, typename Step<FMT, D>::u32x4>(
-            kp + (on_b ? sb : sa) * slab_bytes + ((int64_t)slot * D + c * E) * ESZ);
+            kp + (on_b ? sb : sa) * slab_bytes + k_byte(slot, c * 16, bs, D * ESZ));
       }
     }
 #pragma unroll

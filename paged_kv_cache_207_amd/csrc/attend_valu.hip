@@ -69,6 +69,7 @@ __global__ __launch_bounds__(64) void attend_valu_kernel(AttendArgs a) {
 
   const int lane = threadIdx.x;
   const int D = a.head_dim, bs = a.page_size, G = a.group;
+  constexpr int kEsz = FMT == PKV_FMT_F32 ? 4 : FMT == PKV_FMT_BF16 ? 2 : 1;
   const int nhc = (G + kHeads - 1) / kHeads;
   const int s = blockIdx.x;
   const int g = blockIdx.y / nhc, hc = blockIdx.y - g * nhc;
@@ -120,10 +121,10 @@ __global__ __launch_bounds__(64) void attend_valu_kernel(AttendArgs a) {
     for (int hh = 0; hh < kHeads; ++hh) acc[hh] = 0.f;
     const int64_t slab = (a.layer_page0 + (page < 0 ? 0 : page)) * a.n_kv_heads + g;
     if (page >= 0) {
-      const int64_t kb = slab * slab_elems + (int64_t)slot * D;
+      const int64_t kb = slab * slab_elems;
       for (int d0 = 0; d0 < D; d0 += 8) {
-        float x[8];
-        load8<FMT>(a.k_pages, kb + d0, x);
+        float x[8];  // 8 elements: inside one 64-byte piece where rows are pieced
+        load8<FMT>(a.k_pages, kb + k_byte(slot, d0 * kEsz, bs, D * kEsz) / kEsz, x);
 #pragma unroll
         for (int hh = 0; hh < kHeads; ++hh) {
           if (hh < gc) {

@@ -57,9 +57,10 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
       const int t = t0 + r;
       if (t >= a.len) continue;
       uint4 x = {0, 0, 0, 0};
-      if (slab_off[r] >= 0) {
-        const int64_t e = slab_off[r] + (int64_t)slot_of[r] * D + d0;
-        x = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_pages) + e * ESZ);
+      if (slab_off[r] >= 0) {  // 16 bytes: inside one 64-byte piece where rows are pieced
+        const int64_t byte = slab_off[r] * ESZ + k_byte(slot_of[r], d0 * ESZ, a.page_size,
+                                                        D * ESZ);
+        x = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_pages) + byte);
       }
       const int64_t o = ((int64_t)t * a.n_kv_heads + h) * D + d0;
       *reinterpret_cast<uint4*>(static_cast<char*>(a.k_out) + o * ESZ) = x;

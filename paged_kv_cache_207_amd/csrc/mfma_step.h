@@ -153,10 +153,12 @@ __device__ __forceinline__ void load_step(Step<FMT, D>& r, const PageSrc& s, int
     const bool on_b = BS == 16 && tok >= 16;
     const char* kb = s.k + (on_b ? slab_b : slab_a) * s.slab_bytes;
     const int row = BS == 16 ? (tok & 15) : slot0 + tok;
+    // a load of 16 bytes stays inside one piece of the K layout (64 bytes
+    // or more for these rows)
 #pragma unroll
     for (int c = 0; c < S::NK; ++c)
       r.k[tau][c] = stream_load<typename S::KT, typename S::NKT>(
-          kb + (row * D + kdim_of<FMT>(S::KPL * c, j)) * ESZ);
+          kb + k_byte(row, kdim_of<FMT>(S::KPL * c, j) * ESZ, bs, D * ESZ));
   }
   // V operand: tokens 8j .. 8j+7 of dim 16 * dt + n
   const bool v_on_b = BS == 16 && j >= 2;

@@ -9,6 +9,33 @@ namespace pkv {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// ---- K page layout -------------------------------------------------------
+// A (page, KV head) slab of K holds page_size token rows of head_dim
+// elements.  Rows of 64 or 128 bytes (bf16 head_dim 64, int8 head_dim 64 or
+// 128) are stored piece-major: the first 64 bytes of every row, then the
+// next 64 bytes of every row, with the rows of a piece in k_slot order, which
+// places next to each other the rows one score tile of a 32-token step takes
+// from a page (tokens 8i + 4t + 0..3 for tile t).  A K load of the
+// matrix-core kernels (16 rows x 64 bytes per instruction) then reads runs
+// of 512 bytes or more instead of 16 separate 64-byte pieces: on gfx950,
+// reads of 4 KiB blocks as 16 pieces of 64 bytes per instruction stream at
+// 5.9 TB/s, as runs of 512 bytes at 6.8 (in-order reads 6.85); the
+// shared-prefix split launch (head_dim 64) went from 66.3 to 61.7 us, the
+// int8 split pass from 88.8 to 87.3.  Other rows keep slot order, whole
+// (bf16 head_dim 128 measured 1% slower piece-major).
+__host__ __device__ constexpr bool k_pieced(int row_bytes) {
+  return row_bytes == 64 || row_bytes == 128;
+}
+__host__ __device__ constexpr int k_slot(int t, int bs, int row_bytes) {
+  return (!k_pieced(row_bytes) || (bs & 7)) ? t
+                                            : ((t >> 2) & 1) * (bs >> 1) + (t >> 3) * 4 + (t & 3);
+}
+// Byte offset, within its slab, of byte b of token t's K row.
+__host__ __device__ constexpr int k_byte(int t, int b, int bs, int row_bytes) {
+  return k_pieced(row_bytes) ? ((b >> 6) * bs + k_slot(t, bs, row_bytes)) * 64 + (b & 63)
+                             : t * row_bytes + b;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

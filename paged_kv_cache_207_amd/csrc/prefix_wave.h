@@ -52,7 +52,7 @@ __device__ __forceinline__ void load_step_cached(Step<FMT, D>& r, const PageSrc&
 #pragma unroll
     for (int c = 0; c < S::NK; ++c)
       r.k[tau][c] = *reinterpret_cast<const typename S::KT*>(
-          kb + (row * D + kdim_of<FMT>(S::KPL * c, j)) * ESZ);
+          kb + k_byte(row, kdim_of<FMT>(S::KPL * c, j) * ESZ, bs, D * ESZ));
   }
   const bool v_on_b = BS == 16 && j >= 2;
   const char* vb = s.v + (v_on_b ? slab_b : slab_a) * s.slab_bytes;

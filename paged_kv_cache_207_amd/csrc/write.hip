@@ -37,7 +37,8 @@ constexpr int kRows = 16;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct RowMeta {
-  int64_t k_off;  // element offset of the row's K slot row, -1 = skip
+  int64_t k_off;  // element offset of the row's K slab, -1 = skip
+  int slot;       // the row's slot in its page
   int64_t v_off;  // element offset of (dim 0, slot) in the V slab
   int64_t s_off;  // scale index (slab * page_size + slot)
 };
@@ -58,7 +59,7 @@ __device__ __forceinline__ bool group_is_run(const RowMeta* meta, int rr0, int n
 // position has no page (reported in the status word).
 __device__ __forceinline__ RowMeta slot_meta(const WriteArgs& a, int b, int t, int h,
                                              int64_t layer_page0) {
-  RowMeta m{-1, 0, 0};
+  RowMeta m{-1, 0, 0, 0};
   const int j = t >= 0 ? t / a.page_size : -1;
   if (t < 0 || j >= a.table_stride) {
     report(a.status, PKV_DEV_WRITE_TABLE);
@@ -71,7 +72,8 @@ __device__ __forceinline__ RowMeta slot_meta(const WriteArgs& a, int b, int t, i
   }
   const int slot = t - j * a.page_size;
   const int64_t slab = (layer_page0 + page) * a.n_kv_heads + h;
-  m.k_off = (slab * a.page_size + slot) * a.head_dim;
+  m.k_off = slab * a.page_size * a.head_dim;
+  m.slot = slot;
   m.v_off = slab * a.page_size * a.head_dim + slot;
   m.s_off = slab * a.page_size + slot;
   return m;
@@ -243,8 +245,10 @@ __global__ __launch_bounds__(64) void write_kernel(WriteArgs a) {
       const int rr = rr_[it], d0 = d0_[it];
       if (rr < kRows) {
         const int64_t k_off = meta[rr].k_off;
-        if (k_off >= 0)
-          *reinterpret_cast<u32x4*>(static_cast<char*>(a.k_pages) + (k_off + d0) * OESZ) = kx[it];
+        if (k_off >= 0)  // 16 bytes: inside one 64-byte piece where K rows are pieced
+          *reinterpret_cast<u32x4*>(static_cast<char*>(a.k_pages) + k_off * OESZ +
+                                    k_byte(meta[rr].slot, d0 * OESZ, a.page_size, D * OESZ)) =
+              kx[it];
       }
     }
     // V: groups of GV rows.  A group whose rows are consecutive slots of one
@@ -343,7 +347,8 @@ __global__ __launch_bounds__(64) void write_kernel(WriteArgs a) {
         vector_codes<IN_BF16>(kx[it], __uint_as_float(rmax[0][rr]), kc);
         vector_codes<IN_BF16>(vx[it], __uint_as_float(rmax[1][rr]), vc);
         const int64_t k_off = meta[rr].k_off;
-        int8_t* dst = static_cast<int8_t*>(a.k_pages) + k_off + d0;
+        int8_t* dst = static_cast<int8_t*>(a.k_pages) + k_off +
+                      k_byte(meta[rr].slot, d0, a.page_size, D);
         if constexpr (EPV == 8) {
           if (k_off >= 0) *reinterpret_cast<uint2*>(dst) = uint2{kc[0], kc[EPV / 4 - 1]};
           *reinterpret_cast<uint2*>(cv + rr * pb + d0) = uint2{vc[0], vc[EPV / 4 - 1]};

@@ -177,8 +177,10 @@ class PagedKVCache:
 
     # -- typed views of the page arrays (layout of include/pkv.h) --------------
     def k_view(self) -> torch.Tensor:
+        """[layers, pages, kv_heads, page_size * head_dim]: each (page, KV head)
+        slab of K as stored (piece-major rows in slot order, see include/pkv.h)."""
         L, P, H, bs, D = self.n_layers, self.n_pages, self.n_kv_heads, self.page_size, self.head_dim
-        return self.k_pages.view(PAGE_DTYPE[self.fmt]).view(L, P, H, bs, D)
+        return self.k_pages.view(PAGE_DTYPE[self.fmt]).view(L, P, H, bs * D)
 
     def v_view(self) -> torch.Tensor:
         L, P, H, bs, D = self.n_layers, self.n_pages, self.n_kv_heads, self.page_size, self.head_dim

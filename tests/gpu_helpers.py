@@ -51,10 +51,26 @@ def gpu_write(c, table_dev, rounds, layer=0):
         c.write(table_dev, dev(r.start_pos), dev(r.cu_new), r.k.cuda(), r.v.cuda(), layer=layer)
 
 
+def k_token_rows(c) -> torch.Tensor:
+    """GPU K pages as [layer][page][kv_head][slot][dim] elements, undoing the
+    K layout of include/pkv.h: rows of 64 or 128 bytes in 64-byte pieces,
+    piece-major, the rows of a piece in slot order m(t) (when the page size is
+    a multiple of 8); other rows whole, in slot order."""
+    L, P, H, bs, D = c.n_layers, c.n_pages, c.n_kv_heads, c.page_size, c.head_dim
+    raw = c.k_pages.view(L, P, H, -1)  # bytes of each slab
+    rb = raw.shape[-1] // bs
+    if rb in (64, 128):
+        m = [t if bs % 8 else ((t >> 2) & 1) * (bs // 2) + (t >> 3) * 4 + (t & 3)
+             for t in range(bs)]
+        x = raw.view(L, P, H, rb // 64, bs, 64)[:, :, :, :, m]
+        raw = x.permute(0, 1, 2, 4, 3, 5).reshape(L, P, H, bs * rb).contiguous()
+    return raw.view(c.k_view().dtype).view(L, P, H, bs, D)
+
+
 def pages_in_oracle_order(c):
     """GPU pages as [layer][page][slot][kv_head][dim] bit patterns (+ int8 scales
     as [layer][page][slot][kv_head])."""
-    K = c.k_view().permute(0, 1, 3, 2, 4).contiguous().cpu()
+    K = k_token_rows(c).permute(0, 1, 3, 2, 4).contiguous().cpu()
     V = c.v_view().permute(0, 1, 4, 2, 3).contiguous().cpu()
     if c.fmt == "int8":
         ks, vs = c.scale_views()

@@ -46,6 +46,15 @@ namespace {
 // small calls, so their partials stay few).
 constexpr int kMinWaveSteps = 8;
 
+// Most waves per workgroup.  Each wave takes its own work; the workgroup's
+// first wave builds the schedule in LDS for all of them.  The dispatcher
+// hands workgroups to the XCDs in turn, and with one-wave workgroups the
+// last XCDs received theirs 2.5-4 us after the first (per-wave start stamps
+// of a 1024-wave launch): several waves a workgroup shorten that stagger.
+// A launch with fewer waves than four per compute unit takes narrower
+// workgroups, so that its waves still spread over every compute unit.
+constexpr int kGroupWaves = 4;
+
 
 // Partials are exchanged between workgroups, which may sit on different XCDs
 // with separate L2 caches.  Writers store them as agent-scope relaxed atomics
@@ -104,14 +113,14 @@ __device__ __forceinline__ void combine_group(const AttendArgs& a, int b, int g,
 // balanced schedule's loop state.
 template <int FMT, int D, int BS, bool SB>
 __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* fpre,
-                                           const int32_t* qpre, const int32_t* lens) {
+                                           const int32_t* qpre, const int32_t* lens, int vb) {
   using S = Step<FMT, D>;
   using KT = typename S::KT;
   constexpr int NC = S::NC, ND = S::ND;
   constexpr int ESZ = FMT == PKV_FMT_BF16 ? 2 : 1;
   constexpr int KPL = S::KPL;
   auto kdim = [](int c, int jj) { return kdim_of<FMT>(c, jj); };
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int n = lane & 15;  // head column (B/C operands), row (A operands)
   const int j = lane >> 4;  // k group (A/B operands), row quad (C operand)
   const int G = a.group;
@@ -123,8 +132,8 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
 
   // sequences with no tokens have no work item: their output is zero (with a
   // shared prefix the combine writes every output)
-  const int nblk = a.prefix_len > 0 ? a.split_blocks : (int)gridDim.x;  // split-pass workgroups
-  for (int b = blockIdx.x; b < (a.prefix_len > 0 ? 0 : B); b += nblk) {
+  const int nblk = a.split_waves;  // split-pass waves; this one is wave vb
+  for (int b = vb; b < (a.prefix_len > 0 ? 0 : B); b += nblk) {
     if (lens[b] != 0) continue;
     for (int i = lane; i < a.n_q_heads * D / 4; i += 64)
       store_out4(a.out, a.q_bf16, (int64_t)b * a.n_q_heads * D + 4 * i, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -137,12 +146,12 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
     T = __builtin_amdgcn_readfirstlane(fpre[B]);
     const int64_t want = std::max<int64_t>(1, (T + kMinWaveSteps - 1) / kMinWaveSteps);
     n_waves = (int)std::min<int64_t>(nblk, want);
-    if ((int)blockIdx.x < n_waves) {
-      F = (int64_t)blockIdx.x * T / n_waves;
-      F1 = ((int64_t)blockIdx.x + 1) * T / n_waves;
+    if (vb < n_waves) {
+      F = (int64_t)vb * T / n_waves;
+      F1 = ((int64_t)vb + 1) * T / n_waves;
     }
   }
-  int item = blockIdx.x;
+  int item = vb;
 
   for (;;) {
   // ---- the next piece: tokens [t_begin, t_end) of unit (b, g); `direct`
@@ -176,7 +185,7 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
     direct = p_lo == s_first && p_hi == u_end && a.prefix_len == 0;
     owns_new = a.k_new != nullptr && p_hi == u_end;
     const int unit = b * a.n_kv_heads + g;
-    const int slot = unit + (int)blockIdx.x;  // strictly increasing along the flat space
+    const int slot = unit + vb;  // strictly increasing along the flat space
     row_base = (int64_t)slot * G;
     row_step = 1;
     if (p_lo == s_first && lane == 0) {
@@ -184,7 +193,7 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
       // waves from this one to the one holding the unit's last step (one
       // piece: the output is written here and the combine skips the unit)
       const int w_last = (int)((u_end * n_waves - 1) / T);
-      *reinterpret_cast<int2*>(a.ws_desc + 2 * unit) = int2{slot, w_last - (int)blockIdx.x + 1};
+      *reinterpret_cast<int2*>(a.ws_desc + 2 * unit) = int2{slot, w_last - vb + 1};
     }
   } else {
     if (item >= n_items) break;
@@ -548,14 +557,15 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
 }
 
 template <int FMT, int D, int BS, bool BAL, bool PRE>
-__global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
+__global__ __launch_bounds__(64 * kGroupWaves, 2) void attend_mfma_kernel(AttendArgs a) {
   using S = Step<FMT, D>;
   using KT = typename S::KT;
   constexpr int NC = S::NC, ND = S::ND;
   constexpr int ESZ = FMT == PKV_FMT_BF16 ? 2 : 1;
   constexpr int KPL = S::KPL;
   auto kdim = [](int c, int jj) { return kdim_of<FMT>(c, jj); };
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int n = lane & 15;  // head column (B/C operands), row (A operands)
   const int j = lane >> 4;  // k group (A/B operands), row quad (C operand)
   const int G = a.group;
@@ -570,7 +580,8 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
     // the next step's table updates, spread over the launch's workgroups;
     // each names an entry no wave of this launch reads (checked: a row past
     // the length), so writing it here races with nothing
-    for (int u = (int)blockIdx.x * 64 + lane; u < a.n_next_upd; u += (int)gridDim.x * 64) {
+    for (int u = (int)(blockIdx.x * blockDim.x + threadIdx.x); u < a.n_next_upd;
+         u += (int)(gridDim.x * blockDim.x)) {
       const int ub = a.next_upd[3 * u], blk = a.next_upd[3 * u + 1], pg = a.next_upd[3 * u + 2];
       if (ub < 0 || ub >= B || blk < 0 || blk >= a.table_stride) continue;
       int len = a.lens[ub];
@@ -581,12 +592,16 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
       }
       a.upd_table[(int64_t)ub * a.table_stride + blk] = pg;
     }
-    if ((int)blockIdx.x >= a.split_blocks) {
+    if ((int)blockIdx.x >= a.split_blocks) {  // a workgroup of prefix waves only
       constexpr int TT = prefix_tiles<D>();
-      if (a.qk_scale_log2 > 0.f)
-        prefix_wave<FMT, D, BS, TT, true>(a, (int)blockIdx.x - a.split_blocks);
-      else
-        prefix_wave<FMT, D, BS, TT, false>(a, (int)blockIdx.x - a.split_blocks);
+      const int wid = ((int)blockIdx.x - a.split_blocks) * (int)(blockDim.x >> 6) + wave;
+      const int n_pre = (int)prefix_col_blocks<TT>(B, G) * a.n_kv_heads * a.n_pchunks;
+      if (wid < n_pre) {
+        if (a.qk_scale_log2 > 0.f)
+          prefix_wave<FMT, D, BS, TT, true>(a, wid);
+        else
+          prefix_wave<FMT, D, BS, TT, false>(a, wid);
+      }
       return;
     }
   }
@@ -595,8 +610,7 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
   // Fixed splits: exclusive prefix sums over the sequences of their full
   // splits and of their partial last splits, and the clamped lengths.  Work
   // items are (split, KV head) pairs, full splits first, so the longest items
-  // are handed out first; each workgroup takes items blockIdx.x,
-  // blockIdx.x + gridDim.x, ...
+  // are handed out first; split wave v takes items v, v + split_waves, ...
   // Balanced (BAL): every (sequence, KV head) unit is a run of 32-token steps
   // preceded by unit_cost set-up slots (its query, table and first loads
   // start cold); fpre holds the exclusive prefix of the sequences' costs
@@ -611,102 +625,111 @@ __global__ __launch_bounds__(64, 2) void attend_mfma_kernel(AttendArgs a) {
   int32_t* fpre = wl;              // [B + 1]
   int32_t* qpre = wl + B + 1;      // [B + 1]
   int32_t* lens = wl + 2 * B + 2;  // [B]
-  // clamped lengths into LDS (one load round trip), with the shortest and
-  // longest non-empty ones
-  int lmin = INT_MAX, lmax = 0;
-  for (int b0 = 0; b0 < B; b0 += 256) {
-    int lv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int bb = b0 + 64 * u + lane;
-      lv[u] = bb < B ? a.lens[bb] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int bb = b0 + 64 * u + lane;
-      int len = clamp_len(lv[u], a.max_len, blockIdx.x == 0 ? a.status : nullptr,
-                          PKV_DEV_LEN);
-      if (a.prefix_len > 0) {
-        // the private suffix past the shared prefix; a decode step's new row
-        // must land in it
-        if (a.k_new && bb < B && len > 0 && len <= a.prefix_len && blockIdx.x == 0)
-          report(a.status, PKV_DEV_PREFIX);
-        len = max(len - a.prefix_len, 0);
-      }
-      if (bb < B) {
-        lens[bb] = len;
-        if (len > 0) {
-          lmin = min(lmin, len);
-          lmax = max(lmax, len);
-        }
-      }
-    }
-  }
-  bool balanced = false;
-  if constexpr (BAL) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      lmin = min(lmin, __shfl_xor(lmin, o, 64));
-      lmax = max(lmax, __shfl_xor(lmax, o, 64));
-    }
-    balanced = __builtin_amdgcn_readfirstlane(lmin < lmax ? 1 : 0) != 0;
-    if (blockIdx.x == 0 && lane == 0) *a.ws_sched = balanced ? 1 : 0;
-  }
-  // exclusive prefix sums of the schedule's counts, from the LDS lengths
-  // (each lane reads back the entries it wrote)
-  {
-    int carry_f = 0, carry_q = 0;
+  int32_t* sched = wl + 3 * B + 2;  // [1]: the balanced schedule is taken
+  // the workgroup's first wave builds the schedule for all of its waves
+  if (wave == 0) {
+    // clamped lengths into LDS (one load round trip), with the shortest and
+    // longest non-empty ones
+    int lmin = INT_MAX, lmax = 0;
     for (int b0 = 0; b0 < B; b0 += 256) {
+      int lv[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int bb = b0 + 64 * u + lane;
-        const int len = bb < B ? lens[bb] : 0;
-        int f, q;
-        if (balanced) {
-          const int steps = (len + 31) >> 5;
-          f = bb < B && steps > 0 ? a.n_kv_heads * (steps + a.unit_cost) : 0;
-          q = 0;
-        } else {
-          f = bb < B ? len / C : 0;
-          q = bb < B && len % C != 0 ? 1 : 0;
-        }
-        int sf = f, sq = q;
+        lv[u] = bb < B ? a.lens[bb] : 0;
+      }
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int tf = __shfl_up(sf, o, 64), tq = __shfl_up(sq, o, 64);
-          if (lane >= o) {
-            sf += tf;
-            sq += tq;
-          }
+      for (int u = 0; u < 4; ++u) {
+        const int bb = b0 + 64 * u + lane;
+        int len = clamp_len(lv[u], a.max_len, blockIdx.x == 0 ? a.status : nullptr,
+                            PKV_DEV_LEN);
+        if (a.prefix_len > 0) {
+          // the private suffix past the shared prefix; a decode step's new row
+          // must land in it
+          if (a.k_new && bb < B && len > 0 && len <= a.prefix_len && blockIdx.x == 0)
+            report(a.status, PKV_DEV_PREFIX);
+          len = max(len - a.prefix_len, 0);
         }
         if (bb < B) {
-          fpre[bb] = carry_f + sf - f;
-          qpre[bb] = carry_q + sq - q;
+          lens[bb] = len;
+          if (len > 0) {
+            lmin = min(lmin, len);
+            lmax = max(lmax, len);
+          }
         }
-        carry_f += __shfl(sf, 63, 64);
-        carry_q += __shfl(sq, 63, 64);
       }
     }
-    if (lane == 0) {
-      fpre[B] = carry_f;
-      qpre[B] = carry_q;
+    bool balanced = false;
+    if constexpr (BAL) {
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        lmin = min(lmin, __shfl_xor(lmin, o, 64));
+        lmax = max(lmax, __shfl_xor(lmax, o, 64));
+      }
+      balanced = __builtin_amdgcn_readfirstlane(lmin < lmax ? 1 : 0) != 0;
+      if (blockIdx.x == 0 && lane == 0) *a.ws_sched = balanced ? 1 : 0;
     }
-  }
+    if (lane == 0) *sched = balanced ? 1 : 0;
+    // exclusive prefix sums of the schedule's counts, from the LDS lengths
+    // (each lane reads back the entries it wrote)
+    {
+      int carry_f = 0, carry_q = 0;
+      for (int b0 = 0; b0 < B; b0 += 256) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int bb = b0 + 64 * u + lane;
+          const int len = bb < B ? lens[bb] : 0;
+          int f, q;
+          if (balanced) {
+            const int steps = (len + 31) >> 5;
+            f = bb < B && steps > 0 ? a.n_kv_heads * (steps + a.unit_cost) : 0;
+            q = 0;
+          } else {
+            f = bb < B ? len / C : 0;
+            q = bb < B && len % C != 0 ? 1 : 0;
+          }
+          int sf = f, sq = q;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const int tf = __shfl_up(sf, o, 64), tq = __shfl_up(sq, o, 64);
+            if (lane >= o) {
+              sf += tf;
+              sq += tq;
+            }
+          }
+          if (bb < B) {
+            fpre[bb] = carry_f + sf - f;
+            qpre[bb] = carry_q + sq - q;
+          }
+          carry_f += __shfl(sf, 63, 64);
+          carry_q += __shfl(sq, 63, 64);
+        }
+      }
+      if (lane == 0) {
+        fpre[B] = carry_f;
+        qpre[B] = carry_q;
+      }
+    }
+  }  // wave 0
   __syncthreads();
+  // this wave's rank among the split waves, numbered across the workgroups
+  // first: when only the first ranks find work, they still sit in different
+  // workgroups, spread over every compute unit
+  const int vb = wave * a.split_blocks + (int)blockIdx.x;
+  if (vb >= a.split_waves) return;  // ranks past the last (a short launch's spare waves)
   if constexpr (BAL) {
-    if (balanced) {
-      run_pieces<FMT, D, BS, true>(a, fpre, qpre, lens);
+    if (__builtin_amdgcn_readfirstlane(*sched) != 0) {
+      run_pieces<FMT, D, BS, true>(a, fpre, qpre, lens, vb);
       return;
     }
   }
-  run_pieces<FMT, D, BS, false>(a, fpre, qpre, lens);
+  run_pieces<FMT, D, BS, false>(a, fpre, qpre, lens, vb);
 }
 
-// Persistent launch: as many workgroups as the chip holds at once for this
+// Persistent launch: as many waves as the chip holds at once for this
 // kernel (occupancy x compute units), capped by the number of work items
 // the host can bound (every sequence at max_len).
-template <typename K>
-int resident_workgroups(K kernel, size_t lds) {
+int compute_units() {
   static thread_local int cus = 0;
   if (!cus) {
     int dev = 0;
@@ -714,33 +737,53 @@ int resident_workgroups(K kernel, size_t lds) {
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
   }
+  return cus;
+}
+
+template <typename K>
+int resident_waves(K kernel, size_t lds) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64, lds) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * kGroupWaves, lds) !=
+          hipSuccess ||
       per_cu < 1)
     per_cu = 1;
-  return per_cu * cus;
+  return per_cu * kGroupWaves * compute_units();
+}
+
+// Waves per workgroup for a launch of `waves` waves: the widest of 4, 2, 1
+// that still gives every compute unit a workgroup.
+inline int group_width(int64_t waves) {
+  const int64_t cus = compute_units();
+  return waves >= 4 * cus ? 4 : waves >= 2 * cus ? 2 : 1;
 }
 
 template <int FMT, int D, int BS, bool BAL, bool PRE>
 hipError_t launch_sched(const AttendArgs& a, const Launch& l) {
   auto kernel = attend_mfma_kernel<FMT, D, BS, BAL, PRE>;
-  const size_t lds = (size_t)(3 * a.batch + 2) * sizeof(int32_t);
+  const size_t lds = (size_t)(3 * a.batch + 3) * sizeof(int32_t);
   const int64_t bound = BAL ? a.bal_waves : (int64_t)a.n_kv_heads * a.batch * a.n_split;
-  const int64_t resident = resident_workgroups(kernel, lds);
+  const int64_t resident = resident_waves(kernel, lds);
+  AttendArgs b = a;
   if (a.prefix_len <= 0) {
-    const int64_t grid = std::min<int64_t>(bound, resident);
-    return launch1(kernel, dim3((unsigned)std::max<int64_t>(grid, 1)), dim3(64), lds, l, a);
+    const int64_t waves = std::max<int64_t>(1, std::min<int64_t>(bound, resident));
+    const int gw = group_width(waves);
+    b.split_waves = (int32_t)waves;
+    b.split_blocks = (int32_t)((waves + gw - 1) / gw);
+    return launch1(kernel, dim3((unsigned)b.split_blocks), dim3(64 * gw), lds, l, b);
   }
-  // shared-prefix mode: split workgroups first, then the prefix waves, all
-  // resident together when they fit (the split grid leaves room for them)
+  // shared-prefix mode: split workgroups first, then workgroups of prefix
+  // waves, all resident together when they fit (the split pass leaves room)
   const int64_t pre = prefix_col_blocks<prefix_tiles<D>()>(a.batch, a.group) * a.n_kv_heads *
                       a.n_pchunks;
   int64_t split = a.split_wanted ? std::min<int64_t>(bound, resident) : 0;
-  if (split > 0) split = std::max<int64_t>(1, std::min(split, std::max(resident - pre, resident / 2)));
-  if (split + pre > 0x7fffffff) return hipErrorInvalidValue;
-  AttendArgs b = a;
-  b.split_blocks = (int32_t)split;
-  return launch1(kernel, dim3((unsigned)(split + pre)), dim3(64), lds, l, b);
+  if (split > 0)
+    split = std::max<int64_t>(1, std::min(split, std::max(resident - pre, resident / 2)));
+  const int gw = group_width(split + pre);
+  const int64_t split_groups = (split + gw - 1) / gw, groups = split_groups + (pre + gw - 1) / gw;
+  if (groups > 0x7fffffff || split > 0x7fffffff) return hipErrorInvalidValue;
+  b.split_waves = (int32_t)split;
+  b.split_blocks = (int32_t)split_groups;
+  return launch1(kernel, dim3((unsigned)groups), dim3(64 * gw), lds, l, b);
 }
 
 template <int FMT, int D, int BS>

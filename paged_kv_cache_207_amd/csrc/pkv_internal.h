@@ -96,6 +96,9 @@ struct AttendArgs {
   // rows), then the prefix pass's waves
   int32_t split_blocks = 0;
   int32_t split_wanted = 1;
+  // waves of the split pass (each takes its own items; a launch's workgroups
+  // hold several, set by the launcher)
+  int32_t split_waves = 0;
   // shared-prefix mode: table updates for the next step (upd_table[b *
   // table_stride + block] = page for each (b, block, page) row), each for an
   // entry this launch does not read

@@ -104,7 +104,7 @@ template <int FMT, int D, int BS, int TT, bool RAW>
 __device__ __forceinline__ void prefix_wave(const AttendArgs& a, int wid) {
   using S = Step<FMT, D>;
   constexpr int NC = S::NC, ND = S::ND;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;
   const int G = a.group;
   const int nb = (int)prefix_col_blocks<TT>(a.batch, G);

@@ -459,11 +459,12 @@ def run_shared_prefix(args, device, cpu_seconds: float = 0.0):
             graphs.append(g)
     torch.cuda.synchronize()
 
+    g_upd_np = [u.numpy() for u in g_upd_host]  # views of the pinned lists
+
     def graph_job(seqs):
         def fill(s):
             seqs.append_all(ones)
-            n = seqs.take_updates(g_upd_host[s]).shape[0]
-            g_upd_host[s][n:].fill_(-1)
+            seqs.take_updates_padded(g_upd_np[s])
         fill(0)
         pkv.table_apply(table, g_upd_host[0])
         for s in range(sp.n_steps):

@@ -1028,8 +1028,15 @@ int plan_growth(const pkv_seqs* s, const int32_t* n, std::vector<char>& copy, in
                   (long long)need, s->stride);
     if (s->npages[b] > 0 && n[b] > 0 && s->lens[b] % s->page_size) {
       const int32_t last = s->last_page(b);
+      // a page held once never needs a copy (simulated counts only fall),
+      // so only shared pages go through the map
+      const int32_t held = pkv_pool_refcount(s->pool, last);
+      if (held <= 1) {
+        total += s->new_pages(b, n[b]);
+        continue;
+      }
       auto it = refs.find(last);
-      if (it == refs.end()) it = refs.emplace(last, pkv_pool_refcount(s->pool, last)).first;
+      if (it == refs.end()) it = refs.emplace(last, held).first;
       if (s->needs_copy(b, n[b], it->second)) {
         copy[b] = 1;
         --it->second;

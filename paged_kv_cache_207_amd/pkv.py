@@ -617,6 +617,20 @@ class SeqTables:
         p = lib().pkv_seqs_lens(self._h)
         return [p[b] for b in range(self.batch)]
 
+    def take_updates_padded(self, out: np.ndarray) -> int:
+        """Move queued update triples into the rows of ``out`` (a C-contiguous
+        int32 [cap, 3] array, such as the numpy view of a pinned tensor) and
+        set the rows after them to -1, which a device update skips; returns
+        the number moved.  For a step loop that hands the device a list of
+        fixed size."""
+        if out.dtype != np.int32 or out.ndim != 2 or out.shape[1] != 3 or not out.flags.c_contiguous:
+            raise ValueError("out must be a C-contiguous int32 array [cap, 3]")
+        n = lib().pkv_seqs_take_updates(self._h, out.ctypes.data_as(_PI32), out.shape[0])
+        if n < 0:
+            _check(n)
+        out[n:] = -1
+        return n
+
     def take_updates(self, out: torch.Tensor | None = None, cap: int = 1 << 20):
         """Move queued update triples into a host int32 tensor [n, 3] (pinned if
         ``out`` is pinned); returns the filled view."""

@@ -8,6 +8,7 @@ import os
 import random
 import re
 
+import numpy as np
 import pytest
 
 from oracle import PoolModel, PoolError
@@ -140,6 +141,17 @@ def test_seqs_growth_share_release_and_updates():
             s.append(b, 1)
     assert before - pool.num_free() == grew
     assert s.take_updates().shape[0] == grew
+    # the padded form: the same triples, then rows of -1 up to the capacity
+    for b in range(B):
+        s.append(b, bs)
+    buf = np.full((3 * B + 5, 3), 7, dtype=np.int32)
+    n = s.take_updates_padded(buf)
+    assert n == B and (buf[n:] == -1).all()
+    tab = s.table()
+    assert all(tab[b][j] == page for b, j, page in buf[:n].tolist())
+    assert s.take_updates_padded(buf) == 0 and (buf == -1).all()
+    with pytest.raises(ValueError):
+        s.take_updates_padded(np.zeros((4, 2), np.int32))
     # release: shared pages survive until the last reader lets go
     for b in range(B):
         s.release(b)

@@ -670,45 +670,52 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void attend_mfma_kernel(Attend
       if (blockIdx.x == 0 && lane == 0) *a.ws_sched = balanced ? 1 : 0;
     }
     if (lane == 0) *sched = balanced ? 1 : 0;
-    // exclusive prefix sums of the schedule's counts, from the LDS lengths
-    // (each lane reads back the entries it wrote)
-    {
-      int carry_f = 0, carry_q = 0;
-      for (int b0 = 0; b0 < B; b0 += 256) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int bb = b0 + 64 * u + lane;
-          const int len = bb < B ? lens[bb] : 0;
-          int f, q;
-          if (balanced) {
-            const int steps = (len + 31) >> 5;
-            f = bb < B && steps > 0 ? a.n_kv_heads * (steps + a.unit_cost) : 0;
-            q = 0;
-          } else {
-            f = bb < B ? len / C : 0;
-            q = bb < B && len % C != 0 ? 1 : 0;
-          }
-          int sf = f, sq = q;
-#pragma unroll
-          for (int o = 1; o < 64; o <<= 1) {
-            const int tf = __shfl_up(sf, o, 64), tq = __shfl_up(sq, o, 64);
-            if (lane >= o) {
-              sf += tf;
-              sq += tq;
-            }
-          }
-          if (bb < B) {
-            fpre[bb] = carry_f + sf - f;
-            qpre[bb] = carry_q + sq - q;
-          }
-          carry_f += __shfl(sf, 63, 64);
-          carry_q += __shfl(sq, 63, 64);
-        }
+    // exclusive prefix sums of the schedule's counts: lane l sums its run of
+    // E = ceil(B / 64) consecutive sequences from the LDS lengths, one wave
+    // scan gives the runs' offsets, then each lane writes its run.  (One
+    // scan per 64 sequences, each a chain of lane shuffles, took 1.5-1.9 us
+    // of the launch's start.)
+    __builtin_amdgcn_wave_barrier();  // the lengths above, written by other lanes
+    auto counts = [&](int len, int& f, int& q) {
+      if (balanced) {
+        const int steps = (len + 31) >> 5;
+        f = steps > 0 ? a.n_kv_heads * (steps + a.unit_cost) : 0;
+        q = 0;
+      } else {
+        f = len / C;
+        q = len % C != 0 ? 1 : 0;
       }
-      if (lane == 0) {
-        fpre[B] = carry_f;
-        qpre[B] = carry_q;
+    };
+    const int E = (B + 63) >> 6;
+    const int s0 = min(lane * E, B), s1 = min(s0 + E, B);
+    int tf = 0, tq = 0;
+    for (int bb = s0; bb < s1; ++bb) {
+      int f, q;
+      counts(lens[bb], f, q);
+      tf += f;
+      tq += q;
+    }
+    int sf = tf, sq = tq;  // inclusive scan over the lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int uf = __shfl_up(sf, o, 64), uq = __shfl_up(sq, o, 64);
+      if (lane >= o) {
+        sf += uf;
+        sq += uq;
       }
+    }
+    int cf = sf - tf, cq = sq - tq;
+    for (int bb = s0; bb < s1; ++bb) {
+      int f, q;
+      counts(lens[bb], f, q);
+      fpre[bb] = cf;
+      qpre[bb] = cq;
+      cf += f;
+      cq += q;
+    }
+    if (lane == 63) {
+      fpre[B] = sf;
+      qpre[B] = sq;
     }
   }  // wave 0
   __syncthreads();

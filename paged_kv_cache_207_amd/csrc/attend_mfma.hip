@@ -661,12 +661,13 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void attend_mfma_kernel(Attend
     }
     bool balanced = false;
     if constexpr (BAL) {
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        lmin = min(lmin, __shfl_xor(lmin, o, 64));
-        lmax = max(lmax, __shfl_xor(lmax, o, 64));
+      // uneven lengths: some lane's non-empty ones differ from the first
+      // non-empty lane's (two ballots and a lane read, no shuffles)
+      const uint64_t busy = __builtin_amdgcn_ballot_w64(lmax > 0);
+      if (busy) {
+        const int l0 = __builtin_amdgcn_readlane(lmax, (int)__builtin_ctzll(busy));
+        balanced = __builtin_amdgcn_ballot_w64(lmax > 0 && (lmin != l0 || lmax != l0)) != 0;
       }
-      balanced = __builtin_amdgcn_readfirstlane(lmin < lmax ? 1 : 0) != 0;
       if (blockIdx.x == 0 && lane == 0) *a.ws_sched = balanced ? 1 : 0;
     }
     if (lane == 0) *sched = balanced ? 1 : 0;

@@ -558,16 +558,8 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
 
 template <int FMT, int D, int BS, bool BAL, bool PRE>
 __global__ __launch_bounds__(64 * kGroupWaves, 2) void attend_mfma_kernel(AttendArgs a) {
-  using S = Step<FMT, D>;
-  using KT = typename S::KT;
-  constexpr int NC = S::NC, ND = S::ND;
-  constexpr int ESZ = FMT == PKV_FMT_BF16 ? 2 : 1;
-  constexpr int KPL = S::KPL;
-  auto kdim = [](int c, int jj) { return kdim_of<FMT>(c, jj); };
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const int n = lane & 15;  // head column (B/C operands), row (A operands)
-  const int j = lane >> 4;  // k group (A/B operands), row quad (C operand)
   const int G = a.group;
   const int bs = BS ? BS : a.page_size;
   const int C = a.split_tokens;

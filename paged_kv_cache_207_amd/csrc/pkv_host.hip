@@ -199,7 +199,7 @@ struct Timer {
     if (hipEventCreate(&l.e0) != hipSuccess) {
       l.e0 = nullptr;
     } else if (hipEventCreate(&l.e1) != hipSuccess) {
-      hipEventDestroy(l.e0);
+      (void)hipEventDestroy(l.e0);
       l.e0 = l.e1 = nullptr;
     }
   }
@@ -209,8 +209,8 @@ struct Timer {
     if (e == hipSuccess && l.used) {
       c->events[kind].emplace_back(l.e0, l.e1);
     } else {
-      hipEventDestroy(l.e0);
-      hipEventDestroy(l.e1);
+      (void)hipEventDestroy(l.e0);
+      (void)hipEventDestroy(l.e1);
     }
     l.e0 = l.e1 = nullptr;
   }
@@ -239,8 +239,8 @@ int pkv_timing_read(pkv_cache* c, double* ms, int32_t* counts) {
           hipEventElapsedTime(&t, e.first, e.second) != hipSuccess)
         rc = fail(PKV_EHIP, "event query failed");
       sum += t;
-      hipEventDestroy(e.first);
-      hipEventDestroy(e.second);
+      (void)hipEventDestroy(e.first);
+      (void)hipEventDestroy(e.second);
     }
     ms[k] = sum;
     counts[k] = (int32_t)c->events[k].size();
@@ -304,8 +304,8 @@ void pkv_cache_destroy(pkv_cache* c) {
   if (!c) return;
   for (auto& v : c->events)
     for (auto& e : v) {
-      hipEventDestroy(e.first);
-      hipEventDestroy(e.second);
+      (void)hipEventDestroy(e.first);
+      (void)hipEventDestroy(e.second);
     }
   delete c;
 }

@@ -73,6 +73,28 @@ def test_full_size_decode(name):
     assert worst <= TOL[w.kv_format]
 
 
+@pytest.mark.parametrize("name", ["decode_bf16", "int8_kv"])
+def test_full_size_vector_path(name):
+    """The vector-ALU path (forced) at full size: the row-tiled kernel, on
+    sampled sequences against the oracle."""
+    require_gpu()
+    w = W.by_name(name)
+    say(f"full-size {name}, vector path: B={w.batch} sum(len)={int(w.lens.sum())}")
+    c = make_cache(w)
+    tdev = dev(w.tables)
+    gpu_write(c, tdev, w.rounds())
+    q = w.query()
+    out = c.attend(q.cuda(), tdev, dev(w.lens), w.max_len, w.scale, flags=pkv.ATTEND_VALU)
+    torch.cuda.synchronize()
+    assert c.status() == 0
+    worst = 0.0
+    for b in samples(w):
+        k, v = w.seq_kv(b)
+        worst = max(worst, check_seq(c, w, tdev, b, out, k, v, q[b]))
+    say(f"  sampled max err {worst:.3e} (tol {TOL[w.kv_format]})")
+    assert worst <= TOL[w.kv_format]
+
+
 def test_full_size_shared_prefix_steps():
     """256 sequences over 64 shared prefix pages; 32 append+attend steps,
     sampled sequences checked at the first, a middle and the last step."""

@@ -586,9 +586,9 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void attend_mfma_kernel(Attend
     }
     if ((int)blockIdx.x >= a.split_blocks) {  // a workgroup of prefix waves only
       constexpr int TT = prefix_tiles<D>();
-      const int wid = ((int)blockIdx.x - a.split_blocks) * (int)(blockDim.x >> 6) + wave;
+      const int wid = ((int)blockIdx.x - a.split_blocks) * a.pre_group_waves + wave;
       const int n_pre = (int)prefix_col_blocks<TT>(B, G) * a.n_kv_heads * a.n_pchunks;
-      if (wid < n_pre) {
+      if (wave < a.pre_group_waves && wid < n_pre) {
         if (a.qk_scale_log2 > 0.f)
           prefix_wave<FMT, D, BS, TT, true>(a, wid);
         else
@@ -778,11 +778,17 @@ hipError_t launch_sched(const AttendArgs& a, const Launch& l) {
   int64_t split = a.split_wanted ? std::min<int64_t>(bound, resident) : 0;
   if (split > 0)
     split = std::max<int64_t>(1, std::min(split, std::max(resident - pre, resident / 2)));
-  const int gw = group_width(split + pre);
-  const int64_t split_groups = (split + gw - 1) / gw, groups = split_groups + (pre + gw - 1) / gw;
+  // The workgroup width follows the split pass's waves; prefix workgroups
+  // use as many of their waves as spreads them over every compute unit (512
+  // prefix waves in 4-wave groups sat on half the units).
+  const int gw = group_width(std::max(split, pre));
+  const int64_t cus = compute_units();
+  const int wp = (int)std::max<int64_t>(1, std::min<int64_t>(gw, pre / cus));
+  const int64_t split_groups = (split + gw - 1) / gw, groups = split_groups + (pre + wp - 1) / wp;
   if (groups > 0x7fffffff || split > 0x7fffffff) return hipErrorInvalidValue;
   b.split_waves = (int32_t)split;
   b.split_blocks = (int32_t)split_groups;
+  b.pre_group_waves = wp;
   return launch1(kernel, dim3((unsigned)groups), dim3(64 * gw), lds, l, b);
 }
 

@@ -99,6 +99,10 @@ struct AttendArgs {
   // waves of the split pass (each takes its own items; a launch's workgroups
   // hold several, set by the launcher)
   int32_t split_waves = 0;
+  // shared-prefix mode: the waves of a prefix workgroup that take work (the
+  // rest exit at once), so that the prefix workgroups spread over every
+  // compute unit
+  int32_t pre_group_waves = 1;
   // shared-prefix mode: table updates for the next step (upd_table[b *
   // table_stride + block] = page for each (b, block, page) row), each for an
   // entry this launch does not read

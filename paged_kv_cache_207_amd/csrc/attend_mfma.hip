@@ -688,15 +688,7 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void attend_mfma_kernel(Attend
       tf += f;
       tq += q;
     }
-    int sf = tf, sq = tq;  // inclusive scan over the lanes
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int uf = __shfl_up(sf, o, 64), uq = __shfl_up(sq, o, 64);
-      if (lane >= o) {
-        sf += uf;
-        sq += uq;
-      }
-    }
+    const int sf = wave_incl_scan(tf), sq = wave_incl_scan(tq);  // inclusive, over the lanes
     int cf = sf - tf, cq = sq - tq;
     for (int bb = s0; bb < s1; ++bb) {
       int f, q;

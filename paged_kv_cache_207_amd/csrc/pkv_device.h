@@ -120,6 +120,24 @@ __device__ __forceinline__ float wave_sum(float x) {
   return rows_sum(x);
 }
 
+// Inclusive prefix sum over the wave's 64 lanes, without LDS: DPP row
+// shifts by 1, 2, 4 and 8 inside each 16-lane row (lanes shifted in from
+// outside the row read 0), then lane 15's sum added into rows 1 and 3 and
+// lane 31's into rows 2 and 3 (row broadcasts).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_add(int x) {
+  return x + __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xf, true);
+}
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x = dpp_add<0x111, 0xf>(x);
+  x = dpp_add<0x112, 0xf>(x);
+  x = dpp_add<0x114, 0xf>(x);
+  x = dpp_add<0x118, 0xf>(x);
+  x = dpp_add<0x142, 0xa>(x);
+  x = dpp_add<0x143, 0xc>(x);
+  return x;
+}
+
 __device__ __forceinline__ void report(int32_t* status, uint32_t bit) {
   if (status) atomicOr(reinterpret_cast<unsigned int*>(status), bit);
 }

@@ -170,14 +170,17 @@ def test_balanced_decode_step_matches_write_then_attend():
     assert torch.equal(pages[0][0], pages[1][0]) and torch.equal(pages[0][1], pages[1][1])
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "int8"])
-def test_many_sequences_scan_blocks(fmt):
-    """700 short sequences, some empty: the kernel's length scan runs over
-    LDS in blocks of 256 sequences with a carry between blocks, for the
-    balanced schedule (bf16) and fixed splits (int8)."""
+@pytest.mark.parametrize("fmt,n_seq", [("bf16", 700), ("int8", 700), ("bf16", 65),
+                                       ("int8", 65), ("bf16", 4096), ("int8", 4096)])
+def test_many_sequences_scan_blocks(fmt, n_seq):
+    """Many short sequences, some empty, for the balanced schedule (bf16)
+    and fixed splits (int8).  The schedule's prefix sums give each of the 64
+    lanes a run of ceil(n / 64) consecutive sequences: 700 leaves the last
+    lane a shorter run, 65 one lane a run of 1 and the rest none, and 4096
+    (the most a call takes) fills every lane with 64."""
     require_gpu()
-    rng = np.random.default_rng(700)
-    lens = rng.integers(0, 90, size=700).astype(np.int32)
+    rng = np.random.default_rng(700 + n_seq)
+    lens = rng.integers(0, 90 if n_seq < 4096 else 40, size=n_seq).astype(np.int32)
     lens[::37] = 0
     lens[5] = 400
     bs = 16
@@ -196,7 +199,7 @@ def test_many_sequences_scan_blocks(fmt):
     ref = attend(o, 0, np_bits(q), dtype_name(q), w.tables, w.lens, w.scale)
     out = c.attend(q.cuda(), tdev, dev(w.lens), w.max_len, w.scale)
     e = max_err(out, ref)
-    say(f"700 sequences ({fmt}): max err {e:.3e}")
+    say(f"{n_seq} sequences ({fmt}): max err {e:.3e}")
     assert e <= TOL[fmt]
     assert not out[np.flatnonzero(w.lens == 0)].float().abs().any()
     assert c.status() == 0

@@ -327,7 +327,19 @@ __global__ __launch_bounds__(64, 2) void attend_rows_kernel(AttendArgs a) {
   const int len = clamp_len(a.lens[b], a.max_len, s == 0 && blockIdx.y == 0 ? a.status : nullptr,
                             PKV_DEV_LEN);
   const int t_begin = s * a.split_tokens;
-  if (t_begin >= len) return;
+  // one output element of head h0 + hh, dim d (direct writes)
+  auto put_out = [&](int hh, int d, float v) {
+    const int64_t oi = ((int64_t)b * a.n_q_heads + h0 + hh) * D + d;
+    if (a.q_bf16) static_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16_bits(v);
+    else static_cast<float*>(a.out)[oi] = v;
+  };
+  if (t_begin >= len) {
+    if (a.direct_out) {  // an empty sequence's output is zero
+      for (int hh = 0; hh < gc; ++hh)
+        for (int d = lane; d < D; d += 64) put_out(hh, d, 0.f);
+    }
+    return;
+  }
   const int t_end = min(t_begin + a.split_tokens, len);
 
   // the query group's dims n DQ .. + DQ - 1, in log2 units (zeros past gc)
@@ -477,6 +489,17 @@ __global__ __launch_bounds__(64, 2) void attend_rows_kernel(AttendArgs a) {
 #pragma unroll
     for (int i = 0; i < DQ; ++i) o[hh][i] = rows_sum(o[hh][i]);
   }
+  if (a.direct_out) {  // the only split: normalise and write the outputs
+#pragma unroll
+    for (int hh = 0; hh < KH; ++hh) {
+      if (hh < gc && j == 0) {
+        const float inv = 1.f / l[hh];
+#pragma unroll
+        for (int i = 0; i < DQ; ++i) put_out(hh, n + 16 * i, o[hh][i] * inv);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int hh = 0; hh < KH; ++hh) {
     if (hh < gc) {
@@ -508,12 +531,14 @@ hipError_t launch_rows(const AttendArgs& a, const Launch& l) {
   }
 }
 
-bool rows_supported(const AttendArgs& a) {
-  const int d = a.head_dim;
-  return a.page_size % 8 == 0 && (d == 32 || d == 64 || d == 96 || d == 128 || d == 256);
-}
+bool rows_supported(const AttendArgs& a) { return valu_rows_supported(a.page_size, a.head_dim); }
 
 }  // namespace
+
+bool valu_rows_supported(int page_size, int head_dim) {
+  const int d = head_dim;
+  return page_size % 8 == 0 && (d == 32 || d == 64 || d == 96 || d == 128 || d == 256);
+}
 
 hipError_t launch_attend_valu(const AttendArgs& a, int fmt, const Launch& l) {
   if (rows_supported(a)) {

@@ -544,6 +544,10 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
   // either.
   a.fuse_combine = mfma && (flags & PKV_ATTEND_COMBINE_FUSED) != 0;
   a.single_done = mfma && max_len > 0 && !pre;
+  // The vector path with every sequence in one split writes the outputs
+  // itself (the row-tiled kernel): no combine launch.
+  a.direct_out = !mfma && !pre && max_len > 0 && n_split == 1 &&
+                 pkv::valu_rows_supported(a.page_size, a.head_dim);
   // The balanced schedule where the library plans the work (split_tokens 0)
   // on the matrix-core path for the page formats it pays off on, unless the
   // in-kernel combine is asked for (it counts fixed splits); its flat slot
@@ -564,7 +568,7 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
              : pkv::launch_attend_valu(a, c->L.format, tm.l);
     tm.stop(e);
     if (e != hipSuccess) return fail(PKV_EHIP, "attend launch failed: %s", hipGetErrorString(e));
-    if (a.fuse_combine) return PKV_OK;  // the split pass combined the splits itself
+    if (a.fuse_combine || a.direct_out) return PKV_OK;  // the split pass wrote the outputs
   }
   Timer tm(c, PKV_T_ATTEND_COMBINE, s, timed);
   e = pkv::launch_reduce(a, tm.l);

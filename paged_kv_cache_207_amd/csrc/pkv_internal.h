@@ -76,6 +76,8 @@ struct AttendArgs {
   int32_t q_bf16;  // 1: q and out are bf16, 0: float32
   int32_t fuse_combine;  // matrix-core path: 1 = combine in the split pass, 0 = combine kernel
   int32_t single_done;   // combine kernel: single-split sequences are already written
+  int32_t direct_out = 0;  // vector path, one split: the split pass writes every output
+                           // (zeros for an empty sequence) and no combine runs
   // Shared-prefix mode (prefix_len > 0): the first prefix_len tokens of every
   // sequence sit in the pages prefix_pages lists (the same physical pages in
   // every table row).  The prefix pass attends over them for all sequences at
@@ -186,6 +188,9 @@ inline hipError_t launch1(K kernel, dim3 grid, dim3 block, size_t shm, const Lau
 hipError_t launch_write(const WriteArgs& a, int fmt, int in_dtype, const Launch& l);
 hipError_t launch_gather(const GatherArgs& a, int fmt, const Launch& l);
 hipError_t launch_attend_valu(const AttendArgs& a, int fmt, const Launch& l);
+// Whether the vector path takes the row-tiled kernel for this page size and
+// head dim (the one that can write outputs directly).
+bool valu_rows_supported(int page_size, int head_dim);
 // Returns hipErrorNotSupported when the shape has no matrix-core variant.  In
 // shared-prefix mode (prefix_len > 0) the launch also runs the prefix pass.
 hipError_t launch_attend_mfma(const AttendArgs& a, int fmt, const Launch& l);

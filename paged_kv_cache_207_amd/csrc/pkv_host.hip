@@ -569,6 +569,9 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
     tm.stop(e);
     if (e != hipSuccess) return fail(PKV_EHIP, "attend launch failed: %s", hipGetErrorString(e));
     if (a.fuse_combine || a.direct_out) return PKV_OK;  // the split pass wrote the outputs
+    // fixed splits on the matrix cores with every sequence in one split: the
+    // split pass wrote each output directly (zeros for an empty sequence)
+    if (mfma && a.bal_waves == 0 && n_split == 1 && a.single_done) return PKV_OK;
   }
   Timer tm(c, PKV_T_ATTEND_COMBINE, s, timed);
   e = pkv::launch_reduce(a, tm.l);

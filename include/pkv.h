@@ -216,9 +216,11 @@ int pkv_attend_workspace_size(const pkv_cache* cache, int32_t batch, int32_t n_q
  *   flags      0, or PKV_ATTEND_VALU, and/or one of PKV_ATTEND_COMBINE_KERNEL
  *              / PKV_ATTEND_COMBINE_FUSED.
  * The matrix-core kernel serves bf16/int8 pages with a bf16 query, head_dim
- * 64 or 128, page_size 16 or a multiple of 32, up to 16 query heads per KV
- * head, at most 64 KV heads and batch <= 4096; every other shape runs on the
- * vector-ALU kernel.
+ * 64 or 128, page_size 16 or a multiple of 32, batch <= 4096, and G =
+ * n_q_heads / n_kv_heads query heads per KV head either up to 16 or with a
+ * divisor g in [8, 16] (the largest is taken: each KV head then counts as
+ * G / g groups of g heads), with at most 64 such groups; every other shape
+ * runs on the vector-ALU kernels.
  * A split size gives at most 16384 splits per sequence (EINVAL otherwise). */
 int pkv_paged_attend(pkv_cache* cache, int32_t layer, const void* q, int32_t q_dtype,
                      int32_t n_q_heads, const int32_t* table, int32_t table_stride,

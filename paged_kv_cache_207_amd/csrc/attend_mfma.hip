@@ -229,9 +229,12 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
                          ((int64_t)b * a.n_q_heads + (int64_t)g * G + n) * D,
                  n < G, j);
 
+  // the pages' KV head: with more than 16 query heads per KV head, each
+  // KV head stands as kv_rep groups of `group` query heads (g counts those)
+  const int gp = g / a.kv_rep, hkv = a.n_kv_heads / a.kv_rep;
   const int64_t slab_bytes = (int64_t)bs * D * ESZ;
   const PageSrc src{static_cast<const char*>(a.k_pages), static_cast<const char*>(a.v_pages),
-                    a.k_scales, a.v_scales, a.layer_page0, slab_bytes, a.n_kv_heads, bs};
+                    a.k_scales, a.v_scales, a.layer_page0, slab_bytes, hkv, bs};
   const int32_t* trow = a.table + (int64_t)b * a.table_stride;
   const int pg_last = (t_end - 1) / bs;
 
@@ -252,7 +255,7 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
   };
   auto fetch_new = [&](NewRow& nr) {
     nr.ok = a.lens[b] - a.prefix_len == len;
-    const int64_t row = ((int64_t)b * a.n_kv_heads + g) * D;
+    const int64_t row = ((int64_t)b * hkv + gp) * D;
     const uint16_t* kr = static_cast<const uint16_t*>(a.k_new) + row;
     const uint16_t* vr = static_cast<const uint16_t*>(a.v_new) + row;
 #pragma unroll
@@ -294,7 +297,7 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
       const int page_a = ts < w_end ? __builtin_amdgcn_readlane(vpage, lp - pg0) : -1;
       int page_b = page_a;
       if (BS == 16) page_b = ts + 16 < w_end ? __builtin_amdgcn_readlane(vpage, lp + 1 - pg0) : -1;
-      load_step<FMT, D, BS>(r, src, page_a, page_b, ts - lp * bs, g, lane);
+      load_step<FMT, D, BS>(r, src, page_a, page_b, ts - lp * bs, gp, lane);
     };
 
     auto compute_step = [&](int ts, S& r) {
@@ -417,11 +420,13 @@ __device__ __forceinline__ void run_pieces(const AttendArgs& a, const int32_t* f
       // the page write
       const int jp = t_new / bs;
       const int page = nr.page;
-      if (page < 0 || page >= a.n_pages) {
+      if (g % a.kv_rep != 0) {
+        // the KV head's row is written by its first group's piece
+      } else if (page < 0 || page >= a.n_pages) {
         report(a.status, PKV_DEV_WRITE_PAGE);
       } else {
         const int slot = t_new - jp * bs;
-        const int64_t slab = (a.layer_page0 + page) * a.n_kv_heads + g;
+        const int64_t slab = (a.layer_page0 + page) * hkv + gp;
         char* kw = static_cast<char*>(const_cast<void*>(a.k_pages)) + slab * slab_bytes;
         char* vw = static_cast<char*>(const_cast<void*>(a.v_pages)) + slab * slab_bytes;
         if (n == 0) {  // lanes j = 0..3 of one row hold the whole K row

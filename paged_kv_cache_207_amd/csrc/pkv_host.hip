@@ -114,6 +114,17 @@ constexpr int kUnitCost = 3;
 constexpr int kPrefixChunkTarget = 512;
 constexpr int kPrefixChunkMax = 1024;
 
+// Query heads per matrix-core group: G itself up to 16; above, the largest
+// divisor of G that is at most 16 (each KV head then stands as G / that
+// many groups), or 0 when that divisor is below 8 (the vector path takes
+// the call).
+int mfma_group(int G) {
+  if (G <= 16) return G;
+  for (int d = 16; d >= 8; --d)
+    if (G % d == 0) return d;
+  return 0;
+}
+
 struct WsLayout {
   uint64_t o_off, ml_off, sched_off, desc_off, total;
   uint64_t pre_o_off = 0, pre_ml_off = 0;  // shared-prefix partials (after the rest)
@@ -133,7 +144,11 @@ WsLayout ws_layout(const pkv_cache* c, int batch, int n_q_heads, int n_split) {
   w.ml_off = (w.o_off + rows * head_dim * sizeof(float) + 255) / 256 * 256;
   w.sched_off = (w.ml_off + rows * 2 * sizeof(float) + 255) / 256 * 256;
   w.desc_off = w.sched_off + 256;
-  w.total = w.desc_off + (uint64_t)batch * n_kv_heads * 2 * sizeof(int32_t);
+  // one record per (sequence, group of query heads): more groups than KV
+  // heads when a KV head stands as several
+  const int G = n_q_heads / std::max(n_kv_heads, 1), gv = mfma_group(G);
+  const uint64_t groups = (uint64_t)n_kv_heads * (gv > 0 ? G / gv : 1);
+  w.total = w.desc_off + (uint64_t)batch * groups * 2 * sizeof(int32_t);
   return w;
 }
 
@@ -502,9 +517,18 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  const bool mfma = !(flags & PKV_ATTEND_VALU) &&
-                    pkv::mfma_supported(c->L.format, a.q_bf16, a.head_dim, a.page_size, a.group,
-                                        batch, c->L.n_kv_heads);
+  // More than 16 query heads per KV head: the matrix-core kernel takes each
+  // KV head as kv_rep groups of gv query heads (its n_kv_heads and group
+  // count those groups; the pages keep the KV heads).
+  const int gv = mfma_group(a.group), rep = gv > 0 ? a.group / gv : 1;
+  const bool mfma = !(flags & PKV_ATTEND_VALU) && gv > 0 &&
+                    pkv::mfma_supported(c->L.format, a.q_bf16, a.head_dim, a.page_size, gv,
+                                        batch, c->L.n_kv_heads * rep);
+  if (mfma && rep > 1) {
+    a.group = gv;
+    a.n_kv_heads = c->L.n_kv_heads * rep;
+    a.kv_rep = rep;
+  }
   a.k_new = a.v_new = nullptr;
   if (k_new) {
     if (mfma && (sfx_max > 0 || pre) && in_dtype == PKV_DT_BF16) {
@@ -555,7 +579,7 @@ int attend_impl(pkv_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
   // record its choice, and the combine writes the zero outputs itself.
   const int wpc = bal_waves_per_cu(c->L.format);
   if (mfma && wpc > 0 && sfx_max > 0 && !a.fuse_combine && split_tokens == 0 &&
-      (int64_t)batch * c->L.n_kv_heads * ((sfx_max + 31) / 32 + kUnitCost) < (int64_t)INT32_MAX) {
+      (int64_t)batch * a.n_kv_heads * ((sfx_max + 31) / 32 + kUnitCost) < (int64_t)INT32_MAX) {
     a.bal_waves = wpc * device_cus();
   }
   // With a shared prefix the split pass's launch also runs the prefix pass

@@ -76,6 +76,10 @@ struct AttendArgs {
   int32_t q_bf16;  // 1: q and out are bf16, 0: float32
   int32_t fuse_combine;  // matrix-core path: 1 = combine in the split pass, 0 = combine kernel
   int32_t single_done;   // combine kernel: single-split sequences are already written
+  // matrix-core path: n_kv_heads / kv_rep KV heads hold the pages, each seen
+  // as kv_rep groups of `group` query heads (more than 16 query heads per KV
+  // head); n_kv_heads and group count those groups
+  int32_t kv_rep = 1;
   int32_t direct_out = 0;  // vector path, one split: the split pass writes every output
                            // (zeros for an empty sequence) and no combine runs
   // Shared-prefix mode (prefix_len > 0): the first prefix_len tokens of every

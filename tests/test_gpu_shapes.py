@@ -3,8 +3,8 @@
 The ABI accepts any head_dim that is a multiple of 16 up to 256, any page
 size and any number of query heads per KV head; the matrix-core kernels take
 head_dim 64/128, pages of 16 tokens or a multiple of 32 and groups of at
-most 16, and everything else runs on the vector-ALU kernel and the split-K
-combine.  Each case here writes its sequences in several rounds from
+most 16 (or larger ones with a divisor in [8, 16]), and everything else runs
+on the vector-ALU kernels and the split-K combine.  Each case here writes its sequences in several rounds from
 unaligned start positions (checked bit for bit on the whole sentinel-filled
 pool), attends with the planned split, the smallest split and the combine
 kernel (checked against the oracle at the stated tolerances), runs a decode

@@ -12,10 +12,12 @@
 // nothing and gives zeros.
 //
 // How, on gfx950.  A workgroup of 8 waves (one per compute unit) owns one
-// (sequence, KV head) and 16 * n_pos consecutive positions of its chunk;
-// each wave holds two tiles of 16 matrix-core columns, each tile n_pos =
-// 16 / G positions times the G heads (mfma_step.h gives the tile layouts),
-// every column with its own causal bound, running maximum and sum.  Both
+// (sequence, KV head) and 16 * n_pos positions of its chunk; each wave holds
+// two tiles of 16 matrix-core columns, each tile n_pos = 16 / G consecutive
+// positions times the G heads (mfma_step.h gives the tile layouts), every
+// column with its own causal bound, running maximum and sum.  The waves'
+// runs of 2 n_pos positions are dealt to the sequence's workgroups in turn,
+// so that each workgroup reads about as many tokens as the others.  Both
 // tiles use the same K/V operand registers, so each LDS read feeds two
 // matrix-core operations.  The workgroup walks the tokens up to its last
 // position in blocks of four 32-token steps: all 512 threads load the next
@@ -31,13 +33,14 @@
 // running maximum grew.
 //
 // LDS holds K as [32 tokens][head_dim] (tokens in score-tile order, see
-// k_row), rows padded by 32 bytes, and V as [head_dim][32 tokens], bf16, with
-// the four 16-byte token chunks of a row permuted (v_chunk), so the rows one
-// read instruction touches fall on different banks.  Measured on gfx950 for
-// 16-byte reads: rows padded by 16 bytes (or 48, 64) conflict 2-way, by 32
-// bytes not at all; unpadded V rows with the chunk index XOR-ed with bits 1-2
-// of the row do not conflict either (V padded by 32 bytes would not fit the
-// eight step buffers in LDS).
+// k_row) and V as [head_dim][32 tokens], bf16, unpadded, with the 16-byte
+// chunks of a row permuted by bits of the row (k_pos, v_chunk), so the rows
+// one read instruction touches fall on different banks.  bf16 pages are
+// copied into LDS by the memory unit itself (global_load_lds, 16 bytes a
+// lane): no registers hold the next block and no LDS stores are issued, so
+// the waves' instruction streams carry only the address arithmetic; each
+// wave's 64 chunks of a load land side by side, which the unpadded layout
+// allows.  Dead slots of a partial step are zeroed after the copy lands.
 //
 // Launch order is XCD-aware: workgroups are handed to the 8 XCDs in turn, so
 // block x runs on XCD x % 8; the blocks of one (sequence, KV head) are given
@@ -59,8 +62,8 @@ constexpr int kHalves = 4;     // 32-token steps per staged block (one barrier e
 
 template <int D>
 struct MultiLds {
-  static constexpr int KP = 2 * D + 32;  // K row pitch in bytes (one token)
-  static constexpr int VP = 2 * 32;      // V row pitch in bytes (one dim), chunks permuted
+  static constexpr int KP = 2 * D;   // K row pitch in bytes (one token), chunks swizzled
+  static constexpr int VP = 2 * 32;  // V row pitch in bytes (one dim), chunks permuted
   static constexpr int K_OFF = 0;
   static constexpr int V_OFF = 32 * KP;
   static constexpr int S_OFF = V_OFF + D * VP;  // int8: 32 K scales, then 32 V scales
@@ -72,10 +75,40 @@ __device__ __forceinline__ int v_chunk(int d, int c) { return c ^ ((d >> 1) & 3)
 
 // LDS row of token r of a step: the 16 tokens of score tile t (token
 // 8 (n / 4) + 4t + n % 4 for row n) are stored in rows 16t .. 16t+15, so the
-// lanes of one read instruction touch consecutive rows, whose 16-byte-padded
-// pitch spreads them over distinct banks.
+// lanes of one read instruction touch consecutive rows.
 __device__ __forceinline__ int k_row(int r) {
   return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+}
+// The token stored in LDS row `row` (k_row inverted).
+__device__ __forceinline__ int k_tok(int row) {
+  const int n = row & 15;
+  return 8 * (n >> 2) + 4 * (row >> 4) + (n & 3);
+}
+// Byte offset of 16-byte chunk c (dims 8c .. 8c+7) of K row `row`: the chunk
+// index is XOR-ed with bits of the row, so the rows one read instruction
+// touches (same c, consecutive rows) fall on distinct banks: 256-byte rows
+// take bits 0-3 (16 chunk positions over 16 rows); 128-byte rows take bits
+// 1-3, row parity giving the other half of the banks.
+template <int D>
+__device__ __forceinline__ int k_pos(int row, int c) {
+  const int swz = D == 128 ? (row & 15) : ((row >> 1) & 7);
+  return row * 2 * D + 16 * (c ^ swz);
+}
+
+// A wave-uniform 64-bit value held in scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// 16 bytes per lane from global memory straight into LDS: the wave's 64
+// chunks land side by side from lds_wave (wave-uniform), lane l's at
+// lds_wave + 16 l.  Completion counts on the vector-memory counter.
+__device__ __forceinline__ void lds_dma16(const char* src, char* lds_wave) {
+  __builtin_amdgcn_global_load_lds(
+      (__attribute__((address_space(1))) void*)(const_cast<char*>(src)),
+      (__attribute__((address_space(3))) void*)(lds_wave), 16, 0, 0);
 }
 
 // 16 int8 codes -> 16 bf16 (two 16-byte words)
@@ -113,7 +146,9 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
   constexpr int NVC = D * CV;                        // V chunks per step
   constexpr int KL = (NKC + kThreads - 1) / kThreads;
   constexpr int VL = (NVC + kThreads - 1) / kThreads;
-  __shared__ __align__(16) char lds[2 * kHalves * L::BUF];
+  // two sets of kHalves step buffers, used in turn
+  __shared__ __align__(16) char lds0[kHalves * L::BUF];
+  __shared__ __align__(16) char lds1[kHalves * L::BUF];
 
   const int tid = threadIdx.x;
   // wave-uniform values are made scalar so that branches on them are
@@ -143,13 +178,20 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
   const int len = clamp_len(__builtin_amdgcn_readfirstlane(a.lens[b]), a.max_len,
                             reporter ? a.status : nullptr, PKV_DEV_LEN);
   if (reporter && (T > len || T > a.max_q)) report(a.status, PKV_DEV_QROWS);
-  const int pb0 = qb * kWaves * kTiles * P;  // the block's first position
-  if (pb0 >= T) return;
-  const int last_blk = min(pb0 + kWaves * kTiles * P, T) - 1;
+  // The chunk's positions go to waves in runs of WP; run r belongs to
+  // workgroup r % nq, so each of the sequence's nq workgroups holds runs from
+  // the start to the end of the chunk and reads about as many tokens as the
+  // others (the last positions see the most tokens).
+  const int WP = kTiles * P;                        // positions per wave
+  const int n_runs = (T + WP - 1) / WP;             // runs holding positions
+  const int nq = min((T + kWaves * WP - 1) / (kWaves * WP), a.n_qgroups);
+  if (qb >= nq) return;  // T = 0 too
+  const int top = min((n_runs - 1 - qb) / nq, kWaves - 1);  // the workgroup's last run
+  const int last_blk = min((qb + nq * top) * WP + WP, T) - 1;
   const int t_end = min(max(len - T + last_blk + 1, 0), len);  // tokens the block reads
 
   // ---- this wave's positions (kTiles tiles of P) and this lane's columns
-  const int p0 = pb0 + wave * kTiles * P;
+  const int p0 = (qb + nq * wave) * WP;  // at or past T: no positions
   const int p = n / G;
   const int h = n - p * G;
   bool col[kTiles];
@@ -167,9 +209,13 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
   }
   const int w_last = p0 < T ? len - T + min(p0 + kTiles * P, T) - 1 : -1;  // wave's last
 
-  const char* kp = static_cast<const char*>(a.k_pages);
-  const char* vp = static_cast<const char*>(a.v_pages);
+  // this KV head's slab of logical page 0 of the layer, and the distance
+  // between the slabs of consecutive page ids
+  const int64_t slab0 = a.layer_page0 * a.n_kv_heads + g;
   const int64_t slab_bytes = (int64_t)bs * D * ESZ;
+  const char* kp = static_cast<const char*>(a.k_pages) + slab0 * slab_bytes;
+  const char* vp = static_cast<const char*>(a.v_pages) + slab0 * slab_bytes;
+  const int64_t page_bytes = slab_bytes * a.n_kv_heads;
   const int32_t* trow = a.table + (int64_t)b * a.table_stride;
   const int pg_last = t_end > 0 ? (t_end - 1) / bs : -1;
 
@@ -198,22 +244,110 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
     return lp < win0 || lp + 2 * kHalves + 1 >= win0 + kPageWin;
   };
 
-  // ---- cooperative step load: registers, then LDS
+  // ---- step staging.  The pages of a step: page_a holds its first slot
+  // (slot0) and, with pages of 16, page_b its last 16 tokens.
+  struct Pages {
+    int page_a, page_b, slot0;
+  };
+  // The page ids of logical pages lp0 .. lp0 + kBlockPages - 1 (the most a
+  // staged block starting in page lp0 touches), one per lane, from one LDS
+  // read: the block's uniform lookups then read lanes of it instead of
+  // waiting on an LDS round trip each.  -1 past the range or on a bad entry.
+  constexpr int kBlockPages = 2 * kHalves + 2;
+  auto block_pages = [&](int lp0) {
+    const int e = min(lane, kBlockPages - 1);  // inside the window (window_misses)
+    const int v = pids[lp0 - win0 + e];
+    return lane < kBlockPages && lp0 + lane <= pg_last ? v : -1;
+  };
+  auto step_pages = [&](int ts, int pl, int lp0) {
+    Pages s;
+    const int lp = ts / bs;
+    s.page_a = __builtin_amdgcn_readlane(pl, lp - lp0);
+    s.page_b = BS == 16 ? (ts + 16 < t_end ? __builtin_amdgcn_readlane(pl, lp + 1 - lp0) : -1)
+                        : s.page_a;
+    s.slot0 = ts - lp * bs;
+    return s;
+  };
+  // a step whose 32 slots are all inside the range on live pages
+  auto step_whole = [&](int ts, const Pages& s) {
+    return ts + 32 <= t_end && s.page_a >= 0 && s.page_b >= 0;
+  };
+
+  // bf16: the step's 16-byte LDS chunks, K rows first, then V rows; chunk q
+  // comes from one 16-byte piece of a page
+  constexpr int KCB = D / 8;                // chunks per K row
+  constexpr int NKB = 32 * KCB;             // K chunks per step
+  constexpr int NCH = NKB + D * 4;          // all chunks of a step
+  constexpr int CL = NCH / kThreads;        // chunks per thread
+  static_assert(NCH % kThreads == 0 && NKB % 64 == 0, "a wave's chunks are all K or all V");
+  // Chunk i of a thread (q = tid + i kThreads) is a K chunk for the first
+  // NKB (whole waves).  Its source, for a step whose pages are at byte
+  // offsets 0 and whose first slot is 0, and the page it lies on (page_b:
+  // the second 16 tokens with pages of 16) are the same for every step; a
+  // step adds its page's offset and, for pages of more than 32 tokens, its
+  // first slot's (slot0, a multiple of 32, moves every K byte of a slab by
+  // k_byte(slot0, 0) and every V byte by 2 slot0).
+  auto is_k = [&](int i) {
+    return NKB >= kThreads ? i < NKB / kThreads : wave < NKB / 64;  // uniform
+  };
+  const char* csrc[CL];
+  bool con_b[CL];
+#pragma unroll
+  for (int i = 0; i < CL; ++i) {
+    const int q = tid + i * kThreads;
+    if (is_k(i)) {
+      const int row = q / KCB, c = (q % KCB) ^ ((k_pos<D>(row, 0) / 16) & (KCB - 1));
+      const int r = k_tok(row);
+      con_b[i] = BS == 16 && r >= 16;
+      csrc[i] = kp + k_byte(BS == 16 ? (r & 15) : r, c * 16, bs, D * 2);
+    } else {
+      const int d = (q - NKB) >> 2, c = v_chunk(d, (q - NKB) & 3);
+      con_b[i] = BS == 16 && c >= 2;
+      csrc[i] = vp + ((int64_t)d * bs + (BS == 16 ? (8 * c) & 15 : 8 * c)) * 2;
+    }
+  }
+  auto copy_step = [&](const Pages& s, char* buf) {
+    // (scalar offsets, selected per lane: without the read-first-lane the
+    // compiler selects the page per lane and multiplies per lane)
+    const int64_t oa = uniform64(max(s.page_a, 0) * page_bytes);
+    const int64_t ob = uniform64(max(s.page_b, 0) * page_bytes);
+    const int64_t kd = BS == 0 ? k_byte(s.slot0, 0, bs, D * 2) : 0;
+    const int64_t vd = BS == 0 ? 2 * s.slot0 : 0;
+#pragma unroll
+    for (int i = 0; i < CL; ++i) {
+      const int64_t off = (con_b[i] ? ob : oa) + (is_k(i) ? kd : vd);
+      lds_dma16(csrc[i] + off, buf + 16 * (wave * 64 + i * kThreads));
+    }
+  };
+  // after the copy landed: zero the K rows and V slots of tokens past the
+  // range or on a missing page (each chunk is one thread's)
+  auto zero_dead_slots = [&](int ts, const Pages& s, char* buf) {
+    const int live_n = t_end - ts;
+    auto page_dead = [&](int r) { return (BS == 16 && r >= 16 ? s.page_b : s.page_a) < 0; };
+#pragma unroll
+    for (int i = 0; i < CL; ++i) {
+      const int q = tid + i * kThreads;
+      uint4* p = reinterpret_cast<uint4*>(buf + 16 * q);
+      if (q < NKB) {
+        const int r = k_tok(q / KCB);
+        if (r >= live_n || page_dead(r)) *p = uint4{0, 0, 0, 0};
+      } else {
+        const int t0 = 8 * v_chunk((q - NKB) >> 2, (q - NKB) & 3);
+        const int keep = min(max(live_n - t0, 0), 8);
+        const uint32_t dbits = page_dead(t0) ? 0xffu : 0xffu & ~((1u << keep) - 1u);
+        if (dbits) *p = zero_dead(*p, dbits);
+      }
+    }
+  };
+
+  // int8: codes through registers, converted to bf16 on the way into LDS
   struct Stage {
     uint4 kc[KL], vc[VL];
     float sc;
-    int page_a, page_b, slot0;
   };
-  auto page_of = [&](int lp) {  // uniform; -1 past the range or on a bad entry
-    return lp > pg_last ? -1 : __builtin_amdgcn_readfirstlane(pids[lp - win0]);
-  };
-  auto load_stage = [&](int ts, Stage& st) {
-    const int lp = ts / bs;
-    st.page_a = page_of(lp);
-    st.page_b = BS == 16 ? (ts + 16 < t_end ? page_of(lp + 1) : -1) : st.page_a;
-    st.slot0 = ts - lp * bs;
-    const int64_t sa = (a.layer_page0 + max(st.page_a, 0)) * a.n_kv_heads + g;
-    const int64_t sb = (a.layer_page0 + max(st.page_b, 0)) * a.n_kv_heads + g;
+  auto load_stage = [&](const Pages& pg, Stage& st) {
+    const int64_t oa = max(pg.page_a, 0) * page_bytes;
+    const int64_t ob = max(pg.page_b, 0) * page_bytes;
 #pragma unroll
     for (int i = 0; i < KL; ++i) {
       const int q = tid + i * kThreads;
@@ -221,9 +355,9 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
       if (NKC % kThreads == 0 || q < NKC) {
         const int r = q / CK, c = q - r * CK;  // token row, chunk
         const bool on_b = BS == 16 && r >= 16;
-        const int slot = BS == 16 ? (r & 15) : st.slot0 + r;
+        const int slot = BS == 16 ? (r & 15) : pg.slot0 + r;
         st.kc[i] = stream_load<uint4, typename Step<FMT, D>::u32x4>(
-            kp + (on_b ? sb : sa) * slab_bytes + k_byte(slot, c * 16, bs, D * ESZ));
+            kp + (on_b ? ob : oa) + k_byte(slot, c * 16, bs, D * ESZ));
       }
     }
 #pragma unroll
@@ -234,42 +368,38 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
         const int d = q / CV, kk = q - d * CV;  // dim row, token group
         const int t0 = kk * E;
         const bool on_b = BS == 16 && t0 >= 16;
-        const int slot = BS == 16 ? (t0 & 15) : st.slot0 + t0;
+        const int slot = BS == 16 ? (t0 & 15) : pg.slot0 + t0;
         st.vc[i] = stream_load<uint4, typename Step<FMT, D>::u32x4>(
-            vp + (on_b ? sb : sa) * slab_bytes + ((int64_t)d * bs + slot) * ESZ);
+            vp + (on_b ? ob : oa) + ((int64_t)d * bs + slot) * ESZ);
       }
     }
     st.sc = 0.f;
     if (FMT == PKV_FMT_INT8 && tid < 64) {
       const int x = tid & 31;
       const bool on_b = BS == 16 && x >= 16;
-      const int slot = BS == 16 ? (x & 15) : st.slot0 + x;
+      const int slot = BS == 16 ? (x & 15) : pg.slot0 + x;
       const float* sp = tid < 32 ? a.k_scales : a.v_scales;
-      st.sc = __builtin_nontemporal_load(sp + (on_b ? sb : sa) * bs + slot);
+      const int64_t sl = slab0 + (int64_t)max(on_b ? pg.page_b : pg.page_a, 0) * a.n_kv_heads;
+      st.sc = __builtin_nontemporal_load(sp + sl * bs + slot);
     }
   };
-  auto store_stage = [&](int ts, const Stage& st, char* buf) {
+  auto store_stage = [&](int ts, const Pages& pg, const Stage& st, char* buf) {
     // token r of the step is dead past the block's range or on a missing
     // page; a whole step (the common case) is stored as it came
-    const bool whole = ts + 32 <= t_end && st.page_a >= 0 && st.page_b >= 0;  // uniform
+    const bool whole = step_whole(ts, pg);  // uniform
     const int live_n = t_end - ts;  // tokens r < live_n are inside the range
-    auto page_dead = [&](int r) { return (BS == 16 && r >= 16 ? st.page_b : st.page_a) < 0; };
+    auto page_dead = [&](int r) { return (BS == 16 && r >= 16 ? pg.page_b : pg.page_a) < 0; };
 #pragma unroll
     for (int i = 0; i < KL; ++i) {
       const int q = tid + i * kThreads;
       if (NKC % kThreads == 0 || q < NKC) {
-        const int r = q / CK, c = q - r * CK;
-        char* dst = buf + L::K_OFF + k_row(r) * L::KP + c * E * 2;
+        const int r = q / CK, c = q - r * CK;  // 16 codes: bf16 chunks 2c, 2c + 1
         const bool z = !whole && (r >= live_n || page_dead(r));
-        if constexpr (FMT == PKV_FMT_BF16) {
-          *reinterpret_cast<uint4*>(dst) = z ? uint4{0, 0, 0, 0} : st.kc[i];
-        } else {
-          uint4 lo, hi;
-          codes16_to_bf16(st.kc[i], lo, hi);
-          if (z) lo = hi = uint4{0, 0, 0, 0};
-          *reinterpret_cast<uint4*>(dst) = lo;
-          *reinterpret_cast<uint4*>(dst + 16) = hi;
-        }
+        uint4 lo, hi;
+        codes16_to_bf16(st.kc[i], lo, hi);
+        if (z) lo = hi = uint4{0, 0, 0, 0};
+        *reinterpret_cast<uint4*>(buf + L::K_OFF + k_pos<D>(k_row(r), 2 * c)) = lo;
+        *reinterpret_cast<uint4*>(buf + L::K_OFF + k_pos<D>(k_row(r), 2 * c + 1)) = hi;
       }
     }
 #pragma unroll
@@ -286,20 +416,15 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
           const int keep = min(max(live_n - t0, 0), E);
           dbits = page_dead(t0) ? (1u << E) - 1u : ((1u << E) - 1u) & ~((1u << keep) - 1u);
         }
-        if constexpr (FMT == PKV_FMT_BF16) {  // one chunk of 8 tokens
-          *reinterpret_cast<uint4*>(row + 16 * v_chunk(d, kk)) =
-              whole ? st.vc[i] : zero_dead(st.vc[i], dbits);
-        } else {  // 16 codes: two chunks of bf16
-          uint4 lo, hi;
-          codes16_to_bf16(st.vc[i], lo, hi);
-          *reinterpret_cast<uint4*>(row + 16 * v_chunk(d, 2 * kk)) =
-              whole ? lo : zero_dead(lo, dbits & 0xffu);
-          *reinterpret_cast<uint4*>(row + 16 * v_chunk(d, 2 * kk + 1)) =
-              whole ? hi : zero_dead(hi, dbits >> 8);
-        }
+        uint4 lo, hi;  // 16 codes: two chunks of bf16
+        codes16_to_bf16(st.vc[i], lo, hi);
+        *reinterpret_cast<uint4*>(row + 16 * v_chunk(d, 2 * kk)) =
+            whole ? lo : zero_dead(lo, dbits & 0xffu);
+        *reinterpret_cast<uint4*>(row + 16 * v_chunk(d, 2 * kk + 1)) =
+            whole ? hi : zero_dead(hi, dbits >> 8);
       }
     }
-    if (FMT == PKV_FMT_INT8 && tid < 64) {
+    if (tid < 64) {
       const int r = tid & 31;
       reinterpret_cast<float*>(buf + L::S_OFF)[tid] =
           !whole && (r >= live_n || page_dead(r)) ? 0.f : st.sc;
@@ -339,8 +464,8 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
       uint4 kw[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        kw[c] = *reinterpret_cast<const uint4*>(buf + L::K_OFF + row * L::KP +
-                                                kdim_of<PKV_FMT_BF16>(c, j) * 2);
+        kw[c] = *reinterpret_cast<const uint4*>(
+            buf + L::K_OFF + k_pos<D>(row, kdim_of<PKV_FMT_BF16>(c, j) / 8));
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -437,51 +562,104 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
     }
   };
 
-  // ---- the step loop: the loads of step i+1 are in flight while step i is
-  // computed from LDS; then step i+1 goes into the other LDS buffer (one
-  // barrier per step).  The prefetch is issued every iteration (past the
-  // last step it reloads the last step, unused): a load under a condition
-  // would make every step wait for all outstanding loads.
+  // ---- the step loop, in blocks of kHalves 32-token steps: the next
+  // block's copy is in flight while the waves compute the current one from
+  // the other set of LDS buffers; one barrier per block (two where a step of
+  // the next block has dead slots to zero).  The two buffer sets are
+  // distinct arrays, used in turn by a loop unrolled twice, so the compiler
+  // sees that the copy into one never overlaps the reads of the other and
+  // does not wait for it before them.  Halves past the last step take the
+  // last step's pages and are never computed.
   const int n_steps = (t_end + 31) / 32;
   if (n_steps > 0) {
-    // Blocks of kHalves 32-token steps are staged at a time, so one barrier,
-    // one round of page lookups and one load/store round serve 64 tokens.
-    // Halves past the last step load the last step again and are stored as
-    // dead slots (zeros) that no wave computes.
     const int ts_last = 32 * (n_steps - 1);
     const int n_blocks = (n_steps + kHalves - 1) / kHalves;
     auto at = [&](int ts) { return min(ts, ts_last); };
+    // whether step ts of a block just copied has dead slots that a wave reads
+    auto needs_zeros = [&](int ts, const Pages& pg) { return ts < t_end && !step_whole(ts, pg); };
     stage_pages(0);
+    Pages pg[kHalves];
     Stage st[kHalves];
     bool la[kHalves], lb[kHalves];
+    {
+      const int pl0 = block_pages(0);
 #pragma unroll
-    for (int hf = 0; hf < kHalves; ++hf) {
-      load_stage(at(32 * hf), st[hf]);
-      store_stage(32 * hf, st[hf], lds + hf * L::BUF);
-      la[hf] = st[hf].page_a >= 0;
-      lb[hf] = st[hf].page_b >= 0;
+      for (int hf = 0; hf < kHalves; ++hf) {
+        pg[hf] = step_pages(at(32 * hf), pl0, 0);
+        if constexpr (FMT == PKV_FMT_BF16) {
+          copy_step(pg[hf], lds0 + hf * L::BUF);
+        } else {
+          load_stage(pg[hf], st[hf]);
+          store_stage(32 * hf, pg[hf], st[hf], lds0 + hf * L::BUF);
+        }
+        la[hf] = pg[hf].page_a >= 0;
+        lb[hf] = pg[hf].page_b >= 0;
+      }
+      __syncthreads();
+      if constexpr (FMT == PKV_FMT_BF16) {
+        bool z = false;
+#pragma unroll
+        for (int hf = 0; hf < kHalves; ++hf) z = z || needs_zeros(32 * hf, pg[hf]);
+        if (z) {
+#pragma unroll
+          for (int hf = 0; hf < kHalves; ++hf)
+            if (needs_zeros(32 * hf, pg[hf])) zero_dead_slots(32 * hf, pg[hf], lds0 + hf * L::BUF);
+          __syncthreads();
+        }
+      }
     }
-    __syncthreads();
-    for (int i = 0; i < n_blocks; ++i) {
+    auto block = [&](int i, char* cur, char* nxt) __attribute__((always_inline)) {
       const int ts = 32 * kHalves * i;
       const int ts1 = ts + 32 * kHalves;  // the next block
-      if (window_misses(at(ts1) / bs)) stage_pages(at(ts1) / bs);  // uniform, rare
+      const bool more = i + 1 < n_blocks;
+      const int lp1 = at(ts1) / bs;
+      if (window_misses(lp1)) stage_pages(lp1);  // uniform, rare
+      const int pl = block_pages(lp1);
 #pragma unroll
-      for (int hf = 0; hf < kHalves; ++hf) load_stage(at(ts1 + 32 * hf), st[hf]);
-      char* cur = lds + (i & 1) * kHalves * L::BUF;
+      for (int hf = 0; hf < kHalves; ++hf) pg[hf] = step_pages(at(ts1 + 32 * hf), pl, lp1);
+      if constexpr (FMT == PKV_FMT_BF16) {
+        if (more) {
+#pragma unroll
+          for (int hf = 0; hf < kHalves; ++hf) copy_step(pg[hf], nxt + hf * L::BUF);
+        }
+      } else {
+        // issued every block (past the last, the last step again): a load
+        // under a condition would make every step wait for all loads
+#pragma unroll
+        for (int hf = 0; hf < kHalves; ++hf) load_stage(pg[hf], st[hf]);
+      }
 #pragma unroll
       for (int hf = 0; hf < kHalves; ++hf)
         if (ts + 32 * hf <= w_last) compute_step(ts + 32 * hf, cur + hf * L::BUF, la[hf], lb[hf]);
-      if (i + 1 < n_blocks) {
-        char* nxt = lds + ((i + 1) & 1) * kHalves * L::BUF;
+      if constexpr (FMT != PKV_FMT_BF16) {
+        if (more) {
 #pragma unroll
-        for (int hf = 0; hf < kHalves; ++hf) {
-          store_stage(ts1 + 32 * hf, st[hf], nxt + hf * L::BUF);
-          la[hf] = st[hf].page_a >= 0;
-          lb[hf] = st[hf].page_b >= 0;
+          for (int hf = 0; hf < kHalves; ++hf)
+            store_stage(ts1 + 32 * hf, pg[hf], st[hf], nxt + hf * L::BUF);
         }
       }
-      __syncthreads();
+      __syncthreads();  // its fence waits for this thread's copies too
+      if constexpr (FMT == PKV_FMT_BF16) {
+        bool z = false;
+#pragma unroll
+        for (int hf = 0; hf < kHalves; ++hf) z = z || needs_zeros(ts1 + 32 * hf, pg[hf]);
+        if (more && z) {
+#pragma unroll
+          for (int hf = 0; hf < kHalves; ++hf)
+            if (needs_zeros(ts1 + 32 * hf, pg[hf]))
+              zero_dead_slots(ts1 + 32 * hf, pg[hf], nxt + hf * L::BUF);
+          __syncthreads();
+        }
+      }
+#pragma unroll
+      for (int hf = 0; hf < kHalves; ++hf) {
+        la[hf] = pg[hf].page_a >= 0;
+        lb[hf] = pg[hf].page_b >= 0;
+      }
+    };
+    for (int i = 0; i < n_blocks; i += 2) {
+      block(i, lds0, lds1);
+      if (i + 1 < n_blocks) block(i + 1, lds1, lds0);
     }
   }
 

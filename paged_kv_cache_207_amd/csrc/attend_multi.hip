@@ -346,8 +346,8 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
     float sc;
   };
   auto load_stage = [&](const Pages& pg, Stage& st) {
-    const int64_t oa = max(pg.page_a, 0) * page_bytes;
-    const int64_t ob = max(pg.page_b, 0) * page_bytes;
+    const int64_t oa = uniform64(max(pg.page_a, 0) * page_bytes);
+    const int64_t ob = uniform64(max(pg.page_b, 0) * page_bytes);
 #pragma unroll
     for (int i = 0; i < KL; ++i) {
       const int q = tid + i * kThreads;

@@ -56,6 +56,10 @@ CASES = [
     ("bf16", 12, 4, 64, 16, (30, 90), (2, 19)),     # G = 3: 5 positions, 15 columns used
     ("int8", 32, 8, 128, 32, (1, 400), (1, 60)),
     ("int8", 8, 2, 64, 16, (0, 150), (0, 25)),
+    # pages of more than 32 tokens: a step's first slot moves inside the page
+    # (K rows of 128 and 64 bytes stored piece-major)
+    ("bf16", 16, 4, 64, 64, (0, 200), (1, 50)),
+    ("int8", 8, 2, 64, 96, (10, 300), (1, 40)),
 ]
 
 

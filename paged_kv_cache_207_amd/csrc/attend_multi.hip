@@ -102,6 +102,26 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// The column maxima of two tiles at once (each over the four 16-lane rows,
+// in every lane of the column): the first row swap pairs rows 0-1 and 2-3 of
+// x in one register with those of y in the other, so one maximum serves
+// both; x's pair maxima then sit in rows 0 and 2, y's in 1 and 3.  A half
+// swap and a maximum give x's column maxima in rows 0 and 2 and y's in 1
+// and 3, and a last row swap hands each to all four rows.  Three swaps and
+// two maxima instead of four and four.
+__device__ __forceinline__ void rows_max2(float& x, float& y) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false,
+                                                  false);
+  const float z = fmax_fast(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(z), __float_as_uint(z), false,
+                                                  false);
+  const float w = fmax_fast(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(w), __float_as_uint(w), false,
+                                                  false);
+  x = __uint_as_float(c[0]);
+  y = __uint_as_float(c[1]);
+}
+
 // 16 bytes per lane from global memory straight into LDS: the wave's 64
 // chunks land side by side from lds_wave (wave-uniform), lane l's at
 // lds_wave + 16 l.  Completion counts on the vector-memory counter.
@@ -436,15 +456,17 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
   // row of the result is the column's sum over the step's 32 weights, in
   // every lane of the column), which replaces per-lane adds and the final
   // cross-lane reduction; m: the reference maximum the weights are taken
-  // against.
+  // against, and m_use the same with 0 in place of -inf (no token seen yet),
+  // so that the weights' exponent never takes -inf - -inf.
   f32x4 o[kTiles][ND], ls[kTiles];
-  float m[kTiles];
+  float m[kTiles], m_use[kTiles];
 #pragma unroll
   for (int u = 0; u < kTiles; ++u) {
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     ls[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[u] = -INFINITY;
+    m_use[u] = 0.f;
   }
   const bf16x8 ones = as_bf16x8(uint4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
   const float qs = a.qk_scale_log2;
@@ -498,7 +520,7 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
     // Phase 1, per tile: scores, maxima, the reference maximum and the rescale
     // (rare); phase 2 then holds no branch, so the exponentials of one tile
     // and the P.V products of the other can interleave.
-    float sv[kTiles][8], m_use[kTiles];
+    float sv[kTiles][8], mxs[kTiles];
 #pragma unroll
     for (int u = 0; u < kTiles; ++u) {
       // scores: raw sums (int8: times the token's K scale), in log2 units
@@ -516,10 +538,15 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
 #pragma unroll
         for (int x = 0; x < 8; ++x) sv[u][x] = lane_live && x <= lim ? sv[u][x] : -INFINITY;
       }
-      float mx = sv[u][0];
+      mxs[u] = sv[u][0];
 #pragma unroll
-      for (int x = 1; x < 8; ++x) mx = fmax_fast(mx, sv[u][x]);
-      mx = rows_max(mx);
+      for (int x = 1; x < 8; ++x) mxs[u] = fmax_fast(mxs[u], sv[u][x]);
+    }
+    static_assert(kTiles == 2, "the column maxima of two tiles are taken together");
+    rows_max2(mxs[0], mxs[1]);
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) {
+      float mx = mxs[u];
       if (RAW) mx *= qs;  // a positive scale keeps the maximum where it is
       const float m_new = fmax_fast(m[u], mx);
       // Lazy rescale: the weights are taken against a reference maximum that
@@ -527,14 +554,14 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
       // kRescaleSlack (log2 units), so weights stay below 2^kRescaleSlack and
       // the outputs and sums are rescaled on few steps.
       const bool grow = __any(m_new > m[u] + kRescaleSlack);  // -inf + slack: any finite max
-      const float m_ref = grow ? m_new : m[u];
-      m_use[u] = m_ref == -INFINITY ? 0.f : m_ref;
-      if (grow) {
-        const float alpha = __builtin_amdgcn_exp2f(m[u] - m_use[u]);
+      if (grow) {  // (rare) the reference moves to m_new
+        const float mu = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m[u] - mu);
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) o[u][dt] *= alpha;
         ls[u] *= alpha;
-        m[u] = m_ref;
+        m[u] = m_new;
+        m_use[u] = mu;
       }
     }
     // Phase 2: weights, P.V and the sums

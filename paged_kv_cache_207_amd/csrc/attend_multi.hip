@@ -607,7 +607,7 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
     stage_pages(0);
     Pages pg[kHalves];
     Stage st[kHalves];
-    bool la[kHalves], lb[kHalves];
+    int pa[kHalves], pb[kHalves];  // the computed block's page ids (uniform: scalar registers)
     {
       const int pl0 = block_pages(0);
 #pragma unroll
@@ -619,8 +619,8 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
           load_stage(pg[hf], st[hf]);
           store_stage(32 * hf, pg[hf], st[hf], lds0 + hf * L::BUF);
         }
-        la[hf] = pg[hf].page_a >= 0;
-        lb[hf] = pg[hf].page_b >= 0;
+        pa[hf] = pg[hf].page_a;
+        pb[hf] = pg[hf].page_b;
       }
       __syncthreads();
       if constexpr (FMT == PKV_FMT_BF16) {
@@ -657,7 +657,7 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
       }
 #pragma unroll
       for (int hf = 0; hf < kHalves; ++hf)
-        if (ts + 32 * hf <= w_last) compute_step(ts + 32 * hf, cur + hf * L::BUF, la[hf], lb[hf]);
+        if (ts + 32 * hf <= w_last) compute_step(ts + 32 * hf, cur + hf * L::BUF, pa[hf] >= 0, pb[hf] >= 0);
       if constexpr (FMT != PKV_FMT_BF16) {
         if (more) {
 #pragma unroll
@@ -680,8 +680,8 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
       }
 #pragma unroll
       for (int hf = 0; hf < kHalves; ++hf) {
-        la[hf] = pg[hf].page_a >= 0;
-        lb[hf] = pg[hf].page_b >= 0;
+        pa[hf] = pg[hf].page_a;
+        pb[hf] = pg[hf].page_b;
       }
     };
     for (int i = 0; i < n_blocks; i += 2) {

@@ -133,7 +133,9 @@ def test_random_case(i):
 def test_random_multi_query_case(i):
     """Chunked prefill on seeded random shapes: bf16/int8 pages, groups of 1
     to 16 heads (at most 32 query heads), head dims 64/128, pages of 16-64
-    tokens, contexts and chunks of random lengths (empty chunks included)."""
+    tokens, contexts and chunks of random lengths (empty chunks included);
+    every third case takes pages of 96 or 128 tokens, where a step's first
+    slot moves inside the page."""
     require_gpu()
     rng = np.random.default_rng(zlib.crc32(f"random-multi-{i}".encode()))
     fmt = str(rng.choice(["bf16", "int8"]))
@@ -143,6 +145,8 @@ def test_random_multi_query_case(i):
         Hkv //= 2
     D = int(rng.choice([64, 128]))
     bs = int(rng.choice([16, 32, 64]))
+    if i % 3 == 2:
+        bs = int(rng.choice([96, 128]))
     c0 = int(rng.integers(0, 500))
     h0 = int(rng.integers(0, 40))
     cp = W.chunked_prefill(batch=int(rng.integers(1, 9)),

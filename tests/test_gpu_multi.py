@@ -173,3 +173,29 @@ def test_full_size_chunked_prefill_sampled(fmt):
     say(f"  sampled max err {e:.3e}")
     assert e <= TOL[fmt]
     assert c.status() == 0
+
+
+@pytest.mark.parametrize("fmt,bs", [("bf16", 16), ("bf16", 32), ("int8", 16), ("int8", 32)])
+def test_multi_query_bad_page_entries_flagged(fmt, bs):
+    """Table entries inside a sequence's range that name no page (negative,
+    or past the pool): the status reports them, that sequence's output stays
+    finite (its slots on those entries are dropped, never read as data, on
+    NaN-filled pools), and every other sequence's output is unchanged bit
+    for bit."""
+    require_gpu()
+    cp = W.chunked_prefill(batch=4, context=(70, 200), chunk=(10, 40), n_q_heads=16, n_kv_heads=4,
+                           head_dim=64, page_size=bs, kv_format=fmt, seed=53)
+    w = cp.base
+    c, q, clean = run(cp, sentinel=0xFF)
+    assert c.status() == 0
+    bad = w.tables.copy()
+    bad[0, 1] = -7                # inside sequence 0's context
+    bad[1, 2] = w.n_pages + 5     # inside sequence 1's context
+    say(f"bad entries ({fmt}, bs {bs}): lens {w.lens.tolist()}")
+    out = c.attend_multi(q.cuda(), dev(bad), dev(w.lens), dev(cp.cu_q), cp.max_q, w.max_len,
+                         w.scale)
+    torch.cuda.synchronize()
+    assert c.status() & pkv.DEV_READ_PAGE
+    assert torch.isfinite(out.float()).all()
+    rest = slice(int(cp.cu_q[2]), int(cp.cu_q[4]))
+    assert torch.equal(out[rest], clean[rest])

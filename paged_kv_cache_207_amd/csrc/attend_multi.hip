@@ -58,7 +58,8 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTiles = 2;  // 16-column tiles per wave: both use the same K/V operands
 constexpr int kPageWin = 512;  // page ids staged in LDS at a time
-constexpr int kHalves = 4;     // 32-token steps per staged block (one barrier each)
+constexpr int kHalves = 4;
+constexpr int kCopyWaves = 4;  // waves that copy bf16 steps into LDS (one per SIMD)     // 32-token steps per staged block (one barrier each)
 
 template <int D>
 struct MultiLds {
@@ -307,14 +308,22 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
   // step adds its page's offset and, for pages of more than 32 tokens, its
   // first slot's (slot0, a multiple of 32, moves every K byte of a slab by
   // k_byte(slot0, 0) and every V byte by 2 slot0).
+  // Only the first kCopyWaves waves issue the copies (each thread CW
+  // chunks): the two waves of a SIMD would otherwise both spend the start of
+  // every block issuing them, with no compute to overlap; this way the
+  // other wave of each SIMD computes meanwhile.
+  constexpr int kCopyThreads = 64 * kCopyWaves;
+  constexpr int CW = NCH / kCopyThreads;
+  static_assert(NCH % kCopyThreads == 0 && NKB % kCopyThreads == 0 || NKB < kCopyThreads,
+                "a copy wave's chunks are all K or all V");
   auto is_k = [&](int i) {
-    return NKB >= kThreads ? i < NKB / kThreads : wave < NKB / 64;  // uniform
+    return NKB >= kCopyThreads ? i < NKB / kCopyThreads : wave < NKB / 64;  // uniform
   };
-  const char* csrc[CL];
-  bool con_b[CL];
+  const char* csrc[CW];
+  bool con_b[CW];
 #pragma unroll
-  for (int i = 0; i < CL; ++i) {
-    const int q = tid + i * kThreads;
+  for (int i = 0; i < CW; ++i) {
+    const int q = tid + i * kCopyThreads;
     if (is_k(i)) {
       const int row = q / KCB, c = (q % KCB) ^ ((k_pos<D>(row, 0) / 16) & (KCB - 1));
       const int r = k_tok(row);
@@ -334,9 +343,9 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
     const int64_t kd = BS == 0 ? k_byte(s.slot0, 0, bs, D * 2) : 0;
     const int64_t vd = BS == 0 ? 2 * s.slot0 : 0;
 #pragma unroll
-    for (int i = 0; i < CL; ++i) {
+    for (int i = 0; i < CW; ++i) {
       const int64_t off = (con_b[i] ? ob : oa) + (is_k(i) ? kd : vd);
-      lds_dma16(csrc[i] + off, buf + 16 * (wave * 64 + i * kThreads));
+      lds_dma16(csrc[i] + off, buf + 16 * (wave * 64 + i * kCopyThreads));
     }
   };
   // after the copy landed: zero the K rows and V slots of tokens past the
@@ -614,7 +623,7 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
       for (int hf = 0; hf < kHalves; ++hf) {
         pg[hf] = step_pages(at(32 * hf), pl0, 0);
         if constexpr (FMT == PKV_FMT_BF16) {
-          copy_step(pg[hf], lds0 + hf * L::BUF);
+          if (wave < kCopyWaves) copy_step(pg[hf], lds0 + hf * L::BUF);
         } else {
           load_stage(pg[hf], st[hf]);
           store_stage(32 * hf, pg[hf], st[hf], lds0 + hf * L::BUF);
@@ -645,7 +654,7 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
 #pragma unroll
       for (int hf = 0; hf < kHalves; ++hf) pg[hf] = step_pages(at(ts1 + 32 * hf), pl, lp1);
       if constexpr (FMT == PKV_FMT_BF16) {
-        if (more) {
+        if (more && wave < kCopyWaves) {
 #pragma unroll
           for (int hf = 0; hf < kHalves; ++hf) copy_step(pg[hf], nxt + hf * L::BUF);
         }

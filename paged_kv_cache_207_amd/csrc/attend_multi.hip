@@ -170,6 +170,7 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
   // two sets of kHalves step buffers, used in turn
   __shared__ __align__(16) char lds0[kHalves * L::BUF];
   __shared__ __align__(16) char lds1[kHalves * L::BUF];
+  __shared__ int32_t live_bits[2];  // bf16: liveness of the next block's pages, by block parity
 
   const int tid = threadIdx.x;
   // wave-uniform values are made scalar so that branches on them are
@@ -650,15 +651,29 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
       const bool more = i + 1 < n_blocks;
       const int lp1 = at(ts1) / bs;
       if (window_misses(lp1)) stage_pages(lp1);  // uniform, rare
-      const int pl = block_pages(lp1);
-#pragma unroll
-      for (int hf = 0; hf < kHalves; ++hf) pg[hf] = step_pages(at(ts1 + 32 * hf), pl, lp1);
       if constexpr (FMT == PKV_FMT_BF16) {
-        if (more && wave < kCopyWaves) {
+        // bf16: the copy waves look the next block's pages up, copy it and
+        // publish which of its pages are live; the other waves read that
+        // after the barrier instead of looking the pages up themselves
+        if (wave < kCopyWaves) {
+          const int pl = block_pages(lp1);
+          int bits = 0;
 #pragma unroll
-          for (int hf = 0; hf < kHalves; ++hf) copy_step(pg[hf], nxt + hf * L::BUF);
+          for (int hf = 0; hf < kHalves; ++hf) {
+            pg[hf] = step_pages(at(ts1 + 32 * hf), pl, lp1);
+            bits |= (pg[hf].page_a >= 0 ? 1 : 0) << (2 * hf);
+            bits |= (pg[hf].page_b >= 0 ? 2 : 0) << (2 * hf);
+          }
+          if (more) {
+#pragma unroll
+            for (int hf = 0; hf < kHalves; ++hf) copy_step(pg[hf], nxt + hf * L::BUF);
+          }
+          if (tid == 0) live_bits[(i + 1) & 1] = bits;
         }
       } else {
+        const int pl = block_pages(lp1);
+#pragma unroll
+        for (int hf = 0; hf < kHalves; ++hf) pg[hf] = step_pages(at(ts1 + 32 * hf), pl, lp1);
         // issued every block (past the last, the last step again): a load
         // under a condition would make every step wait for all loads
 #pragma unroll
@@ -676,6 +691,14 @@ __global__ __launch_bounds__(kThreads, 1) void attend_multi_kernel(MultiArgs a) 
       }
       __syncthreads();  // its fence waits for this thread's copies too
       if constexpr (FMT == PKV_FMT_BF16) {
+        // the next block's page liveness (only the signs of the ids matter
+        // from here on)
+        const int bits = __builtin_amdgcn_readfirstlane(live_bits[(i + 1) & 1]);
+#pragma unroll
+        for (int hf = 0; hf < kHalves; ++hf) {
+          pg[hf].page_a = (bits >> (2 * hf)) & 1 ? 0 : -1;
+          pg[hf].page_b = (bits >> (2 * hf)) & 2 ? 0 : -1;
+        }
         bool z = false;
 #pragma unroll
         for (int hf = 0; hf < kHalves; ++hf) z = z || needs_zeros(ts1 + 32 * hf, pg[hf]);
